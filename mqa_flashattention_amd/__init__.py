@@ -1,0 +1,19 @@
+"""MI355X-native grouped-query attention forward (MHA / GQA / MQA).
+
+The compute runs in ``libgqa_attn.so`` (hand-written HIP for gfx950 behind a
+C ABI, declared in ``include/gqa_attn.h``).  ``binding`` is a thin ctypes layer
+over it: argument checks and marshalling only, no compute and no fallback.
+
+Importing this package does not load the library; the first use of
+``attn_fwd`` / ``attn_decode`` does, and raises if it has not been built.
+"""
+from __future__ import annotations
+
+__all__ = ["attn_fwd", "attn_decode", "decode_workspace_bytes", "library_path", "GqaError"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

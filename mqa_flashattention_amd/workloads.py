@@ -1,0 +1,133 @@
+"""Seeded synthetic inputs and the named workload shapes.
+
+This module holds no attention arithmetic: it only draws inputs.  The tests
+feed the same host tensors to the HIP library and to the CPU oracle, and the
+benchmark draws its inputs here too.
+
+Recipe (one torch CPU generator per draw, ``manual_seed(seed)``):
+  forward: Q, K, V in that order, each ``torch.randn(shape, float32)``, i.e.
+           N(0, 1); for bf16 workloads each tensor is then rounded to
+           bfloat16 (round-to-nearest-even) -- the rounded values are the
+           inputs both sides consume.
+  decode:  q, K cache, V cache in that order as above, then the per-sequence
+           cache lengths ``torch.randint(lo, hi + 1, (B,))`` (inclusive
+           uniform integers) from the same generator.
+
+The shapes are the workloads the pages turn on:
+  * LLaMA-3-8B attention shape (seq 2K, Hq 32, Hkv 8, d 128) from the
+    BootstrapAI evolution log, "Kernel 9 -- GQA", KV-read estimate.
+  * seq 4096 x 16 heads x batch 4 from the same log's "Kernel 8 --
+    persistent kernel" scheduling example, with head dim 64 from its
+    warp-specialization entry, swept over MHA / GQA / MQA (mode table of
+    "Kernel 9").
+  * cached decode at batch 8 with contexts up to 2048 (microLLM-rocm
+    optimization log, experiments 060/085/294, which time steady decode at
+    T2048 and B1..B8).
+  * a 512-token chunk of a 4096-token prompt (kaispace.site note on Chunked
+    Prefill, which splits a 4096-token prompt into chunks).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class FwdShape:
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool = False
+    q_offset: int = 0
+    dtype: torch.dtype = torch.bfloat16
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def visible_pairs_per_head(self) -> int:
+        """Number of (query, key) pairs the causal mask leaves visible, per head."""
+        if not self.causal:
+            return self.Nq * self.Nk
+        total = 0
+        for i in range(self.Nq):
+            total += min(self.Nk, self.q_offset + i + 1)
+        return total
+
+
+@dataclass(frozen=True)
+class DecodeShape:
+    B: int
+    Hq: int
+    Hkv: int
+    Smax: int
+    d: int
+    len_lo: int
+    len_hi: int
+    dtype: torch.dtype = torch.bfloat16
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    description: str
+    fwd: tuple = field(default_factory=tuple)       # FwdShape variants
+    decode: DecodeShape | None = None
+
+
+WORKLOADS = {
+    "tiny_gqa_f32": Workload(
+        "tiny_gqa_f32",
+        "Tiny GQA forward, fp32, non-causal: B=1 Hq=4 Hkv=2 N=64 d=32",
+        fwd=(FwdShape(1, 4, 2, 64, 64, 32, False, 0, torch.float32),)),
+    "llama3_8b_prefill": Workload(
+        "llama3_8b_prefill",
+        "LLaMA-3-8B-shaped causal prefill, bf16: B=1 Hq=32 Hkv=8 N=2048 d=128",
+        fwd=(FwdShape(1, 32, 8, 2048, 2048, 128, True, 0),)),
+    "mha_gqa_mqa_sweep": Workload(
+        "mha_gqa_mqa_sweep",
+        "MHA/GQA/MQA sweep, bf16, non-causal: B=4 N=4096 Hq=16 Hkv in {16,4,1} d=64",
+        fwd=tuple(FwdShape(4, 16, hkv, 4096, 4096, 64, False, 0) for hkv in (16, 4, 1))),
+    "kv_decode_b8": Workload(
+        "kv_decode_b8",
+        "KV-cache decode, bf16 cache: B=8 Hq=12 Hkv=2 d=128, lengths U[512,2048], Smax=2048",
+        decode=DecodeShape(8, 12, 2, 2048, 128, 512, 2048)),
+    "chunked_prefill_4k": Workload(
+        "chunked_prefill_4k",
+        "Chunked prefill, bf16, causal: B=1 Hq=32 Hkv=8 d=128, Nq=512 at q_offset=3584, Nk=4096",
+        fwd=(FwdShape(1, 32, 8, 512, 4096, 128, True, 3584),)),
+}
+
+
+def fwd_inputs(s: FwdShape, seed: int = 0):
+    """CPU tensors (q, k, v) for a forward shape; see the module recipe."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((s.B, s.Hq, s.Nq, s.d), generator=g, dtype=torch.float32)
+    k = torch.randn((s.B, s.Hkv, s.Nk, s.d), generator=g, dtype=torch.float32)
+    v = torch.randn((s.B, s.Hkv, s.Nk, s.d), generator=g, dtype=torch.float32)
+    return q.to(s.dtype), k.to(s.dtype), v.to(s.dtype)
+
+
+def decode_inputs(s: DecodeShape, seed: int = 0):
+    """CPU tensors (q, kcache, vcache, seqlens[int32]) for a decode shape."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((s.B, s.Hq, s.d), generator=g, dtype=torch.float32)
+    kc = torch.randn((s.B, s.Hkv, s.Smax, s.d), generator=g, dtype=torch.float32)
+    vc = torch.randn((s.B, s.Hkv, s.Smax, s.d), generator=g, dtype=torch.float32)
+    lens = torch.randint(s.len_lo, s.len_hi + 1, (s.B,), generator=g, dtype=torch.int64)
+    return q.to(s.dtype), kc.to(s.dtype), vc.to(s.dtype), lens.to(torch.int32)
+
+
+def random_tensor(shape, seed: int, dtype=torch.float32, scale: float = 1.0):
+    """One N(0, scale^2) tensor from its own seeded generator, rounded to dtype."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return (torch.randn(shape, generator=g, dtype=torch.float32) * scale).to(dtype)

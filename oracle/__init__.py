@@ -1,0 +1,168 @@
+"""CPU fp64 oracle for grouped-query attention forward -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls it, and this package never
+imports the product package: the two sides share nothing but the seeded
+inputs handed to both.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, fp64, OpenMP over output
+rows).  This module only compiles it with gcc and marshals numpy arrays.
+Every function widens its inputs to float64 exactly before the call (bf16 and
+fp32 values are exactly representable in fp64).
+
+What it computes, with its sources, is written at the top of ``attn_oracle.c``:
+the definition O = softmax(scale * Q K^T [causal, q_offset]) V with query head
+h reading K/V head h // (Hq // Hkv) (BootstrapAI evolution log, "Kernel 9 --
+GQA Flash Attention"), evaluated as max / exp-sum / weighted sum per row.
+
+Parity status: pinned (see tests/test_oracle.py -- library attention routine
+on random shapes, closed forms, invariants, and planted-mistake checks).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "attn_oracle.c")
+LIBRARY = os.path.join(_HERE, "libattn_oracle.so")
+
+_lock = threading.Lock()
+_libs: dict[str, ctypes.CDLL] = {}
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_lp = ctypes.c_long
+
+
+def compile_oracle(source: str = SOURCE, output: str = LIBRARY, strict: bool = True) -> str:
+    """Compile the oracle C source into a shared library with gcc (-O2, IEEE).
+
+    ``strict`` turns warnings into errors (the real source must build clean)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra"]
+    if strict:
+        cmd.append("-Werror")
+    cmd += [source, "-o", output, "-lm"]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+def load(path: str = LIBRARY, build_if_missing: bool = True) -> ctypes.CDLL:
+    """Load (compiling first if absent) an oracle library and declare its ABI."""
+    with _lock:
+        if path in _libs:
+            return _libs[path]
+        if not os.path.exists(path):
+            if not build_if_missing:
+                raise FileNotFoundError(path)
+            compile_oracle(SOURCE, path)
+        lib = ctypes.CDLL(path)
+        lib.oracle_attn_fwd.argtypes = [_dp, _dp, _dp, _dp, _lp, _lp, _lp, _lp, _lp, _lp,
+                                        ctypes.c_int, _lp, ctypes.c_double]
+        lib.oracle_attn_fwd_rows.argtypes = [_dp, _dp, _dp, _lp, _lp, _lp, _lp, _lp, _lp,
+                                             ctypes.c_int, _lp, ctypes.c_double,
+                                             ctypes.POINTER(ctypes.c_int64), _lp, _dp]
+        lib.oracle_attn_probs.argtypes = [_dp, _dp, _dp, _lp, _lp, _lp, _lp, _lp, _lp,
+                                          ctypes.c_int, _lp, ctypes.c_double,
+                                          _lp, _lp, _lp, _dp]
+        lib.oracle_attn_decode.argtypes = [_dp, _dp, _dp, ctypes.POINTER(ctypes.c_int32),
+                                           _dp, _lp, _lp, _lp, _lp, _lp, ctypes.c_double]
+        for name in ("oracle_attn_fwd", "oracle_attn_fwd_rows", "oracle_attn_probs",
+                     "oracle_attn_decode", "oracle_num_threads"):
+            getattr(lib, name).restype = ctypes.c_int
+        _libs[path] = lib
+        return lib
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening of a numpy array or (CPU) torch tensor to contiguous float64."""
+    if hasattr(x, "detach"):  # torch tensor: widen in torch (bf16 has no numpy dtype)
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_dp)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"{what}: oracle returned {rc}")
+
+
+def attn_fwd(q, k, v, *, causal: bool = False, q_offset: int = 0, scale: float | None = None,
+             lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """O[B,Hq,Nq,d] (float64) for q[B,Hq,Nq,d], k,v[B,Hkv,Nk,d]."""
+    lib = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty_like(q)
+    _check(lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Nq, Nk, d,
+                               int(bool(causal)), int(q_offset), float(scale)), "attn_fwd")
+    return o
+
+
+def attn_fwd_rows(q, k, v, row_ids, *, causal: bool = False, q_offset: int = 0,
+                  scale: float | None = None, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """Rows (b*Hq + h)*Nq + i of the forward output, as float64 [len(row_ids), d]."""
+    lib = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    ids = np.ascontiguousarray(np.asarray(row_ids, dtype=np.int64))
+    out = np.empty((ids.size, d), dtype=np.float64)
+    _check(lib.oracle_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Nq, Nk, d,
+                                    int(bool(causal)), int(q_offset), float(scale),
+                                    ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                    ids.size, _ptr(out)), "attn_fwd_rows")
+    return out
+
+
+def attn_probs(q, k, v, b: int, h: int, i: int, *, causal: bool = False, q_offset: int = 0,
+               scale: float | None = None, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """Softmax weights [Nk] of query row (b, h, i); zero for masked keys."""
+    lib = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    p = np.empty(Nk, dtype=np.float64)
+    _check(lib.oracle_attn_probs(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, Nq, Nk, d,
+                                 int(bool(causal)), int(q_offset), float(scale), b, h, i,
+                                 _ptr(p)), "attn_probs")
+    return p
+
+
+def attn_decode(q, kcache, vcache, seqlens, *, scale: float | None = None,
+                lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """O[B,Hq,d] for q[B,Hq,d], caches [B,Hkv,Smax,d], seqlens int[B]."""
+    lib = lib or load()
+    q, kc, vc = _f64(q), _f64(kcache), _f64(vcache)
+    if hasattr(seqlens, "detach"):
+        seqlens = seqlens.detach().to("cpu").numpy()
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    B, Hq, d = q.shape
+    Hkv, Smax = kc.shape[1], kc.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty_like(q)
+    _check(lib.oracle_attn_decode(_ptr(q), _ptr(kc), _ptr(vc),
+                                  sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(o),
+                                  B, Hq, Hkv, Smax, d, float(scale)), "attn_decode")
+    return o
+
+
+def num_threads(lib: ctypes.CDLL | None = None) -> int:
+    """OpenMP threads the oracle's parallel regions use in this process."""
+    lib = lib or load()
+    return int(lib.oracle_num_threads())

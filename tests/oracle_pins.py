@@ -1,0 +1,346 @@
+"""Pins for the CPU oracle: each checks it against something other than itself.
+
+Used two ways:
+  * ``tests/test_oracle.py`` runs every pin against the real oracle;
+  * ``python tests/oracle_pins.py LIB.so`` runs them all against one compiled
+    oracle library and exits non-zero if any fails.  ``test_oracle_mutants``
+    uses that to show that a planted mistake in the oracle source (dropped
+    term, wrong sign or index, transposed operand) fails at least one pin.
+
+What pins what (each pin names the passage or mathematical fact it rests on):
+  library    -- torch's scaled_dot_product_attention in fp64 on the CPU, with
+                K/V heads replicated by repeat_interleave; for q_offset = 0 its
+                own is_causal mask (top-left aligned) is used.
+  closed forms and invariants -- see each function's docstring.
+Inputs are numpy/torch draws with fixed seeds; nothing comes from the GPU.
+"""
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+
+TOL = 1e-12
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _case(seed, B, Hq, Hkv, Nq, Nk, d):
+    return (_rand((B, Hq, Nq, d), seed), _rand((B, Hkv, Nk, d), seed + 1),
+            _rand((B, Hkv, Nk, d), seed + 2))
+
+
+def _sdpa(q, k, v, causal, q_offset, scale):
+    import torch
+    import torch.nn.functional as F
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    g = qt.shape[1] // kt.shape[1]
+    kt = kt.repeat_interleave(g, dim=1)
+    vt = vt.repeat_interleave(g, dim=1)
+    Nq, Nk = qt.shape[2], kt.shape[2]
+    if causal and q_offset == 0:
+        out = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=scale)
+    elif causal:
+        i = torch.arange(Nq)[:, None]
+        j = torch.arange(Nk)[None, :]
+        out = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=(j <= q_offset + i),
+                                             scale=scale)
+    else:
+        out = F.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    return out.numpy()
+
+
+def _maxerr(a, b):
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+
+
+# --------------------------------------------------------------------------- pins
+
+def pin_library_attention(lib):
+    """Whole definition vs a library attention routine (fp64) on random tiny shapes,
+    MHA / GQA / MQA (BootstrapAI log, "Kernel 9" mode table), causal offsets
+    0, 1, Nk-Nq and past the end."""
+    rng = np.random.default_rng(1234)
+    for t in range(24):
+        Hkv = int(rng.choice([1, 2, 3]))
+        g = int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 3))
+        Nq = int(rng.integers(1, 23))
+        Nk = int(rng.integers(1, 29))
+        d = int(rng.choice([4, 8, 32]))
+        q, k, v = _case(100 + 3 * t, B, Hkv * g, Hkv, Nq, Nk, d)
+        scale = 1.0 / math.sqrt(d)
+        offsets = {0, 1, Nk + 3}
+        if Nk >= Nq:
+            offsets.add(Nk - Nq)
+        for causal in (False, True):
+            for off in (sorted(offsets) if causal else [0]):
+                o = oracle.attn_fwd(q, k, v, causal=causal, q_offset=off, scale=scale, lib=lib)
+                ref = _sdpa(q, k, v, causal, off, scale)
+                err = _maxerr(o, ref)
+                assert err <= TOL, f"case {t} causal={causal} off={off}: err {err}"
+
+
+def pin_decode_library(lib):
+    """Decode vs the library routine on each row's first n cache slots."""
+    rng = np.random.default_rng(77)
+    for t in range(8):
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.choice([1, 2]))
+        g = int(rng.choice([1, 3, 6]))
+        Smax = int(rng.integers(1, 40))
+        d = int(rng.choice([8, 32]))
+        q = _rand((B, Hkv * g, d), 500 + t)
+        kc = _rand((B, Hkv, Smax, d), 600 + t)
+        vc = _rand((B, Hkv, Smax, d), 700 + t)
+        lens = rng.integers(1, Smax + 1, size=B).astype(np.int32)
+        lens[0] = Smax
+        scale = 1.0 / math.sqrt(d)
+        o = oracle.attn_decode(q, kc, vc, lens, scale=scale, lib=lib)
+        for b in range(B):
+            n = int(lens[b])
+            ref = _sdpa(q[b:b + 1, :, None, :], kc[b:b + 1, :, :n], vc[b:b + 1, :, :n],
+                        False, 0, scale)[0, :, 0, :]
+            err = _maxerr(o[b], ref)
+            assert err <= TOL, f"decode case {t} row {b}: err {err}"
+
+
+def pin_gqa_equals_replicated_mha(lib):
+    """GQA equals MHA with each K/V head repeated g times (consecutive query heads
+    share a K/V head: h_kv = h_q / group_size)."""
+    for causal, off in ((False, 0), (True, 0), (True, 5)):
+        q, k, v = _case(11, 2, 8, 2, 13, 17, 8)
+        o = oracle.attn_fwd(q, k, v, causal=causal, q_offset=off, lib=lib)
+        o_mha = oracle.attn_fwd(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1),
+                                causal=causal, q_offset=off, lib=lib)
+        assert np.array_equal(o, o_mha), "GQA != replicated MHA"
+
+
+def pin_head_identity(lib):
+    """V of K/V head t set to the constant t+1: query head h returns h//g + 1."""
+    B, Hq, Hkv, N, d = 2, 12, 3, 9, 8
+    q, k, _ = _case(21, B, Hq, Hkv, N, N, d)
+    v = np.zeros((B, Hkv, N, d))
+    for t in range(Hkv):
+        v[:, t] = t + 1.0
+    o = oracle.attn_fwd(q, k, v, causal=True, lib=lib)
+    g = Hq // Hkv
+    for h in range(Hq):
+        assert np.all(np.abs(o[:, h] - (h // g + 1.0)) <= 1e-14), f"head {h}"
+
+
+def pin_probs_sum_to_one(lib):
+    """Each softmax row is a probability vector over its visible keys: weights
+    >= 0, exactly zero where masked, summing to 1; and O = sum_j p_j v_j."""
+    q, k, v = _case(31, 1, 4, 2, 10, 14, 8)
+    for causal, off in ((False, 0), (True, 0), (True, 3)):
+        o = oracle.attn_fwd(q, k, v, causal=causal, q_offset=off, lib=lib)
+        for h in range(4):
+            for i in range(10):
+                p = oracle.attn_probs(q, k, v, 0, h, i, causal=causal, q_offset=off, lib=lib)
+                assert abs(p.sum() - 1.0) <= 1e-13
+                assert np.all(p >= 0)
+                if causal:
+                    assert np.all(p[off + i + 1:] == 0.0)
+                    assert np.all(p[:off + i + 1] > 0)
+                assert _maxerr(p @ v[0, h // 2], o[0, h, i]) <= TOL
+
+
+def pin_constant_v(lib):
+    """Constant V returns that constant (softmax weights sum to one)."""
+    q, k, _ = _case(41, 2, 4, 4, 11, 23, 8)
+    v = np.full((2, 4, 23, 8), -1.75)
+    for causal in (False, True):
+        o = oracle.attn_fwd(q, k, v, causal=causal, q_offset=2, lib=lib)
+        assert np.all(np.abs(o + 1.75) <= 1e-14)
+
+
+def pin_causal_row0(lib):
+    """Causal with q_offset = 0: query row 0 sees only key 0, so it returns V[0]."""
+    q, k, v = _case(51, 2, 6, 3, 7, 7, 8)
+    o = oracle.attn_fwd(q, k, v, causal=True, q_offset=0, lib=lib)
+    for h in range(6):
+        assert np.array_equal(o[:, h, 0], v[:, h // 2, 0])
+
+
+def pin_single_key(lib):
+    """Nk = 1: every row returns V[0]."""
+    q, k, v = _case(61, 1, 4, 1, 5, 1, 8)
+    for causal in (False, True):
+        o = oracle.attn_fwd(q, k, v, causal=causal, lib=lib)
+        assert np.array_equal(o[0], np.broadcast_to(v[0, 0, 0], o[0].shape))
+
+
+def pin_two_keys_closed_form(lib):
+    """Two keys: O = sigmoid(s0 - s1) v0 + sigmoid(s1 - s0) v1."""
+    from scipy.special import expit
+    q, k, v = _case(71, 1, 2, 1, 6, 2, 8)
+    scale = 0.3
+    o = oracle.attn_fwd(q, k, v, scale=scale, lib=lib)
+    for h in range(2):
+        for i in range(6):
+            s0 = scale * float(np.dot(q[0, h, i], k[0, 0, 0]))
+            s1 = scale * float(np.dot(q[0, h, i], k[0, 0, 1]))
+            ref = expit(s0 - s1) * v[0, 0, 0] + expit(s1 - s0) * v[0, 0, 1]
+            assert _maxerr(o[0, h, i], ref) <= TOL
+
+
+def pin_zero_scale_mean(lib):
+    """scale = 0: uniform weights, so each row is the mean of its visible V rows."""
+    q, k, v = _case(81, 1, 4, 2, 6, 9, 8)
+    for causal, off in ((False, 0), (True, 0), (True, 2)):
+        o = oracle.attn_fwd(q, k, v, causal=causal, q_offset=off, scale=0.0, lib=lib)
+        for h in range(4):
+            for i in range(6):
+                last = min(9, off + i + 1) if causal else 9
+                ref = v[0, h // 2, :last].mean(axis=0)
+                assert _maxerr(o[0, h, i], ref) <= TOL
+
+
+def pin_key_shift_invariance(lib):
+    """Adding one vector u to every key shifts a row's scores by scale*q.u, a
+    row constant, which softmax cancels."""
+    q, k, v = _case(91, 1, 4, 2, 8, 12, 8)
+    u = _rand((8,), 92)
+    for causal in (False, True):
+        o1 = oracle.attn_fwd(q, k, v, causal=causal, lib=lib)
+        o2 = oracle.attn_fwd(q, k + u, v, causal=causal, lib=lib)
+        assert _maxerr(o1, o2) <= 1e-11
+
+
+def pin_chunk_consistency(lib):
+    """Chunked prefill: a chunk of queries at q_offset reproduces those rows of
+    the full causal pass (kaispace.site note on Chunked Prefill)."""
+    N, off, n = 30, 17, 9
+    q, k, v = _case(101, 1, 4, 2, N, N, 8)
+    full = oracle.attn_fwd(q, k, v, causal=True, lib=lib)
+    part = oracle.attn_fwd(np.ascontiguousarray(q[:, :, off:off + n]), k, v, causal=True,
+                           q_offset=off, lib=lib)
+    assert _maxerr(full[:, :, off:off + n], part) <= 1e-14
+
+
+def pin_offset_past_end_is_noncausal(lib):
+    """q_offset >= Nk - 1 leaves every key visible: causal equals non-causal."""
+    q, k, v = _case(111, 1, 2, 2, 5, 8, 8)
+    a = oracle.attn_fwd(q, k, v, causal=False, lib=lib)
+    for off in (7, 8, 100):
+        b = oracle.attn_fwd(q, k, v, causal=True, q_offset=off, lib=lib)
+        assert _maxerr(a, b) <= 1e-14
+
+
+def pin_key_permutation(lib):
+    """Non-causal attention does not depend on the order of the (key, value) pairs."""
+    q, k, v = _case(121, 2, 4, 2, 7, 15, 8)
+    perm = np.random.default_rng(5).permutation(15)
+    a = oracle.attn_fwd(q, k, v, lib=lib)
+    b = oracle.attn_fwd(q, k[:, :, perm], v[:, :, perm], lib=lib)
+    assert _maxerr(a, b) <= TOL
+
+
+def pin_linearity_in_v(lib):
+    """O is linear in V for fixed Q, K."""
+    q, k, v1 = _case(131, 1, 4, 2, 6, 10, 8)
+    v2 = _rand(v1.shape, 132)
+    for causal in (False, True):
+        a = oracle.attn_fwd(q, k, v1 + 2.0 * v2, causal=causal, lib=lib)
+        b = oracle.attn_fwd(q, k, v1, causal=causal, lib=lib) + \
+            2.0 * oracle.attn_fwd(q, k, v2, causal=causal, lib=lib)
+        assert _maxerr(a, b) <= TOL
+
+
+def pin_hardmax_limit(lib):
+    """Very large scale: softmax tends to the one-hot of the largest score, so the
+    row returns V at the argmax key (and stays finite, i.e. the max is
+    subtracted before exponentiating)."""
+    d, Nk = 8, 12
+    q = np.zeros((1, 1, 1, d))
+    q[0, 0, 0, 0] = 1.0
+    k = np.zeros((1, 1, Nk, d))
+    k[0, 0, :, 0] = np.linspace(-1.0, 1.0, Nk)[np.random.default_rng(3).permutation(Nk)]
+    v = _rand((1, 1, Nk, d), 141)
+    o = oracle.attn_fwd(q, k, v, scale=1e5, lib=lib)
+    jmax = int(np.argmax(k[0, 0, :, 0]))
+    assert np.all(np.isfinite(o))
+    assert _maxerr(o[0, 0, 0], v[0, 0, jmax]) <= TOL
+
+
+def pin_rows_match_full(lib):
+    """The sampled-row entry computes the same rows as the full pass."""
+    q, k, v = _case(151, 2, 6, 2, 9, 13, 8)
+    full = oracle.attn_fwd(q, k, v, causal=True, q_offset=3, lib=lib)
+    ids = np.array([0, 5, 17, 53, 107, 2 * 6 * 9 - 1])
+    rows = oracle.attn_fwd_rows(q, k, v, ids, causal=True, q_offset=3, lib=lib)
+    assert np.array_equal(rows, full.reshape(-1, 8)[ids])
+
+
+def pin_decode_semantics(lib):
+    """Decode = one query per row over the first n = clamp(seqlens, 0, Smax) slots;
+    slots past n are never read (NaN there changes nothing); n = 0 gives zeros."""
+    B, Hq, Hkv, Smax, d = 4, 6, 2, 19, 8
+    q = _rand((B, Hq, d), 161)
+    kc = _rand((B, Hkv, Smax, d), 162)
+    vc = _rand((B, Hkv, Smax, d), 163)
+    lens = np.array([1, 7, Smax, Smax + 5], dtype=np.int32)
+    o = oracle.attn_decode(q, kc, vc, lens, lib=lib)
+    for b in range(B):
+        n = min(int(lens[b]), Smax)
+        ref = oracle.attn_fwd(q[b:b + 1, :, None, :], kc[b:b + 1, :, :n], vc[b:b + 1, :, :n],
+                              lib=lib)[0, :, 0, :]
+        assert _maxerr(o[b], ref) <= 1e-14
+    kp, vp = kc.copy(), vc.copy()
+    for b in range(B):
+        kp[b, :, min(int(lens[b]), Smax):] = np.nan
+        vp[b, :, min(int(lens[b]), Smax):] = np.nan
+    assert np.array_equal(oracle.attn_decode(q, kp, vp, lens, lib=lib), o)
+    z = oracle.attn_decode(q, kc, vc, np.array([0, -3, 1, 2], dtype=np.int32), lib=lib)
+    assert np.all(z[0] == 0) and np.all(z[1] == 0)
+
+
+PINS = [
+    pin_library_attention,
+    pin_decode_library,
+    pin_gqa_equals_replicated_mha,
+    pin_head_identity,
+    pin_probs_sum_to_one,
+    pin_constant_v,
+    pin_causal_row0,
+    pin_single_key,
+    pin_two_keys_closed_form,
+    pin_zero_scale_mean,
+    pin_key_shift_invariance,
+    pin_chunk_consistency,
+    pin_offset_past_end_is_noncausal,
+    pin_key_permutation,
+    pin_linearity_in_v,
+    pin_hardmax_limit,
+    pin_rows_match_full,
+    pin_decode_semantics,
+]
+
+
+def main(argv):
+    lib = oracle.load(argv[1], build_if_missing=False)
+    failed = []
+    for pin in PINS:
+        try:
+            pin(lib)
+        except Exception as e:  # any failure (assertion, NaN, bad return) counts
+            failed.append(f"{pin.__name__}: {type(e).__name__}: {e}")
+    for f in failed:
+        print("FAIL", f)
+    print(f"{len(PINS) - len(failed)}/{len(PINS)} pins passed")
+    return 1 if failed else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv))

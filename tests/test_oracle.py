@@ -1,0 +1,161 @@
+"""CPU tests of the oracle: its pins, the method's algebra, and planted mistakes.
+
+No GPU and no HIP code is involved.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins
+from tests.oracle_pins import PINS, _case, _maxerr
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    oracle.compile_oracle()  # always the current source
+    return oracle.load()
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(lib, pin):
+    pin(lib)
+
+
+# ------------------------------------------------------------------ method algebra
+# The GPU path evaluates the definition with the tiled online-softmax
+# recurrence (running max m, rescale exp(m_old - m_new) of the running sum and
+# accumulator; BootstrapAI evolution log, "Kernel 2 -- tiling") and, for
+# decode, with split-KV partials merged by a combine pass (microLLM-rocm
+# optimization log, split-sequence experiments 283/284 and split-PV 291/292).
+# In exact arithmetic both equal the definition; these fp64 re-derivations,
+# written here from those descriptions, check that the algebra the kernels
+# use is the definition the oracle computes.
+
+def _online_row(qrow, K, V, last, scale, tiles):
+    m, l, acc = -np.inf, 0.0, np.zeros(V.shape[1])
+    start = 0
+    for t in tiles:
+        stop = min(start + t, last + 1)
+        if stop <= start:
+            break
+        s = scale * (K[start:stop] @ qrow)
+        m_new = max(m, float(s.max()))
+        alpha = 0.0 if m == -np.inf else np.exp(m - m_new)
+        p = np.exp(s - m_new)
+        l = alpha * l + p.sum()
+        acc = alpha * acc + p @ V[start:stop]
+        m = m_new
+        start = stop
+    return acc / l
+
+
+def _split_combine_row(qrow, K, V, n, scale, split):
+    parts = []
+    for s0 in range(0, n, split):
+        s = scale * (K[s0:min(n, s0 + split)] @ qrow)
+        m = float(s.max())
+        p = np.exp(s - m)
+        parts.append((m, p.sum(), p @ V[s0:min(n, s0 + split)]))
+    M = max(m for m, _, _ in parts)
+    w = [np.exp(m - M) for m, _, _ in parts]
+    num = sum(wi * a for wi, (_, _, a) in zip(w, parts))
+    den = sum(wi * l for wi, (_, l, _) in zip(w, parts))
+    return num / den
+
+
+def test_online_recurrence_equals_definition(lib):
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 11, 37, 8
+    q, k, v = _case(201, B, Hq, Hkv, Nq, Nk, d)
+    scale = 0.35
+    for causal, off in ((False, 0), (True, 0), (True, 20)):
+        o = oracle.attn_fwd(q, k, v, causal=causal, q_offset=off, scale=scale, lib=lib)
+        for h in range(Hq):
+            for i in range(Nq):
+                last = min(Nk - 1, off + i) if causal else Nk - 1
+                tiles = list(rng.integers(1, 9, size=Nk))
+                r = _online_row(q[0, h, i], k[0, h // 2], v[0, h // 2], last, scale, tiles)
+                assert _maxerr(r, o[0, h, i]) <= 1e-12
+
+
+def test_split_combine_equals_definition(lib):
+    B, Hq, Hkv, Smax, d = 3, 6, 1, 45, 8
+    rng = np.random.default_rng(10)
+    qd = rng.standard_normal((B, Hq, d))
+    kc = rng.standard_normal((B, Hkv, Smax, d))
+    vc = rng.standard_normal((B, Hkv, Smax, d))
+    lens = np.array([1, 30, 45], dtype=np.int32)
+    o = oracle.attn_decode(qd, kc, vc, lens, scale=0.4, lib=lib)
+    for split in (1, 4, 7, 32, 64):
+        for b in range(B):
+            for h in range(Hq):
+                r = _split_combine_row(qd[b, h], kc[b, 0], vc[b, 0], int(lens[b]), 0.4, split)
+                assert _maxerr(r, o[b, h]) <= 1e-12
+
+
+# ------------------------------------------------------------------ planted mistakes
+# Each mutant is the oracle source with one plausible mistake.  It is compiled
+# to a temporary library and the whole pin suite runs against it in a child
+# process (so a mutant that crashes also counts as caught).  Every mutant
+# must fail at least one pin.
+MUTANTS = [
+    ("head map tiles instead of repeats", "const long hk = h / g;", "const long hk = h % Hkv;", 1),
+    ("decode head map tiles", "const long hk = h / g;", "const long hk = h % Hkv;", 2),
+    ("causal diagonal excluded", "last = q_offset + i;", "last = q_offset + i - 1;", 1),
+    ("q_offset ignored", "if (causal && q_offset + i < last) last = q_offset + i;",
+     "if (causal && i < last) last = i;", 1),
+    ("scale dropped", "scores[j] = scale * dot;", "scores[j] = dot;", 1),
+    ("decode scale dropped", "scores[j] = scale * dot;", "scores[j] = dot;", 2),
+    ("max not subtracted", "scores[j] = exp(scores[j] - m);", "scores[j] = exp(scores[j]);", 1),
+    ("shift sign flipped", "scores[j] = exp(scores[j] - m);", "scores[j] = exp(m - scores[j]);", 1),
+    ("normalisation dropped", "for (long c = 0; c < d; ++c) out[c] /= l;", "", 1),
+    ("K transposed", "dot += qrow[c] * kbase[j * d + c];", "dot += qrow[c] * kbase[c * Nk + j];", 1),
+    ("V transposed", "out[c] += e * vbase[j * d + c];", "out[c] += e * vbase[c * Nk + j];", 1),
+    ("V from query head", "const double* vbase = v + (b * Hkv + hk) * Nk * d;",
+     "const double* vbase = v + (b * Hkv + h % Hkv) * Nk * d;", 1),
+    ("Q read token-major", "q + ((b * Hq + h) * Nq + i) * d", "q + ((b * Nq + i) * Hq + h) * d", 1),
+    ("decode length off by one", "long n = seqlens[b];", "long n = seqlens[b] - 1;", 1),
+    ("decode clamp missing", "if (n > Smax) n = Smax;", "", 1),
+    ("probabilities not normalised", "probs[j] = (j <= last) ? scores[j] / l : 0.0;",
+     "probs[j] = (j <= last) ? scores[j] : 0.0;", 1),
+]
+
+
+def _mutate(src: str, old: str, new: str, occurrence: int) -> str:
+    pos = -1
+    for _ in range(occurrence):
+        pos = src.find(old, pos + 1)
+        assert pos >= 0, f"mutation anchor not found: {old!r} (occurrence {occurrence})"
+    return src[:pos] + new + src[pos + len(old):]
+
+
+def test_real_oracle_passes_suite_in_child(lib, tmp_path):
+    r = subprocess.run([sys.executable, os.path.join(HERE, "oracle_pins.py"), oracle.LIBRARY],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("name,old,new,occ", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new, occ):
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(_mutate(src, old, new, occ))
+    mutant_lib = str(tmp_path / "libmutant.so")
+    oracle.compile_oracle(str(mutant_src), mutant_lib, strict=False)
+    r = subprocess.run([sys.executable, os.path.join(HERE, "oracle_pins.py"), mutant_lib],
+                       capture_output=True, text=True, timeout=300,
+                       env={**os.environ, "OMP_NUM_THREADS": "2"})
+    assert r.returncode != 0, f"mutant '{name}' passed every pin:\n{r.stdout}"
+
+
+def test_pin_module_importable():
+    assert len(oracle_pins.PINS) >= 15
