@@ -1,0 +1,128 @@
+/*
+ * gqa_attn.h -- C ABI of libgqa_attn.so: grouped-query attention forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One operation in three regimes -- full prefill, chunked prefill and
+ * single-token KV-cache decode:
+ *
+ *     O = softmax(Q K^T * scale [+ causal mask]) V
+ *
+ * MHA, GQA and MQA are one code path: query head h reads K/V head
+ * h / (Hq / Hkv), so g = Hq / Hkv consecutive query heads share one K/V head
+ * (BootstrapAI evolution log, entry "Kernel 9 -- GQA Flash Attention
+ * (MHA/GQA/MQA Unified)": the one-line head mapping, its Q/KV stride split
+ * and the MHA / GQA / MQA mode table).  Prefill and decode are the two
+ * regimes of the kaispace.site note on Chunked Prefill (prefill is
+ * compute-bound, decode is bound by KV-cache reads); chunked prefill is a
+ * query chunk placed at an absolute position q_offset.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers on the current HIP device,
+ *    contiguous row-major (innermost dimension last), owned by the caller.
+ *    The library never frees or keeps them.  Outputs must not alias inputs.
+ *  - dtype: GQA_DTYPE_BF16 (bf16 inputs and output, fp32 accumulation) or
+ *    GQA_DTYPE_F32 (fp32 everywhere).  All tensors of one call share it.
+ *  - stream: a hipStream_t (NULL = the legacy default stream).  Calls only
+ *    enqueue work and return; results are valid once the stream has been
+ *    synchronised.
+ *  - Every argument is validated on the host before any HIP call; on any
+ *    error nothing is launched and the output is not written.  There is no
+ *    fallback path: an unsupported case returns GQA_ERR_UNSUPPORTED.
+ *  - Library state: one small scheduler counter per (device, stream),
+ *    allocated on first use and kept until the process ends.  Calls on one
+ *    stream are ordered; calls on different streams use different counters.
+ *  - Return value: a gqa_status_t.  gqa_last_error_string() gives the
+ *    detail of the most recent failure on the calling thread.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GQA_DTYPE_F32 = 0,
+  GQA_DTYPE_BF16 = 1
+} gqa_dtype_t;
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                          */
+  GQA_ERR_BAD_SHAPE = 2,     /* a size <= 0, q_offset < 0, or an index overflows   */
+  GQA_ERR_HEAD_GROUPING = 3, /* Hq is not a multiple of Hkv                        */
+  GQA_ERR_UNSUPPORTED = 4,   /* head dim not in {32,64,128}, unknown dtype,
+                                non-finite scale                                    */
+  GQA_ERR_WORKSPACE = 5,     /* decode workspace NULL or smaller than required      */
+  GQA_ERR_NO_DEVICE = 6,     /* no HIP device, or the current device is not gfx950 */
+  GQA_ERR_HIP = 7            /* a HIP runtime or launch error                       */
+} gqa_status_t;
+
+/*
+ * Prefill / chunked-prefill forward.
+ *
+ *   q, o : [B, Hq,  Nq, d]      k, v : [B, Hkv, Nk, d]
+ *
+ * Query row i sits at absolute position q_offset + i.  With causal != 0 it
+ * sees keys j <= q_offset + i (diagonal included); without, all Nk keys and
+ * q_offset is ignored.  A chunk of Nq queries of a longer prompt at
+ * q_offset attending to the Nk = q_offset + Nq keys before and including it
+ * is the chunked-prefill case of the kaispace.site note.  scale multiplies
+ * Q K^T before the softmax (1/sqrt(d) is the usual value; any finite value
+ * is accepted).
+ *
+ * Requirements: B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0; d in {32, 64, 128};
+ * q_offset >= 0 when causal; Nq*d and Nk*d below 2^31.
+ */
+int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 int causal, int q_offset, float scale,
+                 int dtype, void* stream);
+
+/*
+ * Bytes of device workspace gqa_attn_decode needs for these sizes (an upper
+ * bound that does not depend on seqlens).  Returns 0 for invalid sizes.
+ */
+size_t gqa_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Smax, int d);
+
+/*
+ * Single-token KV-cache decode.
+ *
+ *   q, o            : [B, Hq, d]
+ *   kcache, vcache  : [B, Hkv, Smax, d]   (capacity Smax per head)
+ *   seqlens         : int32[B], device memory
+ *
+ * The single query of row b attends cache slots [0, n) with
+ * n = clamp(seqlens[b], 0, Smax): the caller has already written the new
+ * token's K/V into slot n-1.  Slots >= n are never read (they may hold
+ * anything, NaN included).  A row with n == 0 gets an all-zero output.
+ * Cache heads are addressed in place through the head mapping, with no
+ * per-query-head copies (microLLM-rocm optimization log, experiment 004,
+ * and the per-head capacity stride of experiment 062); the KV sequence is
+ * cut into splits whose partial softmax states are merged by a second pass
+ * (the split-sequence cached attention of experiments 283/284).
+ *
+ * workspace: device memory of at least gqa_attn_decode_workspace_bytes(...)
+ * bytes, owned by the caller; its contents on entry do not matter.  One
+ * workspace must not be used by two calls that may run concurrently.
+ */
+int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
+                    const int32_t* seqlens, void* o,
+                    int B, int Hq, int Hkv, int Smax, int d, float scale,
+                    int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English name of a status code (never NULL). */
+const char* gqa_status_string(int status);
+
+/* Detail of the most recent failing call on this thread ("" if none). */
+const char* gqa_last_error_string(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -1,0 +1,170 @@
+"""ctypes binding of libgqa_attn.so (C ABI in include/gqa_attn.h).
+
+Argument marshalling only: shape/dtype/device checks on torch tensors, output
+and workspace allocation through torch's caching allocator, and the current
+torch stream handed to the library.  Every step of the computation runs in the
+library's HIP kernels; there is no other code path.  If the library is
+missing, loading it raises ``ImportError`` -- it has to be built first
+(``python -m mqa_flashattention_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libgqa_attn.so")
+
+GQA_DTYPE_F32 = 0
+GQA_DTYPE_BF16 = 1
+_DTYPES = {torch.float32: GQA_DTYPE_F32, torch.bfloat16: GQA_DTYPE_BF16}
+
+STATUS_NAMES = {
+    0: "GQA_OK", 1: "GQA_ERR_NULL_POINTER", 2: "GQA_ERR_BAD_SHAPE", 3: "GQA_ERR_HEAD_GROUPING",
+    4: "GQA_ERR_UNSUPPORTED", 5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_NO_DEVICE", 7: "GQA_ERR_HIP",
+}
+EXPORTED = ("gqa_attn_fwd", "gqa_attn_decode", "gqa_attn_decode_workspace_bytes",
+            "gqa_status_string", "gqa_last_error_string")
+
+
+class GqaError(RuntimeError):
+    """A non-zero status from the library; ``status`` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is not built; run `python -m mqa_flashattention_amd.build`")
+    lib = ctypes.CDLL(LIBRARY)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gqa_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.gqa_attn_fwd.restype = i
+    lib.gqa_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.gqa_attn_decode_workspace_bytes.restype = sz
+    lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.gqa_attn_decode.restype = i
+    lib.gqa_status_string.argtypes = [i]
+    lib.gqa_status_string.restype = ctypes.c_char_p
+    lib.gqa_last_error_string.argtypes = []
+    lib.gqa_last_error_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def _raise(status: int) -> None:
+    if status != 0:
+        detail = lib.gqa_last_error_string().decode(errors="replace")
+        raise GqaError(status, detail or lib.gqa_status_string(status).decode())
+
+
+def _check_tensor(name: str, t: torch.Tensor, ndim: int, dtype: torch.dtype, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be on {device} (a GPU device), got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+             q_offset: int = 0, scale: float | None = None,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """O = softmax(scale * Q K^T [causal at q_offset]) V via gqa_attn_fwd.
+
+    q [B, Hq, Nq, d], k and v [B, Hkv, Nk, d], all bfloat16 or all float32,
+    contiguous, on one GPU.  Query head h reads K/V head h // (Hq // Hkv).
+    scale defaults to 1/sqrt(d)."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _check_tensor("q", q, 4, q.dtype, dev)
+    _check_tensor("k", k, 4, q.dtype, dev)
+    _check_tensor("v", v, 4, q.dtype, dev)
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if k.shape[0] != B or k.shape[3] != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, 4, q.dtype, dev)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must have the shape of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(dev):
+        st = lib.gqa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), int(q_offset),
+                              float(scale), _DTYPES[q.dtype], _stream_handle(dev))
+    _raise(st)
+    return out
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, Smax: int, d: int) -> int:
+    return int(lib.gqa_attn_decode_workspace_bytes(B, Hq, Hkv, Smax, d))
+
+
+def attn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                seqlens: torch.Tensor, *, scale: float | None = None,
+                out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Single-token decode via gqa_attn_decode.
+
+    q [B, Hq, d]; kcache, vcache [B, Hkv, Smax, d]; seqlens int32 [B] on the
+    same GPU.  Row b attends slots [0, clamp(seqlens[b], 0, Smax)).  The
+    workspace (uint8, at least decode_workspace_bytes(...)) is allocated when
+    not given."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _check_tensor("q", q, 3, q.dtype, dev)
+    _check_tensor("kcache", kcache, 4, q.dtype, dev)
+    _check_tensor("vcache", vcache, 4, q.dtype, dev)
+    _check_tensor("seqlens", seqlens, 1, torch.int32, dev)
+    B, Hq, d = q.shape
+    _, Hkv, Smax, _ = kcache.shape
+    if kcache.shape[0] != B or kcache.shape[3] != d or tuple(vcache.shape) != tuple(kcache.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} kcache{tuple(kcache.shape)}")
+    if seqlens.shape[0] != B:
+        raise ValueError("seqlens must have B entries")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, 3, q.dtype, dev)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must have the shape of q")
+    need = decode_workspace_bytes(B, Hq, Hkv, Smax, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the GPU of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(dev):
+        st = lib.gqa_attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(),
+                                 seqlens.data_ptr(), out.data_ptr(), B, Hq, Hkv, Smax, d,
+                                 float(scale), _DTYPES[q.dtype], workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream_handle(dev))
+    _raise(st)
+    return out

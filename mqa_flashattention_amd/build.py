@@ -1,0 +1,55 @@
+"""Build libgqa_attn.so in-tree with hipcc for gfx950.
+
+    python -m mqa_flashattention_amd.build          # compile
+    python -m mqa_flashattention_amd.build --asm    # also keep the gfx950 assembly
+
+Flags: -O3, C++17, position-independent shared library, gfx950 only, and
+packed-fp32 VALU instructions disabled for the device pass.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+SOURCES = [os.path.join(CSRC, "gqa_attn.hip")]
+HEADERS = [os.path.join(CSRC, f) for f in ("attn_tile.hpp", "prefill_kernel.hpp",
+                                           "decode_kernel.hpp")] + [
+    os.path.join(INCLUDE, "gqa_attn.h")]
+LIBRARY = os.path.join(PKG, "libgqa_attn.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def compile_flags() -> list[str]:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def build(verbose: bool = False, keep_asm: bool = False) -> str:
+    """Compile the HIP library; returns its path.  Always recompiles."""
+    tmp = LIBRARY + ".tmp"
+    cmd = [hipcc(), *compile_flags(), *SOURCES, "-o", tmp]
+    if keep_asm:
+        cmd += ["-save-temps=obj"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, cwd=CSRC)
+    os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+if __name__ == "__main__":
+    print(build(verbose=True, keep_asm="--asm" in sys.argv))

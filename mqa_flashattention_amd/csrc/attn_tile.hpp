@@ -1,0 +1,406 @@
+// attn_tile.hpp -- device building blocks of the gfx950 attention kernels.
+//
+// One wavefront owns 32 query columns.  Scores are computed transposed,
+// S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32
+// (fp32): K rows come from LDS as the A operand and the wave's Q fragment
+// stays in registers as the B operand for the whole key loop.  In the 32x32
+// accumulator layout a lane then holds 16 scores of ONE query (its column),
+// so the row max and row sum of the online softmax are per-lane scalars plus
+// a single exchange with the other half-wave.  The probabilities feed
+// O^T = V^T P^T straight from registers as the B operand of the second MFMA;
+// V is staged transposed in LDS so each lane's A operand is 16 contiguous
+// bytes.  A fixed row permutation of K (bits 2 and 3 of the row index
+// swapped) makes the keys a lane holds after the first MFMA exactly the 8
+// contiguous keys the second MFMA wants, so nothing is shuffled between the
+// two contractions.
+//
+// Online softmax: per tile, m' = max(m, rowmax s); alpha = 2^((m - m') c);
+// p = 2^(s c - m' c); l' = alpha l + sum p; acc' = alpha acc + P V, with
+// c = |scale| log2(e) -- the running-max rescale exp(m_old - m_new) of the
+// tiled kernel in the BootstrapAI evolution log ("Kernel 2 -- tiling"),
+// evaluated with the hardware base-2 exponential.  A negative scale is
+// applied by negating Q (exact in bf16 and fp32) so c stays >= 0.
+// In the bf16 path p is rounded to bf16 for the PV MFMA and l sums those
+// same rounded values, so the normalisation matches the weights used.
+//
+// Accumulator layout of a 32x32 MFMA (CDNA3/CDNA4): lane L, register r holds
+// row 8*(r/4) + 4*(L/32) + (r%4), column L%32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even), first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 v;
+  v.x = (__bf16)a;
+  v.y = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Low / high 16-bit halves of two words, packed (a's half first).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// K row read by MFMA row i of a 32-key block: bits 2 and 3 of i swapped.
+__device__ __forceinline__ int k_row_perm(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// Key (within a 32-key block) held in accumulator register r by half-wave h2.
+__device__ __forceinline__ constexpr int key_of_reg(int r, int h2) {
+  return 16 * (r / 8) + 8 * h2 + (r % 8);
+}
+
+// Compile-time tile configuration.
+//   T  : element type of Q/K/V/O (float or __bf16 stored as uint16)
+//   D  : head dimension (32, 64, 128)
+//   BC : keys per tile (multiple of 32)
+//   NW : wavefronts sharing one K/V tile
+template <typename T, int D_, int BC_, int NW_>
+struct TileCfg {
+  static constexpr bool F32 = std::is_same<T, float>::value;
+  static constexpr int D = D_;
+  static constexpr int BC = BC_;
+  static constexpr int NW = NW_;
+  static constexpr int NT = 64 * NW;
+  static constexpr int KB = BC / 32;  // 32-key blocks per tile
+  static constexpr int DB = D / 32;   // 32-row blocks of O^T
+  static constexpr int ESZ = sizeof(T);
+  static constexpr int EPC = 16 / ESZ;  // elements per 16-byte chunk
+  // LDS: K row-major [BC][KSTR]; V row-major [BC][VSTR] (fp32) or V^T [D][VSTR] (bf16).
+  static constexpr int KSTR = D + EPC;
+  static constexpr int VSTR = F32 ? D + EPC : BC + EPC;
+  static constexpr int K_ELEMS = BC * KSTR;
+  static constexpr int V_ELEMS = F32 ? BC * VSTR : D * VSTR;
+  static constexpr int STAGE_BYTES = (K_ELEMS + V_ELEMS) * ESZ;
+  // Global -> register staging in 16-byte chunks.
+  static constexpr int ROW_CHUNKS = D / EPC;
+  static constexpr int K_CHUNKS = BC * ROW_CHUNKS;
+  static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
+  // bf16 V is transposed while staging: a thread takes VK consecutive keys of
+  // one 8-element d-chunk and writes VK-key runs of 8 V^T rows.
+  static constexpr int VK_RAW = K_CHUNKS / NT;
+  static constexpr int VK = F32 ? 1 : (VK_RAW >= 8 ? 8 : (VK_RAW >= 4 ? 4 : (VK_RAW >= 2 ? 2 : 1)));
+  static constexpr int V_BLOCKS = (BC / VK) * ROW_CHUNKS;
+  static constexpr int V_PER_T = F32 ? K_PER_T : (V_BLOCKS + NT - 1) / NT;
+  static constexpr int V_LOADS = F32 ? K_PER_T : V_PER_T * VK;
+  // MFMA operand fragments of the wave's 32 queries.
+  static constexpr int QF = F32 ? D / 2 : D / 16;
+  using Frag = typename std::conditional<F32, float, bf16x8>::type;
+  // Probabilities as the B operand of O^T = V^T P^T: fp32 -> one value per
+  // MFMA (16 per key block); bf16 -> 8 values per MFMA (2 per key block).
+  static constexpr int PF = F32 ? 16 : 2;
+
+  static_assert(BC % 32 == 0, "tile must hold whole 32-key blocks");
+  static_assert(D % 32 == 0, "head dim must be a multiple of 32");
+  static_assert(BC % VK == 0, "V staging group must divide the tile");
+};
+
+template <class C>
+struct TileRegs {
+  u32x4 k[C::K_PER_T];
+  u32x4 v[C::V_LOADS];
+};
+
+// Issue the global loads of one K/V tile -- keys key0 .. key0+BC-1 of one
+// head whose rows start at kbase / vbase -- into registers.  Rows at or
+// beyond nkeys read as zero, so they add nothing even before masking.
+// Consecutive threads take consecutive 16-byte chunks of a row, so a wave's
+// load instruction covers whole rows.
+template <typename T, class C>
+__device__ __forceinline__ void load_tile(TileRegs<C>& r, const T* __restrict__ kbase,
+                                          const T* __restrict__ vbase, int key0, int nkeys,
+                                          int tid) {
+#pragma unroll
+  for (int n = 0; n < C::K_PER_T; ++n) {
+    const int id = tid + n * C::NT;
+    const int row = id / C::ROW_CHUNKS;
+    const int col = id % C::ROW_CHUNKS;
+    const int key = key0 + row;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if ((C::K_CHUNKS % C::NT == 0 || id < C::K_CHUNKS) && key < nkeys)
+      val = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * C::D + col * C::EPC);
+    r.k[n] = val;
+  }
+  if constexpr (C::F32) {
+#pragma unroll
+    for (int n = 0; n < C::K_PER_T; ++n) {
+      const int id = tid + n * C::NT;
+      const int row = id / C::ROW_CHUNKS;
+      const int col = id % C::ROW_CHUNKS;
+      const int key = key0 + row;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if ((C::K_CHUNKS % C::NT == 0 || id < C::K_CHUNKS) && key < nkeys)
+        val = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * C::D + col * C::EPC);
+      r.v[n] = val;
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < C::V_PER_T; ++n) {
+      const int id = tid + n * C::NT;
+      const int dc = id % C::ROW_CHUNKS;
+      const int kg = id / C::ROW_CHUNKS;
+#pragma unroll
+      for (int e = 0; e < C::VK; ++e) {
+        const int key = key0 + kg * C::VK + e;
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if ((C::V_BLOCKS % C::NT == 0 || id < C::V_BLOCKS) && key < nkeys)
+          val = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * C::D + dc * 8);
+        r.v[n * C::VK + e] = val;
+      }
+    }
+  }
+}
+
+// Element i (0..7) of a 16-byte chunk of bf16, from VK chunks, packed as a
+// VK-key run (first key in the lowest bits).
+template <int VK>
+struct VRun;
+template <>
+struct VRun<8> {
+  using type = u32x4;
+  __device__ __forceinline__ static type get(const u32x4* c, int i) {
+    const int w = i >> 1;
+    if (i & 1)
+      return u32x4{pair_hi(c[0][w], c[1][w]), pair_hi(c[2][w], c[3][w]),
+                   pair_hi(c[4][w], c[5][w]), pair_hi(c[6][w], c[7][w])};
+    return u32x4{pair_lo(c[0][w], c[1][w]), pair_lo(c[2][w], c[3][w]),
+                 pair_lo(c[4][w], c[5][w]), pair_lo(c[6][w], c[7][w])};
+  }
+};
+template <>
+struct VRun<4> {
+  using type = u32x2;
+  __device__ __forceinline__ static type get(const u32x4* c, int i) {
+    const int w = i >> 1;
+    if (i & 1) return u32x2{pair_hi(c[0][w], c[1][w]), pair_hi(c[2][w], c[3][w])};
+    return u32x2{pair_lo(c[0][w], c[1][w]), pair_lo(c[2][w], c[3][w])};
+  }
+};
+template <>
+struct VRun<2> {
+  using type = uint32_t;
+  __device__ __forceinline__ static type get(const u32x4* c, int i) {
+    const int w = i >> 1;
+    return (i & 1) ? pair_hi(c[0][w], c[1][w]) : pair_lo(c[0][w], c[1][w]);
+  }
+};
+template <>
+struct VRun<1> {
+  using type = uint16_t;
+  __device__ __forceinline__ static type get(const u32x4* c, int i) {
+    const int w = i >> 1;
+    return (uint16_t)((i & 1) ? (c[0][w] >> 16) : (c[0][w] & 0xffffu));
+  }
+};
+
+// Write a staged tile to LDS: K row-major; V row-major (fp32) or transposed
+// (bf16, V^T[d][key]).
+template <typename T, class C>
+__device__ __forceinline__ void store_tile(const TileRegs<C>& r, T* __restrict__ Ks,
+                                           T* __restrict__ Vs, int tid) {
+#pragma unroll
+  for (int n = 0; n < C::K_PER_T; ++n) {
+    const int id = tid + n * C::NT;
+    if (C::K_CHUNKS % C::NT == 0 || id < C::K_CHUNKS) {
+      const int row = id / C::ROW_CHUNKS;
+      const int col = id % C::ROW_CHUNKS;
+      *reinterpret_cast<u32x4*>(Ks + row * C::KSTR + col * C::EPC) = r.k[n];
+      if constexpr (C::F32)
+        *reinterpret_cast<u32x4*>(Vs + row * C::VSTR + col * C::EPC) = r.v[n];
+    }
+  }
+  if constexpr (!C::F32) {
+    using Run = VRun<C::VK>;
+#pragma unroll
+    for (int n = 0; n < C::V_PER_T; ++n) {
+      const int id = tid + n * C::NT;
+      if (C::V_BLOCKS % C::NT == 0 || id < C::V_BLOCKS) {
+        const int dc = id % C::ROW_CHUNKS;
+        const int kg = id / C::ROW_CHUNKS;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<typename Run::type*>(Vs + (dc * 8 + i) * C::VSTR + kg * C::VK) =
+              Run::get(&r.v[n * C::VK], i);
+      }
+    }
+  }
+}
+
+// The wave's query fragment: column j of the B operand is query row qrow.
+// Invalid columns are zero (their scores are 0 and their output is dropped).
+template <typename T, class C>
+__device__ __forceinline__ void load_q_frag(typename C::Frag (&qf)[C::QF],
+                                            const T* __restrict__ qrow, bool valid,
+                                            bool negate, int h2) {
+#pragma unroll
+  for (int ks = 0; ks < C::QF; ++ks) {
+    if constexpr (C::F32) {
+      const float x = valid ? qrow[2 * ks + h2] : 0.f;
+      qf[ks] = negate ? -x : x;
+    } else {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (valid) w = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h2);
+      if (negate) w ^= 0x80008000u;
+      qf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+}
+
+// S^T for one tile: s[kb] holds keys 32*kb .. 32*kb+31 of the tile.
+template <typename T, class C>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const typename C::Frag (&qf)[C::QF],
+                                        const T* __restrict__ Ks, int lane32, int h2) {
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+    f32x16 a = {};
+    const T* krow = Ks + (32 * kb + k_row_perm(lane32)) * C::KSTR;
+#pragma unroll
+    for (int ks = 0; ks < C::QF; ++ks) {
+      if constexpr (C::F32) {
+        a = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks + h2], qf[ks], a, 0, 0, 0);
+      } else {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * ks + 8 * h2);
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], a, 0, 0, 0);
+      }
+    }
+    s[kb] = a;
+  }
+}
+
+// Online-softmax update for one tile.  key0 is the absolute index of the
+// tile's first key; keys > lim are excluded when MASK is set.  On return
+// pf holds this tile's probabilities as the B operand of the PV MFMA, and
+// m, l, acc are rescaled to the new running max.
+template <class C, bool MASK>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[C::KB], float& m, float& l,
+                                             f32x16 (&acc)[C::DB],
+                                             typename C::Frag (&pf)[C::KB][C::PF], int key0,
+                                             int lim, int h2, float c) {
+  float mt = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[kb][r];
+      if (MASK && key0 + 32 * kb + key_of_reg(r, h2) > lim) x = kNegInf;
+      s[kb][r] = x;
+      mt = fmaxf(mt, x);
+    }
+  }
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  const float m_new = fmaxf(m, mt);
+  const float alpha = (m == kNegInf) ? 0.f : fast_exp2((m - m_new) * c);
+  const float mc = m_new * c;
+  float lt = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+    if constexpr (C::F32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = s[kb][r];
+        float p = fast_exp2(__builtin_fmaf(x, c, -mc));
+        if (MASK && x == kNegInf) p = 0.f;
+        pf[kb][r] = p;
+        lt += p;
+      }
+    } else {
+#pragma unroll
+      for (int hk = 0; hk < 2; ++hk) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = s[kb][8 * hk + 2 * e];
+          const float x1 = s[kb][8 * hk + 2 * e + 1];
+          float p0 = fast_exp2(__builtin_fmaf(x0, c, -mc));
+          float p1 = fast_exp2(__builtin_fmaf(x1, c, -mc));
+          if (MASK && x0 == kNegInf) p0 = 0.f;
+          if (MASK && x1 == kNegInf) p1 = 0.f;
+          const uint32_t pk = pack_bf16(p0, p1);
+          lt += bf16_lo(pk) + bf16_hi(pk);
+          w[e] = pk;
+        }
+        pf[kb][hk] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  }
+  l = alpha * l + lt;
+  m = m_new;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+}
+
+// acc[db] += V^T P^T for one tile (O^T rows 32*db .. 32*db+31).
+template <typename T, class C>
+__device__ __forceinline__ void pv_tile(f32x16 (&acc)[C::DB],
+                                        const typename C::Frag (&pf)[C::KB][C::PF],
+                                        const T* __restrict__ Vs, int lane32, int h2) {
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      if constexpr (C::F32) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float vf = Vs[(32 * kb + key_of_reg(r, h2)) * C::VSTR + 32 * db + lane32];
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf, pf[kb][r], acc[db], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int hk = 0; hk < 2; ++hk) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
+              Vs + (32 * db + lane32) * C::VSTR + 32 * kb + 16 * hk + 8 * h2);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][hk], acc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// Store one query row of O from the O^T accumulator: this lane holds d =
+// 32*db + 8*a + 4*h2 + (0..3) for a = 0..3.
+template <typename T, class C>
+__device__ __forceinline__ void store_out_row(T* __restrict__ orow, const f32x16 (&acc)[C::DB],
+                                              float inv, int h2) {
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * db + 8 * a + 4 * h2;
+      const float x0 = acc[db][4 * a + 0] * inv;
+      const float x1 = acc[db][4 * a + 1] * inv;
+      const float x2 = acc[db][4 * a + 2] * inv;
+      const float x3 = acc[db][4 * a + 3] * inv;
+      if constexpr (C::F32) {
+        *reinterpret_cast<float4*>(orow + d0) = float4{x0, x1, x2, x3};
+      } else {
+        *reinterpret_cast<u32x2*>(orow + d0) = u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
+      }
+    }
+  }
+}
+
+}  // namespace gqa

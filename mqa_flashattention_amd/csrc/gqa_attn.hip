@@ -1,0 +1,369 @@
+// gqa_attn.hip -- the C ABI of libgqa_attn.so (declared in include/gqa_attn.h).
+//
+// Host side only: argument validation (pure CPU, before any HIP call), the
+// gfx950 device check, the per-(device, stream) scheduler counters, choice
+// of the unit decomposition and split size, and the kernel launches.  All
+// arithmetic runs in the kernels of prefill_kernel.hpp / decode_kernel.hpp.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "decode_kernel.hpp"
+#include "gqa_attn.h"
+#include "prefill_kernel.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(GQA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
+
+constexpr long long kIntMax = 2147483647LL;
+
+struct DeviceInfo {
+  bool gfx950 = false;
+  int cus = 0;
+  std::string arch;
+};
+
+std::mutex g_mu;
+std::map<int, DeviceInfo> g_devices;
+std::map<std::pair<int, void*>, int*> g_counters;
+std::map<const void*, int> g_occupancy;
+
+// The current device, checked to be a gfx950.
+int current_device(int* dev_out, DeviceInfo* info_out) {
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return fail(GQA_ERR_NO_DEVICE, "no HIP device available (%s)",
+                e == hipSuccess ? "device count is 0" : hipGetErrorString(e));
+  }
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_devices.find(dev);
+  if (it == g_devices.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    DeviceInfo info;
+    info.arch = prop.gcnArchName;
+    info.gfx950 = info.arch.compare(0, 6, "gfx950") == 0;
+    info.cus = prop.multiProcessorCount;
+    it = g_devices.emplace(dev, info).first;
+  }
+  if (!it->second.gfx950)
+    return fail(GQA_ERR_NO_DEVICE, "device %d is %s, this library runs on gfx950 only", dev,
+                it->second.arch.c_str());
+  *dev_out = dev;
+  *info_out = it->second;
+  return GQA_OK;
+}
+
+__global__ void zero_ints_kernel(int* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
+// Two-int scheduler counter of one (device, stream), zeroed in stream order
+// on first use; each persistent launch leaves it at zero when it ends.
+int stream_counter(int dev, hipStream_t stream, int** out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  const auto key = std::make_pair(dev, reinterpret_cast<void*>(stream));
+  auto it = g_counters.find(key);
+  if (it != g_counters.end()) {
+    *out = it->second;
+    return GQA_OK;
+  }
+  int* p = nullptr;
+  hipError_t e = hipMalloc(&p, 2 * sizeof(int));
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(scheduler counter)");
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, stream, p, 2);
+  e = hipGetLastError();
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return hip_fail(e, "counter initialisation launch");
+  }
+  g_counters.emplace(key, p);
+  *out = p;
+  return GQA_OK;
+}
+
+// Resident workgroups per CU of a kernel (cached).
+int occupancy(const void* kernel, int threads) {
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_occupancy.find(kernel);
+    if (it != g_occupancy.end()) return it->second;
+  }
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess ||
+      nb < 1) {
+    (void)hipGetLastError();
+    nb = 1;
+  }
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_occupancy[kernel] = nb;
+  return nb;
+}
+
+// ------------------------------------------------------------------ prefill
+
+// bf16: 64-key tiles; fp32: 32-key tiles (LDS budget).  Four waves per
+// workgroup, 128 query columns per unit.
+constexpr int kPrefillWaves = 4;
+template <int D>
+using CfgBf16 = gqa::TileCfg<uint16_t, D, 64, kPrefillWaves>;
+template <int D>
+using CfgF32 = gqa::TileCfg<float, D, 32, kPrefillWaves>;
+
+template <typename T, class C, bool CAUSAL>
+int launch_prefill(gqa::PrefillArgs& a, const DeviceInfo& dev, hipStream_t stream) {
+  const void* kern = reinterpret_cast<const void*>(&gqa::prefill_kernel<T, C, CAUSAL>);
+  const int per_cu = occupancy(kern, C::NT);
+  long long grid = (long long)dev.cus * per_cu;
+  if (grid > a.T) grid = a.T;
+  hipLaunchKernelGGL((gqa::prefill_kernel<T, C, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+  return GQA_OK;
+}
+
+template <typename T, int D, template <int> class Cfg>
+int dispatch_prefill_d(gqa::PrefillArgs& a, int causal, const DeviceInfo& dev, hipStream_t s) {
+  return causal ? launch_prefill<T, Cfg<D>, true>(a, dev, s)
+                : launch_prefill<T, Cfg<D>, false>(a, dev, s);
+}
+
+template <typename T, template <int> class Cfg>
+int dispatch_prefill(gqa::PrefillArgs& a, int d, int causal, const DeviceInfo& dev,
+                     hipStream_t s) {
+  switch (d) {
+    case 32: return dispatch_prefill_d<T, 32, Cfg>(a, causal, dev, s);
+    case 64: return dispatch_prefill_d<T, 64, Cfg>(a, causal, dev, s);
+    default: return dispatch_prefill_d<T, 128, Cfg>(a, causal, dev, s);
+  }
+}
+
+// ------------------------------------------------------------------ decode
+
+constexpr int kMinSplit = 32;
+
+template <int D>
+using DecCfgBf16 = gqa::TileCfg<uint16_t, D, 32, 1>;
+template <int D>
+using DecCfgF32 = gqa::TileCfg<float, D, 32, 1>;
+
+// Tokens per split: enough splits to put about two waves on every CU when
+// every row is full, in whole 32-token tiles.
+int decode_split_tokens(int B, int Hkv, int ncb, int smax, int cus) {
+  const long long tiles_per_row = (smax + 31) / 32;
+  const long long heads = (long long)B * Hkv * ncb;
+  const long long target = 2LL * cus;
+  long long tiles_per_split = (heads * tiles_per_row + target - 1) / target;
+  if (tiles_per_split < 1) tiles_per_split = 1;
+  if (tiles_per_split > tiles_per_row) tiles_per_split = tiles_per_row;
+  return (int)(tiles_per_split * 32);
+}
+
+template <typename T, class C>
+int launch_decode(gqa::DecodeArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)a.NS, (unsigned)(a.Hkv * a.NCB), (unsigned)a.B);
+  hipLaunchKernelGGL((gqa::decode_split_kernel<T, C>), grid, dim3(64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "decode split kernel launch");
+  hipLaunchKernelGGL((gqa::decode_combine_kernel<T, C::D>), dim3((unsigned)a.Hq, (unsigned)a.B),
+                     dim3(64), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "decode combine kernel launch");
+  return GQA_OK;
+}
+
+template <typename T, template <int> class Cfg>
+int dispatch_decode(gqa::DecodeArgs& a, int d, hipStream_t s) {
+  switch (d) {
+    case 32: return launch_decode<T, Cfg<32>>(a, s);
+    case 64: return launch_decode<T, Cfg<64>>(a, s);
+    default: return launch_decode<T, Cfg<128>>(a, s);
+  }
+}
+
+size_t decode_ws_bytes(int B, int Hq, int smax, int d, int split) {
+  const size_t ns = (size_t)((smax + split - 1) / split);
+  return (size_t)B * Hq * ns * (size_t)(d + 4) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_NULL_POINTER: return "null pointer";
+    case GQA_ERR_BAD_SHAPE: return "bad shape";
+    case GQA_ERR_HEAD_GROUPING: return "query heads not a multiple of key/value heads";
+    case GQA_ERR_UNSUPPORTED: return "unsupported argument";
+    case GQA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GQA_ERR_NO_DEVICE: return "no gfx950 device";
+    case GQA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* gqa_last_error_string(void) { return g_last_error.c_str(); }
+
+int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+                 int Nq, int Nk, int d, int causal, int q_offset, float scale, int dtype,
+                 void* stream) {
+  g_last_error.clear();
+  // ---- validation: host only, before any HIP call
+  if (!q || !k || !v || !o) return fail(GQA_ERR_NULL_POINTER, "q, k, v and o must be non-NULL");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1)
+    return fail(GQA_ERR_BAD_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d)", B,
+                Hq, Hkv, Nq, Nk, d);
+  if (causal && q_offset < 0) return fail(GQA_ERR_BAD_SHAPE, "q_offset=%d < 0", q_offset);
+  if (Hq % Hkv != 0)
+    return fail(GQA_ERR_HEAD_GROUPING, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+  if (!std::isfinite(scale)) return fail(GQA_ERR_UNSUPPORTED, "scale must be finite");
+  if ((long long)Nq * d > kIntMax || (long long)Nk * d > kIntMax ||
+      (causal && (long long)q_offset + Nq > kIntMax))
+    return fail(GQA_ERR_BAD_SHAPE, "sequence too long for 32-bit in-head indexing");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(GQA_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+
+  const int M = 32 * kPrefillWaves;
+  const int g = Hq / Hkv;
+  const int Gu = g < M ? g : M;
+  const int R = M / Gu;
+  const int HB = (g + Gu - 1) / Gu;
+  const long long NQB = ((long long)Nq + R - 1) / R;
+  const long long T = (long long)B * Hkv * HB * NQB;
+  if (T > kIntMax) return fail(GQA_ERR_BAD_SHAPE, "too many work units (%lld)", T);
+
+  // ---- device
+  int dev = 0;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != GQA_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  int* ctr = nullptr;
+  st = stream_counter(dev, hs, &ctr);
+  if (st != GQA_OK) return st;
+
+  gqa::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.g = g;
+  a.Gu = Gu;
+  a.R = R;
+  a.HB = HB;
+  a.NQB = (int)NQB;
+  a.T = (int)T;
+  a.q_offset = causal ? q_offset : 0;
+  a.c = std::fabs(scale) * gqa::kLog2e;
+  a.negate_q = scale < 0.f ? 1 : 0;
+  a.ctr = ctr;
+  (void)hipGetLastError();  // a stale error belongs to an earlier call
+  if (dtype == GQA_DTYPE_BF16) return dispatch_prefill<uint16_t, CfgBf16>(a, d, causal, info, hs);
+  return dispatch_prefill<float, CfgF32>(a, d, causal, info, hs);
+}
+
+size_t gqa_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Smax, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Smax < 1 || !head_dim_ok(d) || Hq % Hkv != 0) return 0;
+  return decode_ws_bytes(B, Hq, Smax, d, kMinSplit);
+}
+
+int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
+                    const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int Smax, int d,
+                    float scale, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  g_last_error.clear();
+  if (!q || !kcache || !vcache || !seqlens || !o)
+    return fail(GQA_ERR_NULL_POINTER, "q, kcache, vcache, seqlens and o must be non-NULL");
+  if (B < 1 || Hq < 1 || Hkv < 1 || Smax < 1 || d < 1)
+    return fail(GQA_ERR_BAD_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Smax=%d d=%d)", B, Hq,
+                Hkv, Smax, d);
+  if (Hq % Hkv != 0)
+    return fail(GQA_ERR_HEAD_GROUPING, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+  if (!std::isfinite(scale)) return fail(GQA_ERR_UNSUPPORTED, "scale must be finite");
+  if ((long long)Smax * d > kIntMax)
+    return fail(GQA_ERR_BAD_SHAPE, "cache capacity too large for 32-bit in-head indexing");
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o))
+    return fail(GQA_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+  const size_t need = decode_ws_bytes(B, Hq, Smax, d, kMinSplit);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(GQA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+
+  int dev = 0;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != GQA_OK) return st;
+
+  const int g = Hq / Hkv;
+  gqa::DecodeArgs a;
+  a.q = q;
+  a.kc = kcache;
+  a.vc = vcache;
+  a.seqlens = seqlens;
+  a.o = o;
+  a.ws = reinterpret_cast<float*>(workspace);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Smax = Smax;
+  a.g = g;
+  a.NCB = (g + 31) / 32;
+  a.S_TOK = decode_split_tokens(B, Hkv, a.NCB, Smax, info.cus);
+  a.NS = (Smax + a.S_TOK - 1) / a.S_TOK;
+  a.c = std::fabs(scale) * gqa::kLog2e;
+  a.negate_q = scale < 0.f ? 1 : 0;
+  if ((long long)a.Hkv * a.NCB > 65535 || B > 65535)
+    return fail(GQA_ERR_BAD_SHAPE, "grid too large (B=%d, Hkv*blocks=%d)", B, a.Hkv * a.NCB);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (dtype == GQA_DTYPE_BF16) return dispatch_decode<uint16_t, DecCfgBf16>(a, d, hs);
+  return dispatch_decode<float, DecCfgF32>(a, d, hs);
+}
+
+}  // extern "C"

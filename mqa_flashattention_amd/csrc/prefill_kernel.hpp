@@ -1,0 +1,168 @@
+// prefill_kernel.hpp -- persistent GQA forward (prefill and chunked prefill).
+//
+// Work unit = (batch b, K/V head hkv, head block hb, position block qb): the
+// Gu query heads hb*Gu .. hb*Gu+Gu-1 of the group that shares K/V head hkv
+// (head mapping hkv = h / g, BootstrapAI evolution log, "Kernel 9 -- GQA"),
+// stacked over R consecutive query positions, Gu*R <= 32*NW columns.  Column
+// m of the unit is head r = m / R at position p = m % R, so every K/V tile a
+// workgroup stages in LDS is read from HBM once and serves all Gu heads: the
+// "one K/V tile shared by many query rows" idea of the same log's
+// cooperative-loading kernel ("Kernel 3"), widened from query rows to the
+// whole head group.
+//
+// Scheduling is persistent ("Kernel 8 -- persistent kernel" of the same
+// log): the grid holds as many workgroups as fit on the device at once and
+// each repeatedly takes the next unit index from a device counter with one
+// atomic add, exiting once the index passes the unit count.  Units are
+// numbered heaviest first for causal attention (the last position blocks see
+// the most keys), which makes the first-come order a longest-job-first
+// schedule; for non-causal attention units that share a K/V head are
+// numbered consecutively so they run close in time and share L2.  The last
+// workgroup to leave resets the counter for the next launch on the stream.
+//
+// Per unit the key tiles stream through a two-stage LDS ring: the global
+// loads of tile t+1 are issued before tile t is computed and written to the
+// other stage afterwards.  Causal masking runs only on tiles that cross the
+// diagonal (or the ragged end of the keys); tiles above the diagonal of the
+// whole unit are never loaded.
+#pragma once
+
+#include "attn_tile.hpp"
+
+namespace gqa {
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int B, Hq, Hkv, Nq, Nk;
+  int g;    // Hq / Hkv
+  int Gu;   // query heads per unit
+  int R;    // query positions per unit
+  int HB;   // head blocks per K/V head, ceil(g / Gu)
+  int NQB;  // position blocks, ceil(Nq / R)
+  int T;    // units, B * Hkv * HB * NQB
+  int q_offset;
+  float c;  // |scale| * log2(e)
+  int negate_q;
+  int* ctr;  // [0] next unit, [1] workgroups finished
+};
+
+template <typename T, class C, bool CAUSAL>
+__global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+  __shared__ int s_unit;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int j = lane & 31;
+  const int h2 = lane >> 5;
+
+  // stage st: K at smem + st*STAGE_BYTES, V right after it
+  auto stK = [&](int st) { return reinterpret_cast<T*>(smem + st * C::STAGE_BYTES); };
+  auto stV = [&](int st) { return stK(st) + C::K_ELEMS; };
+
+  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q);
+  const T* __restrict__ K = reinterpret_cast<const T*>(a.k);
+  const T* __restrict__ V = reinterpret_cast<const T*>(a.v);
+  T* __restrict__ O = reinterpret_cast<T*>(a.o);
+
+  for (;;) {
+    if (tid == 0) s_unit = atomicAdd(a.ctr, 1);
+    __syncthreads();
+    const int t = s_unit;
+    if (t >= a.T) break;
+
+    // ---- unit index -> (b, hkv, hb, qb)
+    const int per_qb = a.B * a.Hkv * a.HB;
+    int qb, rest;
+    if (CAUSAL) {
+      qb = a.NQB - 1 - t / per_qb;
+      rest = t % per_qb;
+    } else {
+      qb = t % a.NQB;
+      rest = t / a.NQB;
+    }
+    const int hb = rest % a.HB;
+    const int bh = rest / a.HB;
+    const int hkv = bh % a.Hkv;
+    const int b = bh / a.Hkv;
+
+    // ---- this lane's query column
+    const int m = 32 * w + j;
+    const int r = m / a.R;
+    const int p = m - r * a.R;
+    const int hig = hb * a.Gu + r;  // head within the group
+    const int i = qb * a.R + p;     // query row
+    const bool valid = (r < a.Gu) && (hig < a.g) && (i < a.Nq);
+    const int h = hkv * a.g + hig;
+    const size_t qrow_off = valid ? (((size_t)b * a.Hq + h) * a.Nq + i) * C::D : 0;
+
+    typename C::Frag qf[C::QF];
+    load_q_frag<T, C>(qf, Q + qrow_off, valid, a.negate_q != 0, h2);
+
+    const size_t kv_off = ((size_t)b * a.Hkv + hkv) * a.Nk * C::D;
+    const T* kbase = K + kv_off;
+    const T* vbase = V + kv_off;
+
+    // ---- key range of the unit
+    const int i_lo = qb * a.R;
+    const int i_hi = min(a.Nq, i_lo + a.R) - 1;
+    const int kend = CAUSAL ? min(a.Nk, a.q_offset + i_hi + 1) : a.Nk;
+    const int ntiles = (kend + C::BC - 1) / C::BC;
+    // keys below full_lim are visible to every column of the unit
+    const int full_lim = CAUSAL ? min(a.Nk, a.q_offset + i_lo + 1) : a.Nk;
+    // last key this lane's query may see
+    const int lim = (CAUSAL && valid) ? min(a.q_offset + i, a.Nk - 1) : a.Nk - 1;
+
+    float mrun = kNegInf, lrun = 0.f;
+    f32x16 acc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+
+    TileRegs<C> regs;
+    load_tile<T, C>(regs, kbase, vbase, 0, a.Nk, tid);
+    store_tile<T, C>(regs, stK(0), stV(0), tid);
+    __syncthreads();
+
+    for (int kt = 0; kt < ntiles; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < ntiles;
+      if (more) load_tile<T, C>(regs, kbase, vbase, (kt + 1) * C::BC, a.Nk, tid);
+
+      f32x16 s[C::KB];
+      qk_tile<T, C>(s, qf, stK(cur), j, h2);
+
+      typename C::Frag pf[C::KB][C::PF];
+      const int key0 = kt * C::BC;
+      if (key0 + C::BC > full_lim)
+        softmax_tile<C, true>(s, mrun, lrun, acc, pf, key0, lim, h2, a.c);
+      else
+        softmax_tile<C, false>(s, mrun, lrun, acc, pf, key0, lim, h2, a.c);
+
+      pv_tile<T, C>(acc, pf, stV(cur), j, h2);
+
+      if (more) store_tile<T, C>(regs, stK(cur ^ 1), stV(cur ^ 1), tid);
+      __syncthreads();
+    }
+
+    const float lsum = lrun + __shfl_xor(lrun, 32);
+    if (valid) store_out_row<T, C>(O + qrow_off, acc, 1.0f / lsum, h2);
+  }
+
+  // Leave the counter at zero for the next launch: the last workgroup out
+  // (all others have made their final, failing fetch) resets both words.
+  if (tid == 0) {
+    __threadfence();
+    const int done = atomicAdd(a.ctr + 1, 1);
+    if (done == (int)gridDim.x - 1) {
+      atomicExch(a.ctr, 0);
+      atomicExch(a.ctr + 1, 0);
+    }
+  }
+}
+
+}  // namespace gqa

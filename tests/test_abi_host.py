@@ -1,0 +1,131 @@
+"""CPU tests of the C ABI: the library loads, exports what include/gqa_attn.h
+declares, and rejects every invalid argument on the host before any HIP call.
+
+No kernel is launched: every call here fails validation (or, with no GPU
+visible, the device check), so the pointers passed are never dereferenced.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from mqa_flashattention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+OK, NULLP, SHAPE, GROUP, UNSUP, WS, NODEV, HIP = range(8)
+BF16, F32 = 1, 0
+# Distinct, 16-byte-aligned stand-ins for device pointers (never dereferenced).
+P = [ctypes.c_void_p(0x10000 * (n + 1)) for n in range(8)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    assert declared_functions() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIBRARY], check=True,
+                         capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [f for f in declared_functions() if f not in exported]
+    assert not missing, f"not exported: {missing}"
+    for f in declared_functions():
+        assert hasattr(binding.lib, f)
+
+
+def test_library_embeds_gfx950_code_only():
+    blob = open(binding.LIBRARY, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa--(gfx[0-9a-f]+)", blob))
+    assert targets == {b"gfx950"}, targets
+
+
+def test_status_strings():
+    for code in range(8):
+        s = binding.lib.gqa_status_string(code)
+        assert s and isinstance(s, bytes)
+    assert binding.lib.gqa_status_string(99) == b"unknown status"
+
+
+def fwd(q=P[0], k=P[1], v=P[2], o=P[3], B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=32, causal=0,
+        q_offset=0, scale=0.17, dtype=BF16, stream=None):
+    return binding.lib.gqa_attn_fwd(q, k, v, o, B, Hq, Hkv, Nq, Nk, d, causal, q_offset,
+                                    ctypes.c_float(scale), dtype, stream)
+
+
+def dec(q=P[0], kc=P[1], vc=P[2], sl=P[4], o=P[3], B=8, Hq=12, Hkv=2, Smax=2048, d=128,
+        scale=0.09, dtype=BF16, ws=P[5], ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = binding.decode_workspace_bytes(B, Hq, Hkv, Smax, d)
+    return binding.lib.gqa_attn_decode(q, kc, vc, sl, o, B, Hq, Hkv, Smax, d,
+                                       ctypes.c_float(scale), dtype, ws, ws_bytes, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(k=None), NULLP), (dict(v=None), NULLP), (dict(o=None), NULLP),
+    (dict(B=0), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=-1), SHAPE), (dict(Nq=0), SHAPE),
+    (dict(Nk=0), SHAPE), (dict(d=0), SHAPE), (dict(causal=1, q_offset=-1), SHAPE),
+    (dict(Nk=2 ** 30, d=32), SHAPE),
+    (dict(Hq=6, Hkv=4), GROUP), (dict(Hq=3, Hkv=2), GROUP),
+    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(d=16), UNSUP),
+    (dict(dtype=2), UNSUP), (dict(dtype=-1), UNSUP),
+    (dict(scale=float("inf")), UNSUP), (dict(scale=float("nan")), UNSUP),
+    (dict(q=ctypes.c_void_p(0x10008)), UNSUP), (dict(o=ctypes.c_void_p(0x40002)), UNSUP),
+])
+def test_fwd_rejects_invalid_arguments(kw, code):
+    assert fwd(**kw) == code
+    assert binding.lib.gqa_last_error_string()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(kc=None), NULLP), (dict(vc=None), NULLP),
+    (dict(sl=None), NULLP), (dict(o=None), NULLP),
+    (dict(B=0), SHAPE), (dict(Smax=0), SHAPE), (dict(Hkv=0), SHAPE),
+    (dict(Smax=2 ** 25, d=128), SHAPE),
+    (dict(Hq=12, Hkv=5), GROUP),
+    (dict(d=80), UNSUP), (dict(dtype=7), UNSUP), (dict(scale=float("-inf")), UNSUP),
+    (dict(kc=ctypes.c_void_p(0x20004)), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=16), WS), (dict(ws=ctypes.c_void_p(0x60008)), WS),
+])
+def test_decode_rejects_invalid_arguments(kw, code):
+    assert dec(**kw) == code
+    assert binding.lib.gqa_last_error_string()
+
+
+def test_decode_workspace_bytes():
+    ws = binding.decode_workspace_bytes
+    # B * Hq * ceil(Smax / 32) partial records of d accumulators + max + sum,
+    # padded to d + 4 fp32 so each record starts 16-byte aligned
+    assert ws(8, 12, 2, 2048, 128) == 8 * 12 * 64 * 132 * 4
+    assert ws(1, 1, 1, 1, 32) == 1 * 1 * 1 * 36 * 4
+    assert ws(2, 4, 2, 33, 64) == 2 * 4 * 2 * 68 * 4
+    for bad in [(0, 1, 1, 1, 32), (1, 3, 2, 1, 32), (1, 1, 1, 0, 32), (1, 1, 1, 8, 48)]:
+        assert ws(*bad) == 0
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="valid arguments would launch on a GPU")
+def test_valid_call_without_gpu_reports_no_device():
+    assert fwd() == NODEV
+    assert b"device" in binding.lib.gqa_last_error_string()
+    assert dec() == NODEV
+
+
+def test_binding_checks_tensors_before_the_library():
+    q = torch.zeros(1, 4, 8, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.attn_fwd(q, q[:, :2], q[:, :2])  # CPU tensors are refused
+    with pytest.raises(ValueError):
+        binding.attn_fwd(q.float(), q[:, :2], q[:, :2])
+    with pytest.raises(ValueError):
+        binding.attn_decode(q[:, :, 0], q, q, torch.zeros(1, dtype=torch.int32))

@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path through the C ABI against the CPU fp64 oracle.
+
+Bar: max |O_gpu - O_oracle| <= 1e-4 for fp32 inputs and <= 2e-2 for bf16
+inputs, over every compared element, with the oracle fed the exact same
+(rounded) inputs.  The named workloads run at full size: compared in full
+where the oracle takes seconds, on sampled rows plus size-independent
+properties where it does not.  Small cases span several tiles, ragged tails,
+every head-grouping mode and the method's degenerate cases.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mqa_flashattention_amd import attn_decode, attn_fwd
+from mqa_flashattention_amd.workloads import (WORKLOADS, DecodeShape, FwdShape, decode_inputs,
+                                              fwd_inputs, random_tensor)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+DEV = "cuda:0"
+
+
+def _err(gpu: torch.Tensor, ref: np.ndarray) -> float:
+    g = gpu.detach().to("cpu").double().numpy()
+    assert np.all(np.isfinite(g)), "non-finite output"
+    return float(np.max(np.abs(g - ref))) if g.size else 0.0
+
+
+def _fwd_gpu(q, k, v, **kw):
+    out = attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), **kw)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def _check_fwd(s: FwdShape, seed: int = 0, rows: int | None = None):
+    q, k, v = fwd_inputs(s, seed)
+    out = _fwd_gpu(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale)
+    if rows is None:
+        ref = oracle.attn_fwd(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale)
+        err = _err(out, ref)
+    else:
+        total = s.B * s.Hq * s.Nq
+        rng = np.random.default_rng(seed + 17)
+        ids = np.unique(np.concatenate([rng.integers(0, total, rows),
+                                        [0, s.Nq - 1, total - s.Nq, total - 1]]))
+        ref = oracle.attn_fwd_rows(q, k, v, ids, causal=s.causal, q_offset=s.q_offset,
+                                   scale=s.scale)
+        err = _err(out.reshape(-1, s.d)[torch.from_numpy(ids)], ref)
+    assert err <= TOL[s.dtype], f"{s}: max abs error {err}"
+    return q, k, v, out
+
+
+# ---------------------------------------------------------------- named workloads
+
+def test_tiny_gqa_fp32():
+    _check_fwd(WORKLOADS["tiny_gqa_f32"].fwd[0])
+
+
+def test_llama3_8b_causal_prefill_full():
+    _check_fwd(WORKLOADS["llama3_8b_prefill"].fwd[0])
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2], ids=["mha_hkv16", "gqa_hkv4", "mqa_hkv1"])
+def test_mha_gqa_mqa_sweep_sampled(variant):
+    s = WORKLOADS["mha_gqa_mqa_sweep"].fwd[variant]
+    q, k, v, out = _check_fwd(s, rows=384)
+    # Size-independent property: GQA equals MHA with each K/V head repeated.
+    if s.Hkv < s.Hq:
+        g = s.Hq // s.Hkv
+        mha = _fwd_gpu(q, k.repeat_interleave(g, 1).contiguous(),
+                       v.repeat_interleave(g, 1).contiguous(), scale=s.scale)
+        diff = float((mha.double() - out.double()).abs().max())
+        assert diff <= TOL[s.dtype], f"GQA vs replicated MHA differ by {diff}"
+
+
+def test_chunked_prefill_full():
+    _check_fwd(WORKLOADS["chunked_prefill_4k"].fwd[0])
+
+
+def test_kv_decode_full():
+    s = WORKLOADS["kv_decode_b8"].decode
+    q, kc, vc, lens = decode_inputs(s, 0)
+    out = attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV), scale=s.scale)
+    torch.cuda.synchronize()
+    ref = oracle.attn_decode(q, kc, vc, lens, scale=s.scale)
+    err = _err(out, ref)
+    assert err <= TOL[s.dtype], f"decode max abs error {err}"
+    # Slots at or past each row's length are never read: NaN there changes nothing.
+    kp, vp = kc.clone(), vc.clone()
+    for b in range(s.B):
+        kp[b, :, int(lens[b]):] = float("nan")
+        vp[b, :, int(lens[b]):] = float("nan")
+    out2 = attn_decode(q.to(DEV), kp.to(DEV), vp.to(DEV), lens.to(DEV), scale=s.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), out2.cpu())
+
+
+# ---------------------------------------------------------------- small-case matrix
+# MHA (g=1), GQA (g=2, 4, 6) and MQA (Hkv=1) as in the "Kernel 9" test matrix
+# of the BootstrapAI log, over head dims, ragged lengths and causal offsets.
+
+MODES = [(4, 4), (4, 2), (8, 2), (12, 2), (8, 1)]
+LENGTHS = [(1, 1), (17, 17), (63, 65), (65, 63), (129, 129), (40, 200), (200, 40)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("hq,hkv", MODES)
+def test_small_matrix(dtype, d, hq, hkv):
+    seed = 1000 + d + 10 * hq + hkv
+    for n, (nq, nk) in enumerate(LENGTHS):
+        for causal, off in ((False, 0), (True, 0), (True, max(0, nk - nq)), (True, 7)):
+            s = FwdShape(2, hq, hkv, nq, nk, d, causal, off, dtype)
+            _check_fwd(s, seed + n)
+
+
+@pytest.mark.parametrize("g", [40, 160])
+def test_large_groups(g):
+    """More query heads per K/V head than one unit (128 columns) or one decode
+    wave (32 columns) holds."""
+    s = FwdShape(1, g, 1, 37, 70, 64, True, 5)
+    _check_fwd(s, 5)
+    ds = DecodeShape(2, g, 1, 90, 64, 1, 90)
+    q, kc, vc, lens = decode_inputs(ds, 6)
+    out = attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV))
+    torch.cuda.synchronize()
+    assert _err(out, oracle.attn_decode(q, kc, vc, lens)) <= TOL[ds.dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_decode_lengths(dtype, d):
+    B, Hq, Hkv, Smax = 9, 6, 2, 300
+    q = random_tensor((B, Hq, d), 1, dtype)
+    kc = random_tensor((B, Hkv, Smax, d), 2, dtype)
+    vc = random_tensor((B, Hkv, Smax, d), 3, dtype)
+    lens = torch.tensor([1, 31, 32, 33, 64, 65, 299, 300, 150], dtype=torch.int32)
+    out = attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV))
+    torch.cuda.synchronize()
+    assert _err(out, oracle.attn_decode(q, kc, vc, lens)) <= TOL[dtype]
+
+
+def test_decode_empty_and_overlong_rows():
+    """n = clamp(seqlens, 0, Smax): zero/negative lengths give zero rows,
+    lengths beyond the capacity read the whole cache."""
+    B, Hq, Hkv, Smax, d = 4, 4, 1, 70, 128
+    q = random_tensor((B, Hq, d), 11, torch.bfloat16)
+    kc = random_tensor((B, Hkv, Smax, d), 12, torch.bfloat16)
+    vc = random_tensor((B, Hkv, Smax, d), 13, torch.bfloat16)
+    lens = torch.tensor([0, -5, 70, 1000], dtype=torch.int32)
+    out = attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV)).cpu()
+    torch.cuda.synchronize()
+    assert torch.all(out[:2] == 0)
+    assert _err(out, oracle.attn_decode(q, kc, vc, lens)) <= 2e-2
+
+
+def test_decode_matches_single_query_forward():
+    """Decode of row b equals the forward pass with one query over its n keys."""
+    s = DecodeShape(3, 8, 2, 257, 128, 1, 257)
+    q, kc, vc, lens = decode_inputs(s, 21)
+    dec = attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV)).cpu().double()
+    for b in range(s.B):
+        n = int(lens[b])
+        f = _fwd_gpu(q[b:b + 1, :, None, :].contiguous(), kc[b:b + 1, :, :n].contiguous(),
+                     vc[b:b + 1, :, :n].contiguous())
+        assert float((f[0, :, 0].double() - dec[b]).abs().max()) <= 2e-2
+
+
+# ---------------------------------------------------------------- properties / edge cases
+
+def test_causal_row0_and_constant_v_exact():
+    """bf16: causal row 0 returns V[0] bit-exactly; a constant V comes back exactly."""
+    s = FwdShape(1, 8, 2, 130, 130, 128, True, 0)
+    q, k, v = fwd_inputs(s, 3)
+    out = _fwd_gpu(q, k, v, causal=True)
+    for h in range(8):
+        assert torch.equal(out[0, h, 0], v[0, h // 4, 0])
+    vconst = torch.full_like(v, -1.25)
+    out = _fwd_gpu(q, k, vconst, causal=True)
+    assert torch.all(out == -1.25)
+
+
+def test_chunked_equals_rows_of_full_pass():
+    N, off, n = 700, 450, 130
+    s = FwdShape(1, 8, 2, N, N, 64, True, 0)
+    q, k, v = fwd_inputs(s, 8)
+    full = _fwd_gpu(q, k, v, causal=True)
+    part = _fwd_gpu(q[:, :, off:off + n].contiguous(), k, v, causal=True, q_offset=off)
+    assert float((full[:, :, off:off + n].double() - part.double()).abs().max()) <= 2e-2
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 3.0])
+def test_unusual_scales(scale):
+    s = FwdShape(1, 4, 2, 70, 90, 64, True, 20)
+    q, k, v = fwd_inputs(s, 9)
+    out = _fwd_gpu(q, k, v, causal=True, q_offset=20, scale=scale)
+    ref = oracle.attn_fwd(q, k, v, causal=True, q_offset=20, scale=scale)
+    assert _err(out, ref) <= 2e-2
+
+
+def test_output_guard_bands_untouched():
+    s = FwdShape(2, 4, 2, 77, 77, 128, True, 0)
+    q, k, v = fwd_inputs(s, 10)
+    buf = torch.full((4, 4, 77, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[1:3]
+    attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[0] == 7.0) and torch.all(buf[3] == 7.0)
+    ref = oracle.attn_fwd(q, k, v, causal=True)
+    assert _err(out, ref) <= 2e-2
+
+
+def test_bitwise_deterministic_runs():
+    """The atomic scheduler only changes which workgroup runs a unit; each
+    output's arithmetic order is fixed, so repeated runs agree bit for bit."""
+    s = WORKLOADS["llama3_8b_prefill"].fwd[0]
+    q, k, v = (t.to(DEV) for t in fwd_inputs(s, 0))
+    first = attn_fwd(q, k, v, causal=True)
+    for _ in range(10):
+        again = attn_fwd(q, k, v, causal=True)
+        assert torch.equal(first, again)
+    ds = WORKLOADS["kv_decode_b8"].decode
+    dq, dk, dv, dl = (t.to(DEV) for t in decode_inputs(ds, 0))
+    d1 = attn_decode(dq, dk, dv, dl)
+    for _ in range(10):
+        assert torch.equal(d1, attn_decode(dq, dk, dv, dl))
+    torch.cuda.synchronize()
+
+
+def test_two_streams_keep_separate_schedulers():
+    s = FwdShape(1, 8, 2, 300, 300, 64, True, 0)
+    q, k, v = (t.to(DEV) for t in fwd_inputs(s, 12))
+    ref = attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for st in (s1, s2):
+        with torch.cuda.stream(st):
+            outs.append([attn_fwd(q, k, v, causal=True) for _ in range(3)])
+    torch.cuda.synchronize()
+    for group in outs:
+        for o in group:
+            assert torch.equal(o, ref)
