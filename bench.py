@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the GQA attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * prefill: LLaMA-3-8B-shaped causal prefill, bf16 in / fp32 accumulate,
+    B=1 Hq=32 Hkv=8 N=2048 d=128 (gqa_attn_fwd), and
+  * decode:  KV-cache decode, bf16 cache, B=8 Hq=12 Hkv=2 d=128, lengths
+    U[512, 2048] (gqa_attn_decode: split kernel + combine kernel).
+Both are checked against the CPU oracle before anything is timed.
+
+value = prefill TFLOP/s (algorithmic FLOPs = 4 * B * Hq * d * visible
+(query, key) pairs, causal-masked pairs not counted) over the prefill
+launch's event-timed average duration.  The decode part is reported beside
+it in GB/s of algorithmic bytes (the K/V rows each sequence needs, plus q, o
+and the lengths) over its event-timed duration; each decode call reads a
+different one of several independently drawn caches so the reads come from
+HBM, not from the 256 MB Infinity Cache.
+
+`roofline` is for the prefill kernel (the dominant kernel of a step):
+bf16 dense MFMA peak 2500 TFLOP/s.  `traffic` comes from the committed
+rocprofv3 counter summary when it was taken from the current kernel sources,
+else null.  `cpu_baseline` times the fp64 oracle on the host on the full
+prefill workload.
+
+Only one GPU: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_llama3_8b_counters.json")
+KERNEL_SOURCES = ["attn_tile.hpp", "prefill_kernel.hpp", "decode_kernel.hpp", "gqa_attn.hip"]
+DECODE_SETS = 48  # 48 x 16 MiB of caches > 256 MB Infinity Cache
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mqa_flashattention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_flops(s) -> float:
+    """4 FLOPs per (query, key, d) visible triple: QK^T and PV, 2 FLOPs per MAC."""
+    return 4.0 * s.B * s.Hq * s.d * s.visible_pairs_per_head()
+
+
+def decode_bytes(s, lens) -> float:
+    """K and V rows each row needs, plus q, o and the lengths."""
+    elem = 2 if str(s.dtype).endswith("bfloat16") else 4
+    kv = float(sum(int(n) for n in lens)) * s.Hkv * s.d * 2 * elem
+    return kv + 2.0 * s.B * s.Hq * s.d * elem + 4.0 * s.B
+
+
+def fwd_bytes(s) -> float:
+    elem = 2 if str(s.dtype).endswith("bfloat16") else 4
+    return elem * (2.0 * s.B * s.Hq * s.Nq * s.d + 2.0 * s.B * s.Hkv * s.Nk * s.d)
+
+
+def traffic_from_counters():
+    """Measured HBM bytes per prefill launch, if the counters match the sources."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def check(out, ref, tol, what):
+    import numpy as np
+    err = float(np.max(np.abs(out.detach().cpu().double().numpy() - ref)))
+    if not err <= tol:
+        raise SystemExit(f"{what}: parity check failed, max abs error {err} > {tol}")
+    return err
+
+
+def time_fwd_workload(s, steps, warmup):
+    """Event-timed average duration (ms) of one gqa_attn_fwd launch."""
+    import torch
+    from mqa_flashattention_amd import attn_fwd
+    from mqa_flashattention_amd.workloads import fwd_inputs
+    q, k, v = (t.cuda() for t in fwd_inputs(s, 0))
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        attn_fwd(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        attn_fwd(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--all", action="store_true",
+                    help="also time the MHA/GQA/MQA sweep and the chunked prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention "
+              "path is not sharded across GPUs in this build.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import oracle  # test infrastructure: parity gate and CPU baseline only
+    from mqa_flashattention_amd import attn_decode, attn_fwd, decode_workspace_bytes
+    from mqa_flashattention_amd.workloads import WORKLOADS, decode_inputs, fwd_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ps = WORKLOADS["llama3_8b_prefill"].fwd[0]
+    ds = WORKLOADS["kv_decode_b8"].decode
+
+    # ---------------- inputs (seed 0, resident in HBM before timing)
+    q_h, k_h, v_h = fwd_inputs(ps, 0)
+    q, k, v = q_h.to(dev), k_h.to(dev), v_h.to(dev)
+    o = torch.empty_like(q)
+    dq_h, dk_h, dv_h, dl_h = decode_inputs(ds, 0)
+    dq, dl = dq_h.to(dev), dl_h.to(dev)
+    kcs, vcs = [dk_h.to(dev)], [dv_h.to(dev)]
+    gen = torch.Generator(device=dev).manual_seed(1)
+    for _ in range(DECODE_SETS - 1):
+        kcs.append(torch.randn(dk_h.shape, generator=gen, device=dev).to(ds.dtype))
+        vcs.append(torch.randn(dv_h.shape, generator=gen, device=dev).to(ds.dtype))
+    do = torch.empty_like(dq)
+    ws = torch.empty(decode_workspace_bytes(ds.B, ds.Hq, ds.Hkv, ds.Smax, ds.d),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        attn_fwd(q, k, v, causal=True, scale=ps.scale, out=o)
+
+    def decode(i):
+        attn_decode(dq, kcs[i], vcs[i], dl, scale=ds.scale, out=do, workspace=ws)
+
+    # ---------------- parity gate (before any timing)
+    prefill()
+    decode(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ref = oracle.attn_fwd(q_h, k_h, v_h, causal=True, scale=ps.scale)
+    oracle_s = time.perf_counter() - t0
+    prefill_err = check(o, ref, 2e-2, "prefill")
+    t0 = time.perf_counter()
+    dref = oracle.attn_decode(dq_h, dk_h, dv_h, dl_h, scale=ds.scale)
+    oracle_dec_s = time.perf_counter() - t0
+    decode_err = check(do, dref, 2e-2, "decode")
+    print(f"# parity ok: prefill max err {prefill_err:.2e}, decode max err {decode_err:.2e}",
+          file=sys.stderr, flush=True)
+
+    # ---------------- warmup + timed steps
+    for i in range(args.warmup):
+        prefill()
+        decode(i % DECODE_SETS)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        ev[i][0].record()
+        prefill()
+        ev[i][1].record()
+        decode(i % DECODE_SETS)
+        ev[i][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / K
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+
+    flops = prefill_flops(ps)
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    lens = dl_h.tolist()
+    dbytes = decode_bytes(ds, lens)
+    gbps = dbytes / (dec_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "GQA prefill TFLOP/s (% MFMA peak) + decode KV GB/s (% HBM) on 1 MI355X",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V, decode lengths U[512,2048]",
+        "config": {
+            "workload": "llama3_8b_prefill + kv_decode_b8",
+            "prefill": {"B": ps.B, "Hq": ps.Hq, "Hkv": ps.Hkv, "N": ps.Nq, "d": ps.d,
+                        "causal": True, "algorithmic_gflop": round(flops / 1e9, 4)},
+            "decode": {"B": ds.B, "Hq": ds.Hq, "Hkv": ds.Hkv, "Smax": ds.Smax, "d": ds.d,
+                       "sum_seqlens": int(sum(lens)), "cache_sets": DECODE_SETS,
+                       "algorithmic_mb": round(dbytes / 1e6, 4)},
+        },
+        "prefill": {"ms": round(pre_ms, 5), "tflops": round(tflops, 3),
+                    "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4)},
+        "decode": {"ms": round(dec_ms, 5), "value": round(gbps, 2), "unit": "GB/s",
+                   "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                   "note": "split + combine launches, event-timed, HBM-cold caches"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_counters()},
+        "wall_s_timed": round(wall, 4),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = {
+            "value": round(flops / oracle_s / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the whole prefill workload (B1 Hq32 Hkv8 N2048 d128 causal), fp64, "
+                      f"{oracle_s:.2f} s wall",
+            "decode_gbps": round(dbytes / oracle_dec_s / 1e9, 4),
+        }
+
+    if args.all:
+        extra = {}
+        for name in ("mha_gqa_mqa_sweep", "chunked_prefill_4k"):
+            for s in WORKLOADS[name].fwd:
+                ms = time_fwd_workload(s, max(10, K // 2), 3)
+                tf = prefill_flops(s) / (ms * 1e-3) / 1e12
+                extra[f"{name}[Hkv={s.Hkv}]"] = {"ms": round(ms, 5), "tflops": round(tf, 2),
+                                                 "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        result["other_workloads"] = extra
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

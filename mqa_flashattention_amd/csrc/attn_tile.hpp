@@ -19,7 +19,8 @@
 // c = |scale| log2(e) -- the running-max rescale exp(m_old - m_new) of the
 // tiled kernel in the BootstrapAI evolution log ("Kernel 2 -- tiling"),
 // evaluated with the hardware base-2 exponential.  A negative scale is
-// applied by negating Q (exact in bf16 and fp32) so c stays >= 0.
+// applied by negating Q (exact in bf16 and fp32) so c stays > 0; a zero
+// scale is floored to a c so small that every weight rounds to exactly 1.
 // In the bf16 path p is rounded to bf16 for the PV MFMA and l sums those
 // same rounded values, so the normalisation matches the weights used.
 //
@@ -101,10 +102,15 @@ struct TileCfg {
   static constexpr int K_CHUNKS = BC * ROW_CHUNKS;
   static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
   // bf16 V is transposed while staging: a thread takes VK consecutive keys of
-  // one 8-element d-chunk and writes VK-key runs of 8 V^T rows.
+  // one 8-element d-chunk and writes VK-key runs of 8 V^T rows.  Adjacent
+  // threads take adjacent key groups of the same d-chunk, so one LDS write
+  // instruction fills whole V^T rows (bank-conflict free with the padded
+  // stride); each global load instruction still reads 64 contiguous bytes
+  // per row.
   static constexpr int VK_RAW = K_CHUNKS / NT;
   static constexpr int VK = F32 ? 1 : (VK_RAW >= 8 ? 8 : (VK_RAW >= 4 ? 4 : (VK_RAW >= 2 ? 2 : 1)));
-  static constexpr int V_BLOCKS = (BC / VK) * ROW_CHUNKS;
+  static constexpr int KGROUPS = BC / VK;
+  static constexpr int V_BLOCKS = KGROUPS * ROW_CHUNKS;
   static constexpr int V_PER_T = F32 ? K_PER_T : (V_BLOCKS + NT - 1) / NT;
   static constexpr int V_LOADS = F32 ? K_PER_T : V_PER_T * VK;
   // MFMA operand fragments of the wave's 32 queries.
@@ -128,51 +134,54 @@ struct TileRegs {
 // Issue the global loads of one K/V tile -- keys key0 .. key0+BC-1 of one
 // head whose rows start at kbase / vbase -- into registers.  Rows at or
 // beyond nkeys read as zero, so they add nothing even before masking.
-// Consecutive threads take consecutive 16-byte chunks of a row, so a wave's
-// load instruction covers whole rows.
-template <typename T, class C>
-__device__ __forceinline__ void load_tile(TileRegs<C>& r, const T* __restrict__ kbase,
-                                          const T* __restrict__ vbase, int key0, int nkeys,
-                                          int tid) {
+// For K, consecutive threads take consecutive 16-byte chunks of a row, so a
+// wave's load instruction covers whole rows.
+template <typename T, class C, bool CHECKED>
+__device__ __forceinline__ void load_tile_impl(TileRegs<C>& r, const T* __restrict__ kbase,
+                                               const T* __restrict__ vbase, int key0, int nkeys,
+                                               int tid) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int n = 0; n < C::K_PER_T; ++n) {
     const int id = tid + n * C::NT;
     const int row = id / C::ROW_CHUNKS;
     const int col = id % C::ROW_CHUNKS;
     const int key = key0 + row;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if ((C::K_CHUNKS % C::NT == 0 || id < C::K_CHUNKS) && key < nkeys)
-      val = *reinterpret_cast<const u32x4*>(kbase + (size_t)key * C::D + col * C::EPC);
-    r.k[n] = val;
+    const bool ok = (C::K_CHUNKS % C::NT == 0 || id < C::K_CHUNKS) && (!CHECKED || key < nkeys);
+    const size_t off = (size_t)key * C::D + col * C::EPC;
+    r.k[n] = ok ? *reinterpret_cast<const u32x4*>(kbase + off) : zero;
+    if constexpr (C::F32) r.v[n] = ok ? *reinterpret_cast<const u32x4*>(vbase + off) : zero;
   }
-  if constexpr (C::F32) {
-#pragma unroll
-    for (int n = 0; n < C::K_PER_T; ++n) {
-      const int id = tid + n * C::NT;
-      const int row = id / C::ROW_CHUNKS;
-      const int col = id % C::ROW_CHUNKS;
-      const int key = key0 + row;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if ((C::K_CHUNKS % C::NT == 0 || id < C::K_CHUNKS) && key < nkeys)
-        val = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * C::D + col * C::EPC);
-      r.v[n] = val;
-    }
-  } else {
+  if constexpr (!C::F32) {
 #pragma unroll
     for (int n = 0; n < C::V_PER_T; ++n) {
       const int id = tid + n * C::NT;
-      const int dc = id % C::ROW_CHUNKS;
-      const int kg = id / C::ROW_CHUNKS;
+      const int kg = id % C::KGROUPS;
+      const int dc = id / C::KGROUPS;
 #pragma unroll
       for (int e = 0; e < C::VK; ++e) {
         const int key = key0 + kg * C::VK + e;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if ((C::V_BLOCKS % C::NT == 0 || id < C::V_BLOCKS) && key < nkeys)
-          val = *reinterpret_cast<const u32x4*>(vbase + (size_t)key * C::D + dc * 8);
-        r.v[n * C::VK + e] = val;
+        const bool ok =
+            (C::V_BLOCKS % C::NT == 0 || id < C::V_BLOCKS) && (!CHECKED || key < nkeys);
+        r.v[n * C::VK + e] =
+            ok ? *reinterpret_cast<const u32x4*>(vbase + (size_t)key * C::D + dc * 8) : zero;
       }
     }
   }
+}
+
+// FAST_FULL: tiles wholly inside the key range (all but a ragged last one)
+// take a copy of the loads without per-row bounds checks.  Decode uses it;
+// the prefill loop measured faster with the single checked form, whose
+// loads the compiler places earlier.
+template <typename T, class C, bool FAST_FULL>
+__device__ __forceinline__ void load_tile(TileRegs<C>& r, const T* __restrict__ kbase,
+                                          const T* __restrict__ vbase, int key0, int nkeys,
+                                          int tid) {
+  if (FAST_FULL && key0 + C::BC <= nkeys)
+    load_tile_impl<T, C, false>(r, kbase, vbase, key0, nkeys, tid);
+  else
+    load_tile_impl<T, C, true>(r, kbase, vbase, key0, nkeys, tid);
 }
 
 // Element i (0..7) of a 16-byte chunk of bf16, from VK chunks, packed as a
@@ -239,8 +248,8 @@ __device__ __forceinline__ void store_tile(const TileRegs<C>& r, T* __restrict__
     for (int n = 0; n < C::V_PER_T; ++n) {
       const int id = tid + n * C::NT;
       if (C::V_BLOCKS % C::NT == 0 || id < C::V_BLOCKS) {
-        const int dc = id % C::ROW_CHUNKS;
-        const int kg = id / C::ROW_CHUNKS;
+        const int kg = id % C::KGROUPS;
+        const int dc = id / C::KGROUPS;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           *reinterpret_cast<typename Run::type*>(Vs + (dc * 8 + i) * C::VSTR + kg * C::VK) =
@@ -291,39 +300,60 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const typename C::Fr
   }
 }
 
-// Online-softmax update for one tile.  key0 is the absolute index of the
-// tile's first key; keys > lim are excluded when MASK is set.  On return
-// pf holds this tile's probabilities as the B operand of the PV MFMA, and
-// m, l, acc are rescaled to the new running max.
-template <class C, bool MASK>
-__device__ __forceinline__ void softmax_tile(f32x16 (&s)[C::KB], float& m, float& l,
-                                             f32x16 (&acc)[C::DB],
-                                             typename C::Frag (&pf)[C::KB][C::PF], int key0,
-                                             int lim, int h2, float c) {
+// ---- online softmax, one tile at a time (composed in softmax_pv_step).
+// c must be > 0 (the host floors it), so masked scores (-inf) give weights
+// of exactly 0.
+
+// Exclude keys > lim of a tile starting at key key0 (scores set to -inf).
+template <class C>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[C::KB], int key0, int lim, int h2) {
+  const int rel = lim - key0 - 8 * h2;  // key_of_reg(r, h2) - 8*h2 <= rel  <=> visible
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * kb + 16 * (r / 8) + (r % 8) > rel) s[kb][r] = kNegInf;
+}
+
+// Row maximum of a tile's scores across both half-waves (each lane holds
+// 16*KB scores of its query; the other half-wave holds the rest).
+template <class C>
+__device__ __forceinline__ float tile_rowmax(const f32x16 (&s)[C::KB]) {
   float mt = kNegInf;
 #pragma unroll
-  for (int kb = 0; kb < C::KB; ++kb) {
+  for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[kb][r];
-      if (MASK && key0 + 32 * kb + key_of_reg(r, h2) > lim) x = kNegInf;
-      s[kb][r] = x;
-      mt = fmaxf(mt, x);
-    }
-  }
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
+    for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
+  return fmaxf(mt, __shfl_xor(mt, 32));
+}
+
+// Raise the running reference to m_new = max(m, mt) and rescale l and acc by
+// alpha = 2^((m - m_new) c) (alpha = 0 while m is still -inf).
+template <class C>
+__device__ __forceinline__ void raise_reference(float& m, float& l, f32x16 (&acc)[C::DB],
+                                                float mt, float c) {
   const float m_new = fmaxf(m, mt);
-  const float alpha = (m == kNegInf) ? 0.f : fast_exp2((m - m_new) * c);
-  const float mc = m_new * c;
+  const float alpha = fast_exp2((m - m_new) * c);
+  m = m_new;
+  l *= alpha;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+}
+
+// Weights p = 2^(s c - m c) of one tile against reference m, as the B operand
+// of the PV MFMA; returns their sum (of the bf16-rounded values in the bf16
+// path, via v_dot2_f32_bf16 against (1, 1)).
+template <class C>
+__device__ __forceinline__ float tile_weights(const f32x16 (&s)[C::KB], float m, float c,
+                                              typename C::Frag (&pf)[C::KB][C::PF]) {
+  const float mc = m * c;
   float lt = 0.f;
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) {
     if constexpr (C::F32) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float x = s[kb][r];
-        float p = fast_exp2(__builtin_fmaf(x, c, -mc));
-        if (MASK && x == kNegInf) p = 0.f;
+        const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));
         pf[kb][r] = p;
         lt += p;
       }
@@ -333,24 +363,19 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[C::KB], float& m, float
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float x0 = s[kb][8 * hk + 2 * e];
-          const float x1 = s[kb][8 * hk + 2 * e + 1];
-          float p0 = fast_exp2(__builtin_fmaf(x0, c, -mc));
-          float p1 = fast_exp2(__builtin_fmaf(x1, c, -mc));
-          if (MASK && x0 == kNegInf) p0 = 0.f;
-          if (MASK && x1 == kNegInf) p1 = 0.f;
-          const uint32_t pk = pack_bf16(p0, p1);
-          lt += bf16_lo(pk) + bf16_hi(pk);
-          w[e] = pk;
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * hk + 2 * e], c, -mc));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * hk + 2 * e + 1], c, -mc));
+          bf16x2 pk;
+          pk.x = (__bf16)p0;
+          pk.y = (__bf16)p1;
+          lt = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, lt, false);
+          w[e] = __builtin_bit_cast(uint32_t, pk);
         }
         pf[kb][hk] = __builtin_bit_cast(bf16x8, w);
       }
     }
   }
-  l = alpha * l + lt;
-  m = m_new;
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+  return lt;
 }
 
 // acc[db] += V^T P^T for one tile (O^T rows 32*db .. 32*db+31).
@@ -378,6 +403,24 @@ __device__ __forceinline__ void pv_tile(f32x16 (&acc)[C::DB],
       }
     }
   }
+}
+
+// One online-softmax + PV step on a (masked) score tile s:
+//   m' = max(m, rowmax s); l, acc scaled by alpha = 2^((m - m') c);
+//   p = 2^(s c - m' c); l += sum p; acc += V^T P^T.
+// The rescale is unconditional.  Skipping it while the max grows little
+// (a wave-uniform branch) measured no faster on gfx950: the branch merge
+// either copied the MFMA accumulators or, in the variant that avoided the
+// copies, saved no time.
+template <typename T, class C>
+__device__ __forceinline__ void softmax_pv_step(f32x16 (&s)[C::KB], float& m, float& l,
+                                                f32x16 (&acc)[C::DB], const T* __restrict__ Vs,
+                                                int lane32, int h2, float c) {
+  const float mt = tile_rowmax<C>(s);
+  raise_reference<C>(m, l, acc, mt, c);
+  typename C::Frag pf[C::KB][C::PF];
+  l += tile_weights<C>(s, m, c, pf);
+  pv_tile<T, C>(acc, pf, Vs, lane32, h2);
 }
 
 // Store one query row of O from the O^T accumulator: this lane holds d =

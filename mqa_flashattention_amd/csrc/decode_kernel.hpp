@@ -12,7 +12,7 @@
 // accumulator) to the workspace.  Splits past a row's length exit at once;
 // the lengths live on the device and are read by the kernels.
 //
-// The combine pass merges a row's partials in split order:
+// The combine pass merges a row's partials (in a fixed order):
 //   M = max_s m_s,  w_s = 2^(m_s - M),  O = sum_s w_s acc_s / sum_s w_s l_s
 // (m is kept in base-2 scaled units).  The fixed order makes the result
 // bit-reproducible run to run.
@@ -81,23 +81,23 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
+  // Two register stages: the loads of tiles t+1 and t+2 are in flight while
+  // tile t is computed, so a split of up to two tiles costs one memory
+  // round trip.
   const int ntiles = (ntok + 31) / 32;
-  TileRegs<C> regs;
-  load_tile<T, C>(regs, kbase, vbase, 0, ntok, lane);
+  TileRegs<C> regs[2];
+  load_tile<T, C, true>(regs[0], kbase, vbase, 0, ntok, lane);
+  if (ntiles > 1) load_tile<T, C, true>(regs[1], kbase, vbase, 32, ntok, lane);
   for (int kt = 0; kt < ntiles; ++kt) {
-    store_tile<T, C>(regs, Ks, Vs, lane);
+    store_tile<T, C>(regs[kt & 1], Ks, Vs, lane);
     __syncthreads();
-    if (kt + 1 < ntiles) load_tile<T, C>(regs, kbase, vbase, (kt + 1) * 32, ntok, lane);
+    if (kt + 2 < ntiles) load_tile<T, C, true>(regs[kt & 1], kbase, vbase, (kt + 2) * 32, ntok, lane);
 
     f32x16 s[C::KB];
     qk_tile<T, C>(s, qf, Ks, j, h2);
-    typename C::Frag pf[C::KB][C::PF];
     const int key0 = kt * 32;
-    if (key0 + 32 > ntok)
-      softmax_tile<C, true>(s, mrun, lrun, acc, pf, key0, ntok - 1, h2, a.c);
-    else
-      softmax_tile<C, false>(s, mrun, lrun, acc, pf, key0, ntok - 1, h2, a.c);
-    pv_tile<T, C>(acc, pf, Vs, j, h2);
+    if (key0 + 32 > ntok) mask_tile<C>(s, key0, ntok - 1, h2);
+    softmax_pv_step<T, C>(s, mrun, lrun, acc, Vs, j, h2, a.c);
     __syncthreads();
   }
 
@@ -120,50 +120,81 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// grid (Hq, B), 64 threads; thread t produces d = t, t+64, ...
+// grid (Hq, B), 256 threads.  Every partial of the row is read in parallel:
+// first the split maxima (one per thread), then the accumulators, with
+// thread t taking 16-byte chunk t % (D/4) of the splits s = t / (D/4) mod G;
+// the G group sums are added through LDS in fixed order.
 template <typename T, int D>
-__global__ void __launch_bounds__(64) decode_combine_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
+  constexpr int REC = D + 4;    // floats per partial record
+  constexpr int CH = D / 4;     // float4 chunks per record
+  constexpr int G = 256 / CH;   // split groups
+  constexpr bool F32 = std::is_same<T, float>::value;
+  __shared__ float s_red[4];
+  __shared__ float4 s_acc[G][CH];
+  __shared__ float s_l[G];
+
+  const int tid = threadIdx.x;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int n = clamp_len(a.seqlens[b], a.Smax);
   T* orow = reinterpret_cast<T*>(a.o) + ((size_t)b * a.Hq + h) * D;
-  constexpr bool F32 = std::is_same<T, float>::value;
   if (n == 0) {
-    for (int d = threadIdx.x; d < D; d += 64) {
+    for (int d = tid; d < D; d += 256) {
       if constexpr (F32) orow[d] = 0.f;
       else orow[d] = 0;
     }
     return;
   }
   const int ns = (n + a.S_TOK - 1) / a.S_TOK;
-  const float* part = a.ws + ((size_t)b * a.Hq + h) * a.NS * (D + 4);
-  float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part[s * (D + 4) + D]);
+  const float* part = a.ws + ((size_t)b * a.Hq + h) * a.NS * REC;
+
+  // ---- M = max over splits of the scaled maxima
+  float mloc = kNegInf;
+  for (int s = tid; s < ns; s += 256) mloc = fmaxf(mloc, part[(size_t)s * REC + D]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+  if ((tid & 63) == 0) s_red[tid >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+
+  // ---- weighted sums, G split groups in parallel
+  const int c = tid % CH;
+  const int grp = tid / CH;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  float accv[(D + 63) / 64];
-#pragma unroll
-  for (int u = 0; u < (D + 63) / 64; ++u) accv[u] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float* ps = part + s * (D + 4);
+#pragma unroll 4
+  for (int s = grp; s < ns; s += G) {
+    const float* ps = part + (size_t)s * REC;
     const float wgt = fast_exp2(ps[D] - M);
+    const float4 v = *reinterpret_cast<const float4*>(ps + 4 * c);
+    acc.x += wgt * v.x;
+    acc.y += wgt * v.y;
+    acc.z += wgt * v.z;
+    acc.w += wgt * v.w;
     L += wgt * ps[D + 1];
-#pragma unroll
-    for (int u = 0; u < (D + 63) / 64; ++u) {
-      const int d = threadIdx.x + 64 * u;
-      if (d < D) accv[u] += wgt * ps[d];
-    }
   }
-  const float inv = 1.0f / L;
+  s_acc[grp][c] = acc;
+  if (c == 0) s_l[grp] = L;
+  __syncthreads();
+  if (tid < CH) {
+    float4 t = s_acc[0][tid];
+    float lt = s_l[0];
 #pragma unroll
-  for (int u = 0; u < (D + 63) / 64; ++u) {
-    const int d = threadIdx.x + 64 * u;
-    if (d < D) {
-      const float x = accv[u] * inv;
-      if constexpr (F32) {
-        orow[d] = x;
-      } else {
-        orow[d] = (uint16_t)(pack_bf16(x, 0.f) & 0xffffu);
-      }
+    for (int g2 = 1; g2 < G; ++g2) {
+      const float4 u = s_acc[g2][tid];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+      lt += s_l[g2];
+    }
+    const float inv = 1.0f / lt;
+    if constexpr (F32) {
+      *reinterpret_cast<float4*>(orow + 4 * tid) = float4{t.x * inv, t.y * inv, t.z * inv, t.w * inv};
+    } else {
+      *reinterpret_cast<u32x2*>(orow + 4 * tid) =
+          u32x2{pack_bf16(t.x * inv, t.y * inv), pack_bf16(t.z * inv, t.w * inv)};
     }
   }
 }

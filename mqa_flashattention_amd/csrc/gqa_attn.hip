@@ -41,6 +41,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool head_dim_ok(int d) { return d == 32 || d == 64 || d == 128; }
 
+// |scale| * log2(e), floored at 1e-30: the kernels need a positive factor
+// (masked scores are -inf and must give weight exp2(-inf) = 0).  For a zero
+// scale every |score - max| * 1e-30 is below 2^-24, so each weight is exactly
+// 1 and the result is the plain mean, as the definition says.
+float softmax_coef(float scale) {
+  const float c = std::fabs(scale) * gqa::kLog2e;
+  return c > 1e-30f ? c : 1e-30f;
+}
+
 constexpr long long kIntMax = 2147483647LL;
 
 struct DeviceInfo {
@@ -90,8 +99,11 @@ __global__ void zero_ints_kernel(int* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
 }
 
-// Two-int scheduler counter of one (device, stream), zeroed in stream order
-// on first use; each persistent launch leaves it at zero when it ends.
+// Scheduler counters of one (device, stream): one per work queue plus a
+// finished-workgroup count, zeroed in stream order on first use; each
+// persistent launch leaves them at zero when it ends.
+constexpr int kCounterInts = 16;
+static_assert(kCounterInts >= gqa::kNumQueues + 1, "counter block too small");
 int stream_counter(int dev, hipStream_t stream, int** out) {
   std::lock_guard<std::mutex> lock(g_mu);
   const auto key = std::make_pair(dev, reinterpret_cast<void*>(stream));
@@ -101,9 +113,9 @@ int stream_counter(int dev, hipStream_t stream, int** out) {
     return GQA_OK;
   }
   int* p = nullptr;
-  hipError_t e = hipMalloc(&p, 2 * sizeof(int));
+  hipError_t e = hipMalloc(&p, kCounterInts * sizeof(int));
   if (e != hipSuccess) return hip_fail(e, "hipMalloc(scheduler counter)");
-  hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, stream, p, 2);
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, stream, p, kCounterInts);
   e = hipGetLastError();
   if (e != hipSuccess) {
     (void)hipFree(p);
@@ -199,7 +211,7 @@ int launch_decode(gqa::DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode split kernel launch");
   hipLaunchKernelGGL((gqa::decode_combine_kernel<T, C::D>), dim3((unsigned)a.Hq, (unsigned)a.B),
-                     dim3(64), 0, stream, a);
+                     dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode combine kernel launch");
   return GQA_OK;
@@ -297,7 +309,7 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, in
   a.NQB = (int)NQB;
   a.T = (int)T;
   a.q_offset = causal ? q_offset : 0;
-  a.c = std::fabs(scale) * gqa::kLog2e;
+  a.c = softmax_coef(scale);
   a.negate_q = scale < 0.f ? 1 : 0;
   a.ctr = ctr;
   (void)hipGetLastError();  // a stale error belongs to an earlier call
@@ -356,7 +368,7 @@ int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
   a.NCB = (g + 31) / 32;
   a.S_TOK = decode_split_tokens(B, Hkv, a.NCB, Smax, info.cus);
   a.NS = (Smax + a.S_TOK - 1) / a.S_TOK;
-  a.c = std::fabs(scale) * gqa::kLog2e;
+  a.c = softmax_coef(scale);
   a.negate_q = scale < 0.f ? 1 : 0;
   if ((long long)a.Hkv * a.NCB > 65535 || B > 65535)
     return fail(GQA_ERR_BAD_SHAPE, "grid too large (B=%d, Hkv*blocks=%d)", B, a.Hkv * a.NCB);

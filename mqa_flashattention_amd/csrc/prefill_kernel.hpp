@@ -12,13 +12,17 @@
 //
 // Scheduling is persistent ("Kernel 8 -- persistent kernel" of the same
 // log): the grid holds as many workgroups as fit on the device at once and
-// each repeatedly takes the next unit index from a device counter with one
-// atomic add, exiting once the index passes the unit count.  Units are
-// numbered heaviest first for causal attention (the last position blocks see
-// the most keys), which makes the first-come order a longest-job-first
-// schedule; for non-causal attention units that share a K/V head are
-// numbered consecutively so they run close in time and share L2.  The last
-// workgroup to leave resets the counter for the next launch on the stream.
+// each repeatedly takes the next unit from a device counter with one atomic
+// add, exiting once every unit is taken.  The units are split into
+// kNumQueues queues by K/V group (b*Hkv + hkv) modulo kNumQueues, one per
+// XCD: workgroups are dispatched to the XCDs round-robin by block index, so
+// a workgroup first drains the queue of its own XCD and the K/V tiles of a
+// group stay in that XCD's L2; a workgroup whose queue is empty steals from
+// the next ones.  Within a queue units are numbered heaviest first for
+// causal attention (the last position blocks see the most keys), which
+// makes the first-come order a longest-job-first schedule; for non-causal
+// attention the units of one K/V group are numbered consecutively.  The
+// last workgroup to leave resets the counters for the next launch.
 //
 // Per unit the key tiles stream through a two-stage LDS ring: the global
 // loads of tile t+1 are issued before tile t is computed and written to the
@@ -46,8 +50,15 @@ struct PrefillArgs {
   int q_offset;
   float c;  // |scale| * log2(e)
   int negate_q;
-  int* ctr;  // [0] next unit, [1] workgroups finished
+  int* ctr;  // [0, kNumQueues): next unit of each queue; [kNumQueues]: workgroups finished
 };
+
+constexpr int kNumQueues = 8;  // XCDs of an MI355X
+
+// Units in queue q: the K/V groups q, q + kNumQueues, ... below nkv.
+__device__ __forceinline__ int queue_units(int q, int nkv, int per_group) {
+  return nkv > q ? ((nkv - q + kNumQueues - 1) / kNumQueues) * per_group : 0;
+}
 
 template <typename T, class C, bool CAUSAL>
 __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
@@ -70,26 +81,50 @@ prefill_kernel(PrefillArgs a) {
   const T* __restrict__ V = reinterpret_cast<const T*>(a.v);
   T* __restrict__ O = reinterpret_cast<T*>(a.o);
 
+  __shared__ int s_queue;
+  const int home = blockIdx.x % kNumQueues;
+  const int nkv = a.B * a.Hkv;
+  const int per_group = a.HB * a.NQB;
+  int tried = 0;  // queues found empty so far (thread 0 only)
+
   for (;;) {
-    if (tid == 0) s_unit = atomicAdd(a.ctr, 1);
+    if (tid == 0) {
+      int t = -1, q = 0;
+      while (tried < kNumQueues) {
+        q = (home + tried) % kNumQueues;
+        const int cand = atomicAdd(a.ctr + q, 1);
+        if (cand < queue_units(q, nkv, per_group)) {
+          t = cand;
+          break;
+        }
+        ++tried;
+      }
+      s_unit = t;
+      s_queue = q;
+    }
     __syncthreads();
     const int t = s_unit;
-    if (t >= a.T) break;
+    const int q = s_queue;
+    if (t < 0) break;
 
-    // ---- unit index -> (b, hkv, hb, qb)
-    const int per_qb = a.B * a.Hkv * a.HB;
-    int qb, rest;
+    // ---- (queue, index) -> (b, hkv, hb, qb)
+    const int groups = queue_units(q, nkv, per_group) / per_group;
+    int qb, gi, hb;
     if (CAUSAL) {
+      const int per_qb = groups * a.HB;
       qb = a.NQB - 1 - t / per_qb;
-      rest = t % per_qb;
+      const int rest = t % per_qb;
+      hb = rest % a.HB;
+      gi = rest / a.HB;
     } else {
-      qb = t % a.NQB;
-      rest = t / a.NQB;
+      gi = t / per_group;
+      const int rest = t % per_group;
+      hb = rest / a.NQB;
+      qb = rest % a.NQB;
     }
-    const int hb = rest % a.HB;
-    const int bh = rest / a.HB;
-    const int hkv = bh % a.Hkv;
-    const int b = bh / a.Hkv;
+    const int kvg = q + kNumQueues * gi;
+    const int hkv = kvg % a.Hkv;
+    const int b = kvg / a.Hkv;
 
     // ---- this lane's query column
     const int m = 32 * w + j;
@@ -124,26 +159,21 @@ prefill_kernel(PrefillArgs a) {
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
     TileRegs<C> regs;
-    load_tile<T, C>(regs, kbase, vbase, 0, a.Nk, tid);
+    load_tile<T, C, false>(regs, kbase, vbase, 0, a.Nk, tid);
     store_tile<T, C>(regs, stK(0), stV(0), tid);
     __syncthreads();
 
     for (int kt = 0; kt < ntiles; ++kt) {
       const int cur = kt & 1;
       const bool more = kt + 1 < ntiles;
-      if (more) load_tile<T, C>(regs, kbase, vbase, (kt + 1) * C::BC, a.Nk, tid);
+      if (more) load_tile<T, C, false>(regs, kbase, vbase, (kt + 1) * C::BC, a.Nk, tid);
 
       f32x16 s[C::KB];
       qk_tile<T, C>(s, qf, stK(cur), j, h2);
 
-      typename C::Frag pf[C::KB][C::PF];
       const int key0 = kt * C::BC;
-      if (key0 + C::BC > full_lim)
-        softmax_tile<C, true>(s, mrun, lrun, acc, pf, key0, lim, h2, a.c);
-      else
-        softmax_tile<C, false>(s, mrun, lrun, acc, pf, key0, lim, h2, a.c);
-
-      pv_tile<T, C>(acc, pf, stV(cur), j, h2);
+      if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
+      softmax_pv_step<T, C>(s, mrun, lrun, acc, stV(cur), j, h2, a.c);
 
       if (more) store_tile<T, C>(regs, stK(cur ^ 1), stV(cur ^ 1), tid);
       __syncthreads();
@@ -153,14 +183,13 @@ prefill_kernel(PrefillArgs a) {
     if (valid) store_out_row<T, C>(O + qrow_off, acc, 1.0f / lsum, h2);
   }
 
-  // Leave the counter at zero for the next launch: the last workgroup out
-  // (all others have made their final, failing fetch) resets both words.
+  // Leave the counters at zero for the next launch: the last workgroup out
+  // (all others have made their final, failing fetches) resets every word.
   if (tid == 0) {
     __threadfence();
-    const int done = atomicAdd(a.ctr + 1, 1);
+    const int done = atomicAdd(a.ctr + kNumQueues, 1);
     if (done == (int)gridDim.x - 1) {
-      atomicExch(a.ctr, 0);
-      atomicExch(a.ctr + 1, 0);
+      for (int i = 0; i <= kNumQueues; ++i) atomicExch(a.ctr + i, 0);
     }
   }
 }
