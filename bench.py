@@ -2,6 +2,10 @@
 """Benchmark of the GQA attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+    python bench.py --steps 5 --warmup 2 --no-cpu-baseline --calibration-copy
+        (the run profiled with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)
+    python bench.py --summarize-counters FETCH_DIR WRITE_DIR
+        (turns those two rocprofv3 outputs into the committed counter summary)
 
 One step = one pass of the whole hot path over one batch of synthetic input:
   * prefill: LLaMA-3-8B-shaped causal prefill, bf16 in / fp32 accumulate,
@@ -45,6 +49,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_llama3_8b_counters.json")
 KERNEL_SOURCES = ["attn_tile.hpp", "prefill_kernel.hpp", "decode_kernel.hpp", "gqa_attn.hip"]
 DECODE_SETS = 48  # 48 x 16 MiB of caches > 256 MB Infinity Cache
+COPY_BYTES = 256 * 1024 * 1024  # calibration copy: reads and writes this many bytes
 
 
 def kernel_source_hash() -> str:
@@ -84,6 +89,56 @@ def traffic_from_counters():
     return c.get("traffic_bytes_per_launch")
 
 
+def _counter_means(directory: str, counter: str) -> dict:
+    """Mean per-dispatch value of one rocprofv3 counter, by kernel kind."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    vals: dict = {}
+    for path in files:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                if "prefill_kernel" in name and "128, 64, 4>, true" in name:
+                    kind = "prefill"
+                elif "neg_kernel" in name:
+                    kind = "copy"
+                else:
+                    continue
+                vals.setdefault(kind, []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def summarize_counters(fetch_dir: str, write_dir: str) -> dict:
+    """HBM bytes per prefill launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a plain copy of
+    COPY_BYTES (read COPY_BYTES, write COPY_BYTES)."""
+    from mqa_flashattention_amd.workloads import WORKLOADS
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    read_factor = COPY_BYTES / (fetch["copy"] * 1024.0)
+    write_factor = COPY_BYTES / (write["copy"] * 1024.0)
+    traffic = fetch["prefill"] * 1024.0 * read_factor + write["prefill"] * 1024.0 * write_factor
+    out = {
+        "kernel": "prefill_kernel<bf16, d128, 64-key tiles, 4 waves, causal>",
+        "workload": "llama3_8b_prefill (B1 Hq32 Hkv8 N2048 d128 causal, bf16)",
+        "fetch_kib_per_launch": round(fetch["prefill"], 1),
+        "write_kib_per_launch": round(write["prefill"], 1),
+        "copy_fetch_kib": round(fetch["copy"], 1),
+        "copy_write_kib": round(write["copy"], 1),
+        "read_scale": round(read_factor, 4),
+        "write_scale": round(write_factor, 4),
+        "traffic_bytes_per_launch": round(traffic),
+        "algorithmic_bytes_per_launch": round(fwd_bytes(WORKLOADS["llama3_8b_prefill"].fwd[0])),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    return out
+
+
 def check(out, ref, tol, what):
     import numpy as np
     err = float(np.max(np.abs(out.detach().cpu().double().numpy() - ref)))
@@ -119,7 +174,21 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true",
                     help="also time the MHA/GQA/MQA sweep and the chunked prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after timing, stream 256 MiB through a plain elementwise kernel "
+                         "twice (byte-counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the prefill counter summary from two rocprofv3 --pmc outputs")
     args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        summary = summarize_counters(*args.summarize_counters)
+        os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
+        with open(COUNTERS_FILE, "w") as f:
+            json.dump(summary, f, indent=1)
+            f.write("\n")
+        print(json.dumps(summary))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention "
@@ -246,6 +315,16 @@ def main(argv=None):
                       f"{oracle_s:.2f} s wall",
             "decode_gbps": round(dbytes / oracle_dec_s / 1e9, 4),
         }
+
+    if args.calibration_copy:
+        # a plain streaming kernel of known traffic: reads and writes COPY_BYTES
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     if args.all:
         extra = {}

@@ -83,22 +83,27 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
 
   // Two register stages: the loads of tiles t+1 and t+2 are in flight while
   // tile t is computed, so a split of up to two tiles costs one memory
-  // round trip.
+  // round trip.  The loop is unrolled by two so each stage is a named
+  // register set (an indexed pair would be placed in scratch memory).
   const int ntiles = (ntok + 31) / 32;
-  TileRegs<C> regs[2];
-  load_tile<T, C, true>(regs[0], kbase, vbase, 0, ntok, lane);
-  if (ntiles > 1) load_tile<T, C, true>(regs[1], kbase, vbase, 32, ntok, lane);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    store_tile<T, C>(regs[kt & 1], Ks, Vs, lane);
-    __syncthreads();
-    if (kt + 2 < ntiles) load_tile<T, C, true>(regs[kt & 1], kbase, vbase, (kt + 2) * 32, ntok, lane);
+  TileRegs<C> ra, rb;
+  load_tile<T, C, true>(ra, kbase, vbase, 0, ntok, lane);
+  if (ntiles > 1) load_tile<T, C, true>(rb, kbase, vbase, 32, ntok, lane);
 
+  auto step = [&](TileRegs<C>& regs, int kt) {
+    store_tile<T, C>(regs, Ks, Vs, lane);
+    __syncthreads();
+    if (kt + 2 < ntiles) load_tile<T, C, true>(regs, kbase, vbase, (kt + 2) * 32, ntok, lane);
     f32x16 s[C::KB];
     qk_tile<T, C>(s, qf, Ks, j, h2);
     const int key0 = kt * 32;
     if (key0 + 32 > ntok) mask_tile<C>(s, key0, ntok - 1, h2);
     softmax_pv_step<T, C>(s, mrun, lrun, acc, Vs, j, h2, a.c);
     __syncthreads();
+  };
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    step(ra, kt);
+    if (kt + 1 < ntiles) step(rb, kt + 1);
   }
 
   const float lsum = lrun + __shfl_xor(lrun, 32);
