@@ -132,56 +132,44 @@ struct TileRegs {
 };
 
 // Issue the global loads of one K/V tile -- keys key0 .. key0+BC-1 of one
-// head whose rows start at kbase / vbase -- into registers.  Rows at or
-// beyond nkeys read as zero, so they add nothing even before masking.
+// head whose rows start at kbase / vbase -- into registers.  A row at or
+// beyond nkeys re-reads row nkeys-1: always valid memory with finite values,
+// and the caller masks those keys, so their weight is exactly 0 and the
+// duplicate never reaches the result.  (No per-row branch or zero-fill.)
 // For K, consecutive threads take consecutive 16-byte chunks of a row, so a
 // wave's load instruction covers whole rows.
-template <typename T, class C, bool CHECKED>
-__device__ __forceinline__ void load_tile_impl(TileRegs<C>& r, const T* __restrict__ kbase,
-                                               const T* __restrict__ vbase, int key0, int nkeys,
-                                               int tid) {
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+template <typename T, class C>
+__device__ __forceinline__ void load_tile(TileRegs<C>& r, const T* __restrict__ kbase,
+                                          const T* __restrict__ vbase, int key0, int nkeys,
+                                          int tid) {
+  const int last = nkeys - 1;
 #pragma unroll
   for (int n = 0; n < C::K_PER_T; ++n) {
     const int id = tid + n * C::NT;
-    const int row = id / C::ROW_CHUNKS;
-    const int col = id % C::ROW_CHUNKS;
-    const int key = key0 + row;
-    const bool ok = (C::K_CHUNKS % C::NT == 0 || id < C::K_CHUNKS) && (!CHECKED || key < nkeys);
-    const size_t off = (size_t)key * C::D + col * C::EPC;
-    r.k[n] = ok ? *reinterpret_cast<const u32x4*>(kbase + off) : zero;
-    if constexpr (C::F32) r.v[n] = ok ? *reinterpret_cast<const u32x4*>(vbase + off) : zero;
+    if (C::K_CHUNKS % C::NT == 0 || id < C::K_CHUNKS) {
+      const int row = id / C::ROW_CHUNKS;
+      const int col = id % C::ROW_CHUNKS;
+      const size_t off = (size_t)min(key0 + row, last) * C::D + col * C::EPC;
+      r.k[n] = *reinterpret_cast<const u32x4*>(kbase + off);
+      if constexpr (C::F32) r.v[n] = *reinterpret_cast<const u32x4*>(vbase + off);
+    }
   }
   if constexpr (!C::F32) {
 #pragma unroll
     for (int n = 0; n < C::V_PER_T; ++n) {
       const int id = tid + n * C::NT;
-      const int kg = id % C::KGROUPS;
-      const int dc = id / C::KGROUPS;
+      if (C::V_BLOCKS % C::NT == 0 || id < C::V_BLOCKS) {
+        const int kg = id % C::KGROUPS;
+        const int dc = id / C::KGROUPS;
 #pragma unroll
-      for (int e = 0; e < C::VK; ++e) {
-        const int key = key0 + kg * C::VK + e;
-        const bool ok =
-            (C::V_BLOCKS % C::NT == 0 || id < C::V_BLOCKS) && (!CHECKED || key < nkeys);
-        r.v[n * C::VK + e] =
-            ok ? *reinterpret_cast<const u32x4*>(vbase + (size_t)key * C::D + dc * 8) : zero;
+        for (int e = 0; e < C::VK; ++e) {
+          const int key = min(key0 + kg * C::VK + e, last);
+          r.v[n * C::VK + e] =
+              *reinterpret_cast<const u32x4*>(vbase + (size_t)key * C::D + dc * 8);
+        }
       }
     }
   }
-}
-
-// FAST_FULL: tiles wholly inside the key range (all but a ragged last one)
-// take a copy of the loads without per-row bounds checks.  Decode uses it;
-// the prefill loop measured faster with the single checked form, whose
-// loads the compiler places earlier.
-template <typename T, class C, bool FAST_FULL>
-__device__ __forceinline__ void load_tile(TileRegs<C>& r, const T* __restrict__ kbase,
-                                          const T* __restrict__ vbase, int key0, int nkeys,
-                                          int tid) {
-  if (FAST_FULL && key0 + C::BC <= nkeys)
-    load_tile_impl<T, C, false>(r, kbase, vbase, key0, nkeys, tid);
-  else
-    load_tile_impl<T, C, true>(r, kbase, vbase, key0, nkeys, tid);
 }
 
 // Element i (0..7) of a 16-byte chunk of bf16, from VK chunks, packed as a
@@ -259,8 +247,10 @@ __device__ __forceinline__ void store_tile(const TileRegs<C>& r, T* __restrict__
   }
 }
 
-// The wave's query fragment: column j of the B operand is query row qrow.
-// Invalid columns are zero (their scores are 0 and their output is dropped).
+// The wave's query fragment: column j of the B operand is query row qrow
+// (for an invalid column the caller passes any valid row; its values are
+// replaced by zero, so its scores are 0 and its output is dropped).  All
+// loads are issued unconditionally, so they are in flight together.
 template <typename T, class C>
 __device__ __forceinline__ void load_q_frag(typename C::Frag (&qf)[C::QF],
                                             const T* __restrict__ qrow, bool valid,
@@ -268,13 +258,13 @@ __device__ __forceinline__ void load_q_frag(typename C::Frag (&qf)[C::QF],
 #pragma unroll
   for (int ks = 0; ks < C::QF; ++ks) {
     if constexpr (C::F32) {
-      const float x = valid ? qrow[2 * ks + h2] : 0.f;
-      qf[ks] = negate ? -x : x;
+      const float x = qrow[2 * ks + h2];
+      qf[ks] = valid ? (negate ? -x : x) : 0.f;
     } else {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (valid) w = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h2);
+      u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * h2);
       if (negate) w ^= 0x80008000u;
-      qf[ks] = __builtin_bit_cast(bf16x8, w);
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(bf16x8, valid ? w : zero);
     }
   }
 }
@@ -328,12 +318,14 @@ __device__ __forceinline__ float tile_rowmax(const f32x16 (&s)[C::KB]) {
 }
 
 // Raise the running reference to m_new = max(m, mt) and rescale l and acc by
-// alpha = 2^((m - m_new) c) (alpha = 0 while m is still -inf).
+// alpha = 2^((m - m_new) c): 0 when m was -inf and m_new is finite, 1 while
+// both are -inf (a lane whose keys so far were all masked has nothing
+// accumulated yet).
 template <class C>
 __device__ __forceinline__ void raise_reference(float& m, float& l, f32x16 (&acc)[C::DB],
                                                 float mt, float c) {
   const float m_new = fmaxf(m, mt);
-  const float alpha = fast_exp2((m - m_new) * c);
+  const float alpha = m_new == kNegInf ? 1.f : fast_exp2((m - m_new) * c);
   m = m_new;
   l *= alpha;
 #pragma unroll
@@ -346,7 +338,7 @@ __device__ __forceinline__ void raise_reference(float& m, float& l, f32x16 (&acc
 template <class C>
 __device__ __forceinline__ float tile_weights(const f32x16 (&s)[C::KB], float m, float c,
                                               typename C::Frag (&pf)[C::KB][C::PF]) {
-  const float mc = m * c;
+  const float mc = m == kNegInf ? 0.f : m * c;  // all-masked so far: every weight is 0
   float lt = 0.f;
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) {
@@ -406,18 +398,23 @@ __device__ __forceinline__ void pv_tile(f32x16 (&acc)[C::DB],
 }
 
 // One online-softmax + PV step on a (masked) score tile s:
-//   m' = max(m, rowmax s); l, acc scaled by alpha = 2^((m - m') c);
-//   p = 2^(s c - m' c); l += sum p; acc += V^T P^T.
-// The rescale is unconditional.  Skipping it while the max grows little
-// (a wave-uniform branch) measured no faster on gfx950: the branch merge
-// either copied the MFMA accumulators or, in the variant that avoided the
-// copies, saved no time.
+//   if rowmax s exceeds the reference m by more than 2^kRescaleSlack in some
+//   lane: m' = max(m, rowmax s), l and acc scaled by 2^((m - m') c);
+//   p = 2^(s c - m c); l += sum p; acc += V^T P^T.
+// The reference is raised only when needed (a wave-uniform branch; the first
+// tile with a visible key always raises it from -inf).  Between raises the
+// weights are taken against a reference up to kRescaleSlack/c below the true
+// running max, so they stay below 2^kRescaleSlack -- far inside fp32 and
+// bf16 range -- and acc / l is unchanged in exact arithmetic.
+constexpr float kRescaleSlack = 16.0f;
+
 template <typename T, class C>
 __device__ __forceinline__ void softmax_pv_step(f32x16 (&s)[C::KB], float& m, float& l,
                                                 f32x16 (&acc)[C::DB], const T* __restrict__ Vs,
                                                 int lane32, int h2, float c) {
   const float mt = tile_rowmax<C>(s);
-  raise_reference<C>(m, l, acc, mt, c);
+  if (__any(m == kNegInf ? mt != kNegInf : (mt - m) * c > kRescaleSlack))
+    raise_reference<C>(m, l, acc, mt, c);
   typename C::Frag pf[C::KB][C::PF];
   l += tile_weights<C>(s, m, c, pf);
   pv_tile<T, C>(acc, pf, Vs, lane32, h2);

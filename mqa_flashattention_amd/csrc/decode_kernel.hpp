@@ -87,13 +87,13 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   // register set (an indexed pair would be placed in scratch memory).
   const int ntiles = (ntok + 31) / 32;
   TileRegs<C> ra, rb;
-  load_tile<T, C, true>(ra, kbase, vbase, 0, ntok, lane);
-  if (ntiles > 1) load_tile<T, C, true>(rb, kbase, vbase, 32, ntok, lane);
+  load_tile<T, C>(ra, kbase, vbase, 0, ntok, lane);
+  if (ntiles > 1) load_tile<T, C>(rb, kbase, vbase, 32, ntok, lane);
 
   auto step = [&](TileRegs<C>& regs, int kt) {
     store_tile<T, C>(regs, Ks, Vs, lane);
     __syncthreads();
-    if (kt + 2 < ntiles) load_tile<T, C, true>(regs, kbase, vbase, (kt + 2) * 32, ntok, lane);
+    if (kt + 2 < ntiles) load_tile<T, C>(regs, kbase, vbase, (kt + 2) * 32, ntok, lane);
     f32x16 s[C::KB];
     qk_tile<T, C>(s, qf, Ks, j, h2);
     const int key0 = kt * 32;

@@ -146,11 +146,12 @@ int occupancy(const void* kernel, int threads) {
 
 // ------------------------------------------------------------------ prefill
 
-// bf16: 64-key tiles; fp32: 32-key tiles (LDS budget).  Four waves per
-// workgroup, 128 query columns per unit.
+// bf16: 32-key tiles at d=128 (two register staging sets fit the budget of
+// two waves per SIMD), 64-key tiles below; fp32: 32-key tiles.  Four waves
+// per workgroup, 128 query columns per unit.
 constexpr int kPrefillWaves = 4;
 template <int D>
-using CfgBf16 = gqa::TileCfg<uint16_t, D, 64, kPrefillWaves>;
+using CfgBf16 = gqa::TileCfg<uint16_t, D, (D == 128 ? 32 : 64), kPrefillWaves>;
 template <int D>
 using CfgF32 = gqa::TileCfg<float, D, 32, kPrefillWaves>;
 

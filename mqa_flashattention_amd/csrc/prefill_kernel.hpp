@@ -24,9 +24,9 @@
 // attention the units of one K/V group are numbered consecutively.  The
 // last workgroup to leave resets the counters for the next launch.
 //
-// Per unit the key tiles stream through a two-stage LDS ring: the global
-// loads of tile t+1 are issued before tile t is computed and written to the
-// other stage afterwards.  Causal masking runs only on tiles that cross the
+// Per unit the key tiles stream through a two-stage LDS ring fed from two
+// register staging sets, so each tile's global loads are issued two tiles
+// before they are needed.  Causal masking runs only on tiles that cross the
 // diagonal (or the ragged end of the keys); tiles above the diagonal of the
 // whole unit are never loaded.
 #pragma once
@@ -158,25 +158,44 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
-    TileRegs<C> regs;
-    load_tile<T, C, false>(regs, kbase, vbase, 0, a.Nk, tid);
-    store_tile<T, C>(regs, stK(0), stV(0), tid);
+    // Two LDS stages and two register staging sets: the global loads of tile
+    // t+2 are issued at the start of tile t and written to LDS at the end of
+    // tile t+1, so two tiles of compute cover their latency.  The loop is
+    // unrolled by two so each staging set is a named register set, and the
+    // loads and stores are unconditional (indices clamped to the last tile)
+    // so the compiler's wait before each LDS store counts exactly the newer
+    // loads still in flight.
+    //
+    // Each unit walks its tiles starting at a unit-dependent rotation, so the
+    // many workgroups that share a K/V head do not all request the same
+    // tile at the same moment.  The order of tiles does not change the
+    // result in exact arithmetic (masking is per key, and a lane whose first
+    // tiles are all masked keeps an empty state until a visible key comes).
+    const int rot = (int)((7u * (unsigned)t + 3u * (unsigned)q) % (unsigned)ntiles);
+    auto tile_at = [&](int pos) {
+      const int x = (pos < ntiles ? pos : ntiles - 1) + rot;
+      return x >= ntiles ? x - ntiles : x;
+    };
+    TileRegs<C> ra, rb;
+    load_tile<T, C>(ra, kbase, vbase, tile_at(0) * C::BC, a.Nk, tid);
+    load_tile<T, C>(rb, kbase, vbase, tile_at(1) * C::BC, a.Nk, tid);
+    store_tile<T, C>(ra, stK(0), stV(0), tid);
     __syncthreads();
 
-    for (int kt = 0; kt < ntiles; ++kt) {
+    auto step = [&](TileRegs<C>& mine, TileRegs<C>& next, int kt) {
       const int cur = kt & 1;
-      const bool more = kt + 1 < ntiles;
-      if (more) load_tile<T, C, false>(regs, kbase, vbase, (kt + 1) * C::BC, a.Nk, tid);
-
+      load_tile<T, C>(mine, kbase, vbase, tile_at(kt + 2) * C::BC, a.Nk, tid);
       f32x16 s[C::KB];
       qk_tile<T, C>(s, qf, stK(cur), j, h2);
-
-      const int key0 = kt * C::BC;
+      const int key0 = tile_at(kt) * C::BC;
       if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
       softmax_pv_step<T, C>(s, mrun, lrun, acc, stV(cur), j, h2, a.c);
-
-      if (more) store_tile<T, C>(regs, stK(cur ^ 1), stV(cur ^ 1), tid);
+      store_tile<T, C>(next, stK(cur ^ 1), stV(cur ^ 1), tid);
       __syncthreads();
+    };
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      step(ra, rb, kt);
+      if (kt + 1 < ntiles) step(rb, ra, kt + 1);
     }
 
     const float lsum = lrun + __shfl_xor(lrun, 32);
