@@ -423,24 +423,28 @@ __device__ __forceinline__ void softmax_pv_step(f32x16 (&s)[C::KB], float& m, fl
 // Store one query row of O from the O^T accumulator: this lane holds d =
 // 32*db + 8*a + 4*h2 + (0..3) for a = 0..3.
 template <typename T, class C>
+__device__ __forceinline__ void store_out_block(T* __restrict__ orow, const f32x16& acc, float inv,
+                                                int db, int h2) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int d0 = 32 * db + 8 * a + 4 * h2;
+    const float x0 = acc[4 * a + 0] * inv;
+    const float x1 = acc[4 * a + 1] * inv;
+    const float x2 = acc[4 * a + 2] * inv;
+    const float x3 = acc[4 * a + 3] * inv;
+    if constexpr (C::F32) {
+      *reinterpret_cast<float4*>(orow + d0) = float4{x0, x1, x2, x3};
+    } else {
+      *reinterpret_cast<u32x2*>(orow + d0) = u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
+    }
+  }
+}
+
+template <typename T, class C>
 __device__ __forceinline__ void store_out_row(T* __restrict__ orow, const f32x16 (&acc)[C::DB],
                                               float inv, int h2) {
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int d0 = 32 * db + 8 * a + 4 * h2;
-      const float x0 = acc[db][4 * a + 0] * inv;
-      const float x1 = acc[db][4 * a + 1] * inv;
-      const float x2 = acc[db][4 * a + 2] * inv;
-      const float x3 = acc[db][4 * a + 3] * inv;
-      if constexpr (C::F32) {
-        *reinterpret_cast<float4*>(orow + d0) = float4{x0, x1, x2, x3};
-      } else {
-        *reinterpret_cast<u32x2*>(orow + d0) = u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
-      }
-    }
-  }
+  for (int db = 0; db < C::DB; ++db) store_out_block<T, C>(orow, acc[db], inv, db, h2);
 }
 
 }  // namespace gqa

@@ -6,6 +6,7 @@
 // arithmetic runs in the kernels of prefill_kernel.hpp / decode_kernel.hpp.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -60,7 +61,6 @@ struct DeviceInfo {
 
 std::mutex g_mu;
 std::map<int, DeviceInfo> g_devices;
-std::map<std::pair<int, void*>, int*> g_counters;
 std::map<const void*, int> g_occupancy;
 
 // The current device, checked to be a gfx950.
@@ -95,34 +95,65 @@ int current_device(int* dev_out, DeviceInfo* info_out) {
   return GQA_OK;
 }
 
-__global__ void zero_ints_kernel(int* p, int n) {
-  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+__global__ void zero_ints_kernel(int* p, long long n) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x)
+    p[i] = 0;
 }
 
-// Scheduler counters of one (device, stream): one per work queue plus a
-// finished-workgroup count, zeroed in stream order on first use; each
-// persistent launch leaves them at zero when it ends.
-constexpr int kCounterInts = 16;
-static_assert(kCounterInts >= gqa::kNumQueues + 1, "counter block too small");
-int stream_counter(int dev, hipStream_t stream, int** out) {
+hipError_t zero_ints(int* p, long long n, hipStream_t stream) {
+  long long blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+// Device memory the library keeps per (device, stream):
+//  * ctr: one counter per work queue plus a finished-workgroup count, zeroed
+//    in stream order when allocated; each persistent launch leaves them at
+//    zero when it ends;
+//  * ws: partial records of the prefill units that the balanced schedule
+//    cuts, grown on demand (after
+//    the stream drains, so no queued launch still uses the old buffer).
+constexpr int kCounterInts = (gqa::kNumQueues + 1) * gqa::kCounterStride;
+struct StreamState {
+  int* ctr = nullptr;
+  float* ws = nullptr;
+  size_t ws_bytes = 0;
+};
+std::map<std::pair<int, void*>, StreamState> g_streams;
+
+int stream_state(int dev, hipStream_t stream, size_t ws_bytes, StreamState* out) {
   std::lock_guard<std::mutex> lock(g_mu);
-  const auto key = std::make_pair(dev, reinterpret_cast<void*>(stream));
-  auto it = g_counters.find(key);
-  if (it != g_counters.end()) {
-    *out = it->second;
-    return GQA_OK;
+  StreamState& s = g_streams[std::make_pair(dev, reinterpret_cast<void*>(stream))];
+  hipError_t e;
+  if (!s.ctr) {
+    e = hipMalloc(&s.ctr, kCounterInts * sizeof(int));
+    if (e != hipSuccess) {
+      s.ctr = nullptr;
+      return hip_fail(e, "hipMalloc(scheduler counters)");
+    }
+    e = zero_ints(s.ctr, kCounterInts, stream);
+    if (e != hipSuccess) {
+      (void)hipFree(s.ctr);
+      s.ctr = nullptr;
+      return hip_fail(e, "counter initialisation launch");
+    }
   }
-  int* p = nullptr;
-  hipError_t e = hipMalloc(&p, kCounterInts * sizeof(int));
-  if (e != hipSuccess) return hip_fail(e, "hipMalloc(scheduler counter)");
-  hipLaunchKernelGGL(zero_ints_kernel, dim3(1), dim3(64), 0, stream, p, kCounterInts);
-  e = hipGetLastError();
-  if (e != hipSuccess) {
-    (void)hipFree(p);
-    return hip_fail(e, "counter initialisation launch");
+  if (ws_bytes > s.ws_bytes) {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize before workspace growth");
+    if (s.ws) (void)hipFree(s.ws);
+    s.ws = nullptr;
+    s.ws_bytes = 0;
+    e = hipMalloc(&s.ws, ws_bytes);
+    if (e != hipSuccess) {
+      s.ws = nullptr;
+      return hip_fail(e, "hipMalloc(split workspace)");
+    }
+    s.ws_bytes = ws_bytes;
   }
-  g_counters.emplace(key, p);
-  *out = p;
+  *out = s;
   return GQA_OK;
 }
 
@@ -155,32 +186,122 @@ using CfgBf16 = gqa::TileCfg<uint16_t, D, (D == 128 ? 32 : 64), kPrefillWaves>;
 template <int D>
 using CfgF32 = gqa::TileCfg<float, D, 32, kPrefillWaves>;
 
+// Key tiles of the units of position block qb (host copy of the kernels'
+// unit_tiles).
+template <class C>
+long long unit_tiles(const gqa::PrefillArgs& a, bool causal, long long qb) {
+  long long kend = a.Nk;
+  if (causal) {
+    const long long i_hi = std::min<long long>(a.Nq, (qb + 1) * a.R) - 1;
+    kend = std::min<long long>(a.Nk, a.q_offset + i_hi + 1);
+  }
+  return (kend + C::BC - 1) / C::BC;
+}
+
+long long seq_qb(long long pos, long long nqb, bool causal) {
+  if (!causal) return pos;
+  return (pos & 1) ? (pos >> 1) : nqb - 1 - (pos >> 1);
+}
+
+// The balanced schedule (a static partition of each slice's key tiles into
+// Pp equal chunks, one workgroup each, plus a merge of the units the chunk
+// boundaries cut) replaces the persistent one when there are too few units
+// to balance whole units: at most kBalancedUnitsPerSlot per resident
+// workgroup.  Pp is as large as the resident workgroups allow, but no chunk
+// is shorter than kMinChunkTiles and no unit is cut into more than
+// kMaxPieces pieces.  Returns false (persistent schedule) otherwise;
+// *cuts is the number of units that need merging.
+constexpr int kBalancedUnitsPerSlot = 2;
+constexpr int kMinChunkTiles = 4;
+constexpr int kMaxPieces = gqa::kMaxPiecesDev;
+template <class C>
+bool plan_balanced(gqa::PrefillArgs& a, bool causal, long long slots, long long* cuts) {
+  a.nsl = a.B * a.Hkv * a.HB;
+  a.Pp = 1;
+  a.Ws = 0;
+  *cuts = 0;
+  if ((long long)a.T > kBalancedUnitsPerSlot * slots || a.nsl > slots) return false;
+  long long ws = 0, longest = 0;
+  for (long long qb = 0; qb < a.NQB; ++qb) {
+    const long long n = unit_tiles<C>(a, causal, qb);
+    ws += n;
+    longest = std::max(longest, n);
+  }
+  if (ws > kIntMax / 2) return false;
+  long long pp = slots / a.nsl;
+  pp = std::min(pp, std::max<long long>(1, ws / kMinChunkTiles));
+  pp = std::min(pp, std::max<long long>(1, (kMaxPieces - 1) * ws / longest));
+  if (pp < 1) pp = 1;
+  a.Pp = (int)pp;
+  a.Ws = (int)ws;
+  // count the units cut by a chunk boundary (each counted once)
+  long long pre = 0, c = 1;
+  for (long long pos = 0; pos < a.NQB && c < pp; ++pos) {
+    const long long n = unit_tiles<C>(a, causal, seq_qb(pos, a.NQB, causal));
+    bool cut = false;
+    for (; c < pp; ++c) {
+      const long long x = c * ws / pp;
+      if (x >= pre + n) break;
+      if (x > pre) cut = true;
+    }
+    if (cut) ++*cuts;
+    pre += n;
+  }
+  *cuts *= a.nsl;
+  return true;
+}
+
 template <typename T, class C, bool CAUSAL>
-int launch_prefill(gqa::PrefillArgs& a, const DeviceInfo& dev, hipStream_t stream) {
+int launch_prefill(gqa::PrefillArgs& a, int dev_id, const DeviceInfo& dev, hipStream_t stream) {
   const void* kern = reinterpret_cast<const void*>(&gqa::prefill_kernel<T, C, CAUSAL>);
   const int per_cu = occupancy(kern, C::NT);
-  long long grid = (long long)dev.cus * per_cu;
-  if (grid > a.T) grid = a.T;
-  hipLaunchKernelGGL((gqa::prefill_kernel<T, C, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
-                     stream, a);
+  const long long slots = (long long)dev.cus * per_cu;
+  long long cuts = 0;
+  const bool balanced = plan_balanced<C>(a, CAUSAL, slots, &cuts);
+  const long long grid = balanced ? (long long)a.nsl * a.Pp : std::min<long long>(a.T, slots);
+  const size_t ws_bytes = cuts > 0 ? (size_t)grid * 2 * gqa::part_floats<C>() * sizeof(float) : 0;
+  StreamState ss;
+  int st = stream_state(dev_id, stream, ws_bytes, &ss);
+  if (st != GQA_OK) return st;
+  a.ctr = ss.ctr;
+  a.zero = 0;
+  a.ws = cuts > 0 ? ss.ws : nullptr;
+  (void)hipGetLastError();  // a stale error belongs to an earlier call
+  if (!balanced) {
+    hipLaunchKernelGGL((gqa::prefill_kernel<T, C, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+    return GQA_OK;
+  }
+  hipLaunchKernelGGL((gqa::prefill_balanced_kernel<T, C, CAUSAL>), dim3((unsigned)grid),
+                     dim3(C::NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+  if (cuts > 0) {
+    hipLaunchKernelGGL((gqa::prefill_merge_kernel<T, C, CAUSAL>),
+                       dim3((unsigned)(a.nsl * (a.Pp - 1) * C::NW)), dim3(64 * C::DB), 0, stream,
+                       a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "prefill merge kernel launch");
+  }
   return GQA_OK;
 }
 
 template <typename T, int D, template <int> class Cfg>
-int dispatch_prefill_d(gqa::PrefillArgs& a, int causal, const DeviceInfo& dev, hipStream_t s) {
-  return causal ? launch_prefill<T, Cfg<D>, true>(a, dev, s)
-                : launch_prefill<T, Cfg<D>, false>(a, dev, s);
+int dispatch_prefill_d(gqa::PrefillArgs& a, int causal, int dev_id, const DeviceInfo& dev,
+                       hipStream_t s) {
+  return causal ? launch_prefill<T, Cfg<D>, true>(a, dev_id, dev, s)
+                : launch_prefill<T, Cfg<D>, false>(a, dev_id, dev, s);
 }
 
 template <typename T, template <int> class Cfg>
-int dispatch_prefill(gqa::PrefillArgs& a, int d, int causal, const DeviceInfo& dev,
-                     hipStream_t s) {
+int dispatch_prefill(gqa::PrefillArgs& a, int d, int causal, int dev_id,
+                     const DeviceInfo& dev, hipStream_t s) {
   switch (d) {
-    case 32: return dispatch_prefill_d<T, 32, Cfg>(a, causal, dev, s);
-    case 64: return dispatch_prefill_d<T, 64, Cfg>(a, causal, dev, s);
-    default: return dispatch_prefill_d<T, 128, Cfg>(a, causal, dev, s);
+    case 32: return dispatch_prefill_d<T, 32, Cfg>(a, causal, dev_id, dev, s);
+    case 64: return dispatch_prefill_d<T, 64, Cfg>(a, causal, dev_id, dev, s);
+    default: return dispatch_prefill_d<T, 128, Cfg>(a, causal, dev_id, dev, s);
   }
 }
 
@@ -289,9 +410,6 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, in
   int st = current_device(&dev, &info);
   if (st != GQA_OK) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  int* ctr = nullptr;
-  st = stream_counter(dev, hs, &ctr);
-  if (st != GQA_OK) return st;
 
   gqa::PrefillArgs a;
   a.q = q;
@@ -312,10 +430,9 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, in
   a.q_offset = causal ? q_offset : 0;
   a.c = softmax_coef(scale);
   a.negate_q = scale < 0.f ? 1 : 0;
-  a.ctr = ctr;
-  (void)hipGetLastError();  // a stale error belongs to an earlier call
-  if (dtype == GQA_DTYPE_BF16) return dispatch_prefill<uint16_t, CfgBf16>(a, d, causal, info, hs);
-  return dispatch_prefill<float, CfgF32>(a, d, causal, info, hs);
+  if (dtype == GQA_DTYPE_BF16)
+    return dispatch_prefill<uint16_t, CfgBf16>(a, d, causal, dev, info, hs);
+  return dispatch_prefill<float, CfgF32>(a, d, causal, dev, info, hs);
 }
 
 size_t gqa_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Smax, int d) {

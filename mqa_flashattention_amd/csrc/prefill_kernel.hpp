@@ -1,4 +1,4 @@
-// prefill_kernel.hpp -- persistent GQA forward (prefill and chunked prefill).
+// prefill_kernel.hpp -- GQA forward (prefill and chunked prefill).
 //
 // Work unit = (batch b, K/V head hkv, head block hb, position block qb): the
 // Gu query heads hb*Gu .. hb*Gu+Gu-1 of the group that shares K/V head hkv
@@ -8,21 +8,32 @@
 // workgroup stages in LDS is read from HBM once and serves all Gu heads: the
 // "one K/V tile shared by many query rows" idea of the same log's
 // cooperative-loading kernel ("Kernel 3"), widened from query rows to the
-// whole head group.
+// whole head group.  The units of one (b, hkv, hb) form a slice.
 //
-// Scheduling is persistent ("Kernel 8 -- persistent kernel" of the same
-// log): the grid holds as many workgroups as fit on the device at once and
-// each repeatedly takes the next unit from a device counter with one atomic
-// add, exiting once every unit is taken.  The units are split into
-// kNumQueues queues by K/V group (b*Hkv + hkv) modulo kNumQueues, one per
-// XCD: workgroups are dispatched to the XCDs round-robin by block index, so
-// a workgroup first drains the queue of its own XCD and the K/V tiles of a
-// group stay in that XCD's L2; a workgroup whose queue is empty steals from
-// the next ones.  Within a queue units are numbered heaviest first for
-// causal attention (the last position blocks see the most keys), which
-// makes the first-come order a longest-job-first schedule; for non-causal
-// attention the units of one K/V group are numbered consecutively.  The
-// last workgroup to leave resets the counters for the next launch.
+// Two schedules share the per-unit code:
+//
+// * prefill_kernel, for launches with many units, is persistent ("Kernel 8 --
+//   persistent kernel" of the same log): the grid holds as many workgroups
+//   as fit on the device at once and each repeatedly takes the next unit
+//   from a device counter with one atomic add.  The units are split into
+//   kNumQueues queues by K/V group (b*Hkv + hkv) modulo kNumQueues, one per
+//   XCD: workgroups are dispatched to the XCDs round-robin by block index, so
+//   a workgroup first drains the queue of its own XCD and the K/V tiles of a
+//   group stay in that XCD's L2; once its queue is empty it looks at all
+//   queues at once and steals.  Within a queue units are numbered heaviest
+//   first for causal attention (the last position blocks see the most keys),
+//   which makes the first-come order a longest-job-first schedule.  The last
+//   workgroup to leave resets the counters for the next launch.
+//
+// * prefill_balanced_kernel, for launches with about as many units as
+//   resident workgroups or fewer, where whole units cannot be balanced: each
+//   slice's key tiles, taken unit after unit, form one sequence that is cut
+//   into Pp equal chunks, one per workgroup.  A chunk covers the end of one
+//   unit, whole units and the start of another; a unit cut by a chunk
+//   boundary leaves partial softmax states (m, l, unnormalised O) that
+//   prefill_merge_kernel combines.  For causal attention the units are
+//   ordered heavy, light, heavy, light (qb = NQB-1, 0, NQB-2, 1, ...), so
+//   that the chunk boundaries fall mostly between units.
 //
 // Per unit the key tiles stream through a two-stage LDS ring fed from two
 // register staging sets, so each tile's global loads are issued two tiles
@@ -50,14 +61,226 @@ struct PrefillArgs {
   int q_offset;
   float c;  // |scale| * log2(e)
   int negate_q;
-  int* ctr;  // [0, kNumQueues): next unit of each queue; [kNumQueues]: workgroups finished
+  // balanced schedule: slices, chunks per slice, key tiles per slice, and
+  // two partial records per workgroup (first and last segment)
+  int nsl;
+  int Pp;
+  int Ws;
+  float* ws;
+  int zero;  // always 0 (the probe's atomic add, kept a read-modify-write)
+  int* ctr;  // counter i at ctr[i * kCounterStride]: next item of queue i < kNumQueues,
+             // workgroups finished for i = kNumQueues
 };
 
 constexpr int kNumQueues = 8;  // XCDs of an MI355X
+// Scheduler counters sit 256 bytes apart, each in a cache line (and memory
+// channel) of its own, so that the atomics of different queues do not queue
+// up behind one another.
+constexpr int kCounterStride = 64;
+// Pieces of one unit under the balanced schedule, at most.
+constexpr int kMaxPiecesDev = 16;
 
-// Units in queue q: the K/V groups q, q + kNumQueues, ... below nkv.
+// Items in queue q: the K/V groups q, q + kNumQueues, ... below nkv.
 __device__ __forceinline__ int queue_units(int q, int nkv, int per_group) {
   return nkv > q ? ((nkv - q + kNumQueues - 1) / kNumQueues) * per_group : 0;
+}
+
+// Floats of one partial record (one key-range part of one unit): for each of
+// the NW waves, its DB*16 accumulator registers as DB*4 rows of 64 lanes x 4
+// floats (one coalesced 1 KiB row per 16-byte access), then the running
+// reference m and per-lane sum l as 64 lane pairs.
+template <class C>
+constexpr int wave_record_floats() {
+  return (C::DB * 16 + 2) * 64;
+}
+template <class C>
+constexpr int part_floats() {
+  return C::NW * wave_record_floats<C>();
+}
+
+// Key tiles of the units of position block qb.
+template <class C, bool CAUSAL>
+__device__ __forceinline__ int unit_tiles(const PrefillArgs& a, int qb) {
+  const int i_hi = min(a.Nq, (qb + 1) * a.R) - 1;
+  const int kend = CAUSAL ? min(a.Nk, a.q_offset + i_hi + 1) : a.Nk;
+  return (kend + C::BC - 1) / C::BC;
+}
+
+// Position pos of a slice's unit sequence -> position block.  Causal:
+// heavy and light units alternate (NQB-1, 0, NQB-2, 1, ...).
+template <bool CAUSAL>
+__device__ __forceinline__ int seq_qb(int pos, int NQB) {
+  if (!CAUSAL) return pos;
+  return (pos & 1) ? (pos >> 1) : NQB - 1 - (pos >> 1);
+}
+
+// First tile of chunk c of a slice (chunk c covers [bound(c), bound(c+1))).
+__device__ __forceinline__ int chunk_bound(const PrefillArgs& a, int c) {
+  return (int)((long long)c * a.Ws / a.Pp);
+}
+
+// Locates tile X (0 <= X < Ws) of the slice sequence: the sequence position
+// holding it and the number of tiles before that position.  Called by a
+// whole wave; every lane returns the same result.  Each lane sums the tile
+// counts of a contiguous run of positions, a wave prefix sum finds the run
+// holding X, and a short walk inside it finds the position.
+template <class C, bool CAUSAL>
+__device__ __forceinline__ void locate_tile(const PrefillArgs& a, int X, int lane, int& pos_out,
+                                            int& pre_out) {
+  const int E = (a.NQB + 63) / 64;
+  const int p0 = min(a.NQB, lane * E);
+  const int p1 = min(a.NQB, p0 + E);
+  int sum = 0;
+  for (int p = p0; p < p1; ++p) sum += unit_tiles<C, CAUSAL>(a, seq_qb<CAUSAL>(p, a.NQB));
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  const int excl = incl - sum;
+  const unsigned long long hit = __ballot(excl <= X && X < incl);
+  const int L = hit ? __ffsll((long long)hit) - 1 : 63;
+  int pre = __shfl(excl, L);
+  int pos = __shfl(p0, L);
+  for (;;) {
+    const int n = unit_tiles<C, CAUSAL>(a, seq_qb<CAUSAL>(pos, a.NQB));
+    if (pre + n > X || pos + 1 >= a.NQB) break;
+    pre += n;
+    ++pos;
+  }
+  pos_out = pos;
+  pre_out = pre;
+}
+
+// Partial record `slot` (0: first segment, 1: last segment) of workgroup g
+// of the balanced schedule.
+template <class C>
+__device__ __forceinline__ float* part_record(const PrefillArgs& a, int g, int slot) {
+  return a.ws + ((size_t)g * 2 + slot) * part_floats<C>();
+}
+
+// The query column a lane owns: column m = 32 w + j of the unit is head
+// r = m / R of the head block at position p = m % R.
+struct Column {
+  bool valid;
+  int i;           // query row
+  size_t row_off;  // element offset of the row in Q and O
+};
+
+template <class C>
+__device__ __forceinline__ Column lane_column(const PrefillArgs& a, int b, int hkv, int hb, int qb,
+                                              int w, int j) {
+  const int m = 32 * w + j;
+  const int r = m / a.R;
+  const int p = m - r * a.R;
+  const int hig = hb * a.Gu + r;  // head within the group
+  Column c;
+  c.i = qb * a.R + p;
+  c.valid = (r < a.Gu) && (hig < a.g) && (c.i < a.Nq);
+  const int h = hkv * a.g + hig;
+  c.row_off = c.valid ? (((size_t)b * a.Hq + h) * a.Nq + c.i) * C::D : 0;
+  return c;
+}
+
+// Runs key tiles [tile0, tile0 + ntiles) of unit (b, hkv, hb, qb) for the
+// lane's column col: loads the Q fragment, streams the tiles through the LDS
+// ring and leaves the running state (reference m, per-lane sum l and
+// unnormalised O) in mrun, lrun, acc.  All threads of the workgroup call it
+// together; it ends on a barrier, so the LDS ring is free on return.
+//
+// Two LDS stages and two register staging sets: the global loads of tile
+// t+2 are issued at the start of tile t and written to LDS at the end of
+// tile t+1, so two tiles of compute cover their latency.  The loop is
+// unrolled by two so each staging set is a named register set, and the
+// loads and stores are unconditional (indices clamped to the last tile) so
+// the compiler's wait before each LDS store counts exactly the newer loads
+// still in flight.
+//
+// The tiles are walked from a caller-chosen rotation, so the many
+// workgroups that share a K/V head do not all request the same tile at the
+// same moment.  The order of tiles does not change the result in exact
+// arithmetic (masking is per key, and a lane whose first tiles are all
+// masked keeps an empty state until a visible key comes).
+template <typename T, class C, bool CAUSAL>
+__device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, int b, int hkv,
+                                            int qb, int tile0, int ntiles, int rot,
+                                            const Column& col, float& mrun, float& lrun,
+                                            f32x16 (&acc)[C::DB]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int j = lane & 31;
+  const int h2 = lane >> 5;
+  auto stK = [&](int st) { return reinterpret_cast<T*>(smem + st * C::STAGE_BYTES); };
+  auto stV = [&](int st) { return stK(st) + C::K_ELEMS; };
+
+  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q);
+  const size_t kv_off = ((size_t)b * a.Hkv + hkv) * a.Nk * C::D;
+  const T* kbase = reinterpret_cast<const T*>(a.k) + kv_off;
+  const T* vbase = reinterpret_cast<const T*>(a.v) + kv_off;
+
+  typename C::Frag qf[C::QF];
+  load_q_frag<T, C>(qf, Q + col.row_off, col.valid, a.negate_q != 0, h2);
+
+  // keys below full_lim are visible to every column of the unit; lim is the
+  // last key this lane's query may see
+  const int full_lim = CAUSAL ? min(a.Nk, a.q_offset + qb * a.R + 1) : a.Nk;
+  const int lim = (CAUSAL && col.valid) ? min(a.q_offset + col.i, a.Nk - 1) : a.Nk - 1;
+
+  mrun = kNegInf;
+  lrun = 0.f;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+
+  auto tile_at = [&](int pos) {
+    const int x = (pos < ntiles ? pos : ntiles - 1) + rot;
+    return tile0 + (x >= ntiles ? x - ntiles : x);
+  };
+  TileRegs<C> ra, rb;
+  load_tile<T, C>(ra, kbase, vbase, tile_at(0) * C::BC, a.Nk, tid);
+  load_tile<T, C>(rb, kbase, vbase, tile_at(1) * C::BC, a.Nk, tid);
+  store_tile<T, C>(ra, stK(0), stV(0), tid);
+  __syncthreads();
+
+  auto step = [&](TileRegs<C>& mine, TileRegs<C>& next, int kt) {
+    const int cur = kt & 1;
+    load_tile<T, C>(mine, kbase, vbase, tile_at(kt + 2) * C::BC, a.Nk, tid);
+    f32x16 s[C::KB];
+    qk_tile<T, C>(s, qf, stK(cur), j, h2);
+    const int key0 = tile_at(kt) * C::BC;
+    if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
+    softmax_pv_step<T, C>(s, mrun, lrun, acc, stV(cur), j, h2, a.c);
+    store_tile<T, C>(next, stK(cur ^ 1), stV(cur ^ 1), tid);
+    __syncthreads();
+  };
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    step(ra, rb, kt);
+    if (kt + 1 < ntiles) step(rb, ra, kt + 1);
+  }
+}
+
+// Normalises and stores the finished row of the lane's column.
+template <typename T, class C>
+__device__ __forceinline__ void finish_row(const PrefillArgs& a, const Column& col, float lrun,
+                                           const f32x16 (&acc)[C::DB], int h2) {
+  const float lsum = lrun + __shfl_xor(lrun, 32);
+  if (col.valid) store_out_row<T, C>(reinterpret_cast<T*>(a.o) + col.row_off, acc, 1.0f / lsum, h2);
+}
+
+// Writes the wave's partial state to a record: the accumulator registers as
+// rows of 64 lanes x 4 floats, then (m, l) per lane.
+template <class C>
+__device__ __forceinline__ void write_record(float* rec, float mrun, float lrun,
+                                             const f32x16 (&acc)[C::DB], int w, int lane) {
+  rec += w * wave_record_floats<C>();
+  float4* rec4 = reinterpret_cast<float4*>(rec);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      rec4[(db * 4 + r4) * 64 + lane] = make_float4(acc[db][4 * r4], acc[db][4 * r4 + 1],
+                                                    acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]);
+  reinterpret_cast<float2*>(rec + C::DB * 16 * 64)[lane] = make_float2(mrun, lrun);
 }
 
 template <typename T, class C, bool CAUSAL>
@@ -65,6 +288,7 @@ __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
   __shared__ int s_unit;
+  __shared__ int s_queue;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -72,35 +296,43 @@ prefill_kernel(PrefillArgs a) {
   const int j = lane & 31;
   const int h2 = lane >> 5;
 
-  // stage st: K at smem + st*STAGE_BYTES, V right after it
-  auto stK = [&](int st) { return reinterpret_cast<T*>(smem + st * C::STAGE_BYTES); };
-  auto stV = [&](int st) { return stK(st) + C::K_ELEMS; };
-
-  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q);
-  const T* __restrict__ K = reinterpret_cast<const T*>(a.k);
-  const T* __restrict__ V = reinterpret_cast<const T*>(a.v);
-  T* __restrict__ O = reinterpret_cast<T*>(a.o);
-
-  __shared__ int s_queue;
   const int home = blockIdx.x % kNumQueues;
   const int nkv = a.B * a.Hkv;
   const int per_group = a.HB * a.NQB;
-  int tried = 0;  // queues found empty so far (thread 0 only)
+  bool home_empty = false;  // wave 0: the home queue has run dry
 
   for (;;) {
-    if (tid == 0) {
-      int t = -1, q = 0;
-      while (tried < kNumQueues) {
-        q = (home + tried) % kNumQueues;
-        const int cand = atomicAdd(a.ctr + q, 1);
-        if (cand < queue_units(q, nkv, per_group)) {
-          t = cand;
-          break;
-        }
-        ++tried;
+    __syncthreads();  // every wave has read the previous item's shared words
+    if (w == 0) {
+      // Take the next item of the home queue; once that is empty, look at
+      // every queue at once (lane l reads queue home + l with an atomic add
+      // of zero) and take an item from the first that still has one.  Every
+      // failed take means the queue is empty for good, so this ends.
+      int t = -1, q = home;
+      if (!home_empty) {
+        int cand = 0;
+        if (lane == 0) cand = atomicAdd(a.ctr + home * kCounterStride, 1);
+        cand = __shfl(cand, 0);
+        if (cand < queue_units(home, nkv, per_group)) t = cand;
+        else home_empty = true;
       }
-      s_unit = t;
-      s_queue = q;
+      while (t < 0 && home_empty) {
+        const int ql = (home + lane) % kNumQueues;
+        int left = 0;
+        if (lane < kNumQueues)
+          left = atomicAdd(a.ctr + ql * kCounterStride, a.zero) < queue_units(ql, nkv, per_group);
+        const unsigned long long open = __ballot(left);
+        if (open == 0) break;
+        q = (home + __ffsll((long long)open) - 1) % kNumQueues;
+        int cand = 0;
+        if (lane == 0) cand = atomicAdd(a.ctr + q * kCounterStride, 1);
+        cand = __shfl(cand, 0);
+        if (cand < queue_units(q, nkv, per_group)) t = cand;
+      }
+      if (lane == 0) {
+        s_unit = t;
+        s_queue = q;
+      }
     }
     __syncthreads();
     const int t = s_unit;
@@ -126,91 +358,167 @@ prefill_kernel(PrefillArgs a) {
     const int hkv = kvg % a.Hkv;
     const int b = kvg / a.Hkv;
 
-    // ---- this lane's query column
-    const int m = 32 * w + j;
-    const int r = m / a.R;
-    const int p = m - r * a.R;
-    const int hig = hb * a.Gu + r;  // head within the group
-    const int i = qb * a.R + p;     // query row
-    const bool valid = (r < a.Gu) && (hig < a.g) && (i < a.Nq);
-    const int h = hkv * a.g + hig;
-    const size_t qrow_off = valid ? (((size_t)b * a.Hq + h) * a.Nq + i) * C::D : 0;
-
-    typename C::Frag qf[C::QF];
-    load_q_frag<T, C>(qf, Q + qrow_off, valid, a.negate_q != 0, h2);
-
-    const size_t kv_off = ((size_t)b * a.Hkv + hkv) * a.Nk * C::D;
-    const T* kbase = K + kv_off;
-    const T* vbase = V + kv_off;
-
-    // ---- key range of the unit
-    const int i_lo = qb * a.R;
-    const int i_hi = min(a.Nq, i_lo + a.R) - 1;
-    const int kend = CAUSAL ? min(a.Nk, a.q_offset + i_hi + 1) : a.Nk;
-    const int ntiles = (kend + C::BC - 1) / C::BC;
-    // keys below full_lim are visible to every column of the unit
-    const int full_lim = CAUSAL ? min(a.Nk, a.q_offset + i_lo + 1) : a.Nk;
-    // last key this lane's query may see
-    const int lim = (CAUSAL && valid) ? min(a.q_offset + i, a.Nk - 1) : a.Nk - 1;
-
-    float mrun = kNegInf, lrun = 0.f;
-    f32x16 acc[C::DB];
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
-
-    // Two LDS stages and two register staging sets: the global loads of tile
-    // t+2 are issued at the start of tile t and written to LDS at the end of
-    // tile t+1, so two tiles of compute cover their latency.  The loop is
-    // unrolled by two so each staging set is a named register set, and the
-    // loads and stores are unconditional (indices clamped to the last tile)
-    // so the compiler's wait before each LDS store counts exactly the newer
-    // loads still in flight.
-    //
-    // Each unit walks its tiles starting at a unit-dependent rotation, so the
-    // many workgroups that share a K/V head do not all request the same
-    // tile at the same moment.  The order of tiles does not change the
-    // result in exact arithmetic (masking is per key, and a lane whose first
-    // tiles are all masked keeps an empty state until a visible key comes).
+    const int ntiles = unit_tiles<C, CAUSAL>(a, qb);
     const int rot = (int)((7u * (unsigned)t + 3u * (unsigned)q) % (unsigned)ntiles);
-    auto tile_at = [&](int pos) {
-      const int x = (pos < ntiles ? pos : ntiles - 1) + rot;
-      return x >= ntiles ? x - ntiles : x;
-    };
-    TileRegs<C> ra, rb;
-    load_tile<T, C>(ra, kbase, vbase, tile_at(0) * C::BC, a.Nk, tid);
-    load_tile<T, C>(rb, kbase, vbase, tile_at(1) * C::BC, a.Nk, tid);
-    store_tile<T, C>(ra, stK(0), stV(0), tid);
-    __syncthreads();
-
-    auto step = [&](TileRegs<C>& mine, TileRegs<C>& next, int kt) {
-      const int cur = kt & 1;
-      load_tile<T, C>(mine, kbase, vbase, tile_at(kt + 2) * C::BC, a.Nk, tid);
-      f32x16 s[C::KB];
-      qk_tile<T, C>(s, qf, stK(cur), j, h2);
-      const int key0 = tile_at(kt) * C::BC;
-      if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
-      softmax_pv_step<T, C>(s, mrun, lrun, acc, stV(cur), j, h2, a.c);
-      store_tile<T, C>(next, stK(cur ^ 1), stV(cur ^ 1), tid);
-      __syncthreads();
-    };
-    for (int kt = 0; kt < ntiles; kt += 2) {
-      step(ra, rb, kt);
-      if (kt + 1 < ntiles) step(rb, ra, kt + 1);
-    }
-
-    const float lsum = lrun + __shfl_xor(lrun, 32);
-    if (valid) store_out_row<T, C>(O + qrow_off, acc, 1.0f / lsum, h2);
+    const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
+    float mrun, lrun;
+    f32x16 acc[C::DB];
+    run_segment<T, C, CAUSAL>(a, smem, b, hkv, qb, 0, ntiles, rot, col, mrun, lrun, acc);
+    finish_row<T, C>(a, col, lrun, acc, h2);
   }
 
   // Leave the counters at zero for the next launch: the last workgroup out
   // (all others have made their final, failing fetches) resets every word.
   if (tid == 0) {
     __threadfence();
-    const int done = atomicAdd(a.ctr + kNumQueues, 1);
+    const int done = atomicAdd(a.ctr + kNumQueues * kCounterStride, 1);
     if (done == (int)gridDim.x - 1) {
-      for (int i = 0; i <= kNumQueues; ++i) atomicExch(a.ctr + i, 0);
+      for (int i = 0; i <= kNumQueues; ++i) atomicExch(a.ctr + i * kCounterStride, 0);
     }
   }
+}
+
+// Workgroup g = c * nsl + s runs chunk c of slice s, so the workgroups of a
+// slice share an XCD whenever nsl is a multiple of kNumQueues.  Segments
+// that cover a whole unit store the result; a cut unit's first segment in
+// the chunk goes to record slot 0 and its last to slot 1 (a segment that is
+// not the chunk's first always reaches the chunk's end).
+template <typename T, class C, bool CAUSAL>
+__global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+prefill_balanced_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int j = lane & 31;
+  const int h2 = lane >> 5;
+
+  const int g = blockIdx.x;
+  const int s = g % a.nsl;
+  const int c = g / a.nsl;
+  const int hb = s % a.HB;
+  const int kvg = s / a.HB;
+  const int hkv = kvg % a.Hkv;
+  const int b = kvg / a.Hkv;
+
+  const int x_end = chunk_bound(a, c + 1);
+  int x = chunk_bound(a, c);
+  int pos, pre;
+  locate_tile<C, CAUSAL>(a, x, lane, pos, pre);
+  for (int seg = 0; x < x_end && pos < a.NQB; ++seg) {
+    const int qb = seq_qb<CAUSAL>(pos, a.NQB);
+    const int n = unit_tiles<C, CAUSAL>(a, qb);
+    const int t0 = x - pre;
+    const int t1 = min(n, x_end - pre);
+    const int ntiles = t1 - t0;
+    const int rot = (int)((7u * (unsigned)g + 5u * (unsigned)seg) % (unsigned)ntiles);
+    const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
+    float mrun, lrun;
+    f32x16 acc[C::DB];
+    run_segment<T, C, CAUSAL>(a, smem, b, hkv, qb, t0, ntiles, rot, col, mrun, lrun, acc);
+    if (t0 == 0 && t1 == n)
+      finish_row<T, C>(a, col, lrun, acc, h2);
+    else if (a.ws)  // the host provides records whenever a chunk boundary cuts a unit
+      write_record<C>(part_record<C>(a, g, seg == 0 ? 0 : 1), mrun, lrun, acc, w, lane);
+    x = pre + t1;
+    pre += n;
+    ++pos;
+  }
+}
+
+// Combines the pieces of each unit cut by the balanced schedule.  Block
+// ((c - 1) * nsl + s) * NW + w, of DB waves, looks at chunk boundary c of
+// slice s and, if it is the first boundary inside the unit it cuts, merges
+// that unit's pieces (those of chunks c - 1 .. c_hi) for the columns of
+// prefill wave w; wave i of the block takes accumulator block db = i.  The
+// pieces are merged in chunk order with the rescaling of the online softmax
+// (piece p's state is relative to its own reference m_p; the merged
+// reference is M = max_p m_p and piece p is weighted by 2^((m_p - M) c)),
+// so the result does not depend on timing.  All loads of up to
+// kMergeBatch pieces are issued before the first is used.
+constexpr int kMergeBatch = 4;
+template <typename T, class C, bool CAUSAL>
+__global__ void __launch_bounds__(64 * C::DB) prefill_merge_kernel(PrefillArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int db = threadIdx.x >> 6;
+  const int j = lane & 31;
+  const int h2 = lane >> 5;
+
+  const int w = blockIdx.x % C::NW;
+  const int bs = blockIdx.x / C::NW;
+  const int s = bs % a.nsl;
+  const int c = bs / a.nsl + 1;  // boundary 1 .. Pp-1
+  const int X = chunk_bound(a, c);
+  int pos, pre;
+  locate_tile<C, CAUSAL>(a, X, lane, pos, pre);
+  if (pre == X || chunk_bound(a, c - 1) > pre) return;  // no cut here, or merged elsewhere
+  const int qb = seq_qb<CAUSAL>(pos, a.NQB);
+  const int n = unit_tiles<C, CAUSAL>(a, qb);
+  const int hb = s % a.HB;
+  const int kvg = s / a.HB;
+  const int hkv = kvg % a.Hkv;
+  const int b = kvg / a.Hkv;
+  const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
+
+  // pieces: chunk k = c-1 .. c_hi; chunk c-1's piece is its workgroup's
+  // first segment only if the chunk starts at the unit's first tile
+  int c_hi = c;
+  while (c_hi + 1 < a.Pp && chunk_bound(a, c_hi + 1) < pre + n) ++c_hi;
+  const int np = c_hi - c + 2;
+  const int slot_first = chunk_bound(a, c - 1) < pre ? 1 : 0;
+  const float* rec0 = part_record<C>(a, (c - 1) * a.nsl + s, 0) + w * wave_record_floats<C>();
+  auto rec_of = [&](int p) {
+    p = min(p, np - 1);  // beyond the last piece: repeat it (unused)
+    return rec0 + ((size_t)p * a.nsl * 2 + (p == 0 ? slot_first : 0)) * part_floats<C>();
+  };
+
+  float2 ml[kMaxPiecesDev];
+#pragma unroll
+  for (int p = 0; p < kMaxPiecesDev; ++p)
+    ml[p] = reinterpret_cast<const float2*>(rec_of(p) + C::DB * 16 * 64)[lane];
+  float4 x[kMergeBatch][4];
+#pragma unroll
+  for (int p = 0; p < kMergeBatch; ++p)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      x[p][r4] = reinterpret_cast<const float4*>(rec_of(p))[(db * 4 + r4) * 64 + lane];
+  float M = kNegInf;
+#pragma unroll
+  for (int p = 0; p < kMaxPiecesDev; ++p) M = fmaxf(M, ml[p].x);
+
+  f32x16 acc[1] = {f32x16{}};
+  float l = 0.f;
+  for (int p0 = 0; p0 < np; p0 += kMergeBatch) {
+    if (p0 > 0) {
+#pragma unroll
+      for (int p = 0; p < kMergeBatch; ++p)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          x[p][r4] = reinterpret_cast<const float4*>(rec_of(p0 + p))[(db * 4 + r4) * 64 + lane];
+    }
+#pragma unroll
+    for (int p = 0; p < kMergeBatch; ++p) {
+      if (p0 + p < np) {
+        float mp = ml[0].x, lp = ml[0].y;
+#pragma unroll
+        for (int i = 1; i < kMaxPiecesDev; ++i)
+          if (i == p0 + p) { mp = ml[i].x; lp = ml[i].y; }
+        const float wgt = mp == kNegInf ? 0.f : fast_exp2((mp - M) * a.c);
+        l += wgt * lp;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          acc[0][4 * r4] += wgt * x[p][r4].x;
+          acc[0][4 * r4 + 1] += wgt * x[p][r4].y;
+          acc[0][4 * r4 + 2] += wgt * x[p][r4].z;
+          acc[0][4 * r4 + 3] += wgt * x[p][r4].w;
+        }
+      }
+    }
+  }
+  const float lsum = l + __shfl_xor(l, 32);
+  if (col.valid)
+    store_out_block<T, C>(reinterpret_cast<T*>(a.o) + col.row_off, acc[0], 1.0f / lsum, db, h2);
 }
 
 }  // namespace gqa

@@ -247,3 +247,38 @@ def test_two_streams_keep_separate_schedulers():
     for group in outs:
         for o in group:
             assert torch.equal(o, ref)
+
+
+# ---------------------------------------------------------------- key-split units
+# Launches with few units cut each slice's key tiles into equal chunks, one
+# per workgroup; units that a chunk boundary cuts are merged from their pieces.
+
+SPLIT_SHAPES = [
+    # MQA, 8 units of 256 tiles: every unit is cut into many pieces
+    FwdShape(1, 8, 1, 128, 8192, 128, False, 0),
+    # MHA causal with an offset: parts where some query rows see no key
+    FwdShape(1, 2, 2, 700, 737, 64, True, 37),
+    # fp32 chunk at the end of a long cache
+    FwdShape(2, 4, 1, 64, 2000, 32, True, 1936, torch.float32),
+    # GQA causal prefill, one sequence
+    FwdShape(1, 16, 2, 1500, 1500, 128, True, 0),
+]
+
+
+@pytest.mark.parametrize("s", SPLIT_SHAPES, ids=["mqa_long_keys", "mha_causal_offset",
+                                                 "f32_chunk", "gqa_causal"])
+def test_key_split_parity_and_determinism(s):
+    q, k, v, out = _check_fwd(s, 31)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    for _ in range(5):
+        again = attn_fwd(qd, kd, vd, causal=s.causal, q_offset=s.q_offset, scale=s.scale)
+        assert torch.equal(again.cpu(), out)
+
+
+def test_key_split_workspace_regrows_between_sizes():
+    """Launches with cut units, of growing and shrinking sizes, on one stream."""
+    shapes = [FwdShape(1, 4, 1, 32, 600, 64, False, 0),
+              FwdShape(1, 8, 1, 128, 8192, 128, False, 0),
+              FwdShape(1, 4, 1, 32, 600, 64, False, 0)]
+    for n, s in enumerate(shapes):
+        _check_fwd(s, 40 + n)
