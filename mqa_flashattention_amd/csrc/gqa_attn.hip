@@ -258,6 +258,20 @@ int launch_prefill(gqa::PrefillArgs& a, int dev_id, const DeviceInfo& dev, hipSt
   const long long slots = (long long)dev.cus * per_cu;
   long long cuts = 0;
   const bool balanced = plan_balanced<C>(a, CAUSAL, slots, &cuts);
+  // causal, with at least one heavy/light unit pair per CU: one pair per
+  // workgroup of two halves that split each unit's keys
+  const long long pairs = (long long)a.nsl * ((a.NQB + 1) / 2);
+  if (CAUSAL && balanced && pairs >= dev.cus) {
+    StreamState ss;
+    int st = stream_state(dev_id, stream, 0, &ss);
+    if (st != GQA_OK) return st;
+    (void)hipGetLastError();  // a stale error belongs to an earlier call
+    hipLaunchKernelGGL((gqa::prefill_pair_kernel<T, C, CAUSAL>), dim3((unsigned)pairs),
+                       dim3(2 * C::NT), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "prefill pair kernel launch");
+    return GQA_OK;
+  }
   const long long grid = balanced ? (long long)a.nsl * a.Pp : std::min<long long>(a.T, slots);
   const size_t ws_bytes = cuts > 0 ? (size_t)grid * 2 * gqa::part_floats<C>() * sizeof(float) : 0;
   StreamState ss;

@@ -202,12 +202,18 @@ __device__ __forceinline__ Column lane_column(const PrefillArgs& a, int b, int h
 // same moment.  The order of tiles does not change the result in exact
 // arithmetic (masking is per key, and a lane whose first tiles are all
 // masked keeps an empty state until a visible key comes).
-template <typename T, class C, bool CAUSAL>
+//
+// PAIRED: two groups of NW waves (one per half of the workgroup) run the
+// function together on their own LDS rings, each over its own tile range;
+// both loop `steps` times (the longer range) so that they meet at every
+// barrier, and a group whose range is shorter (possibly empty: then tile0
+// must still be a valid tile) skips the compute of its last steps.
+template <typename T, class C, bool CAUSAL, bool PAIRED = false>
 __device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, int b, int hkv,
                                             int qb, int tile0, int ntiles, int rot,
                                             const Column& col, float& mrun, float& lrun,
-                                            f32x16 (&acc)[C::DB]) {
-  const int tid = threadIdx.x;
+                                            f32x16 (&acc)[C::DB], int steps = 0) {
+  const int tid = threadIdx.x % C::NT;  // index within the loading group
   const int lane = tid & 63;
   const int j = lane & 31;
   const int h2 = lane >> 5;
@@ -233,9 +239,11 @@ __device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, in
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
   auto tile_at = [&](int pos) {
+    if (PAIRED && ntiles == 0) return tile0;
     const int x = (pos < ntiles ? pos : ntiles - 1) + rot;
     return tile0 + (x >= ntiles ? x - ntiles : x);
   };
+  if (!PAIRED) steps = ntiles;
   TileRegs<C> ra, rb;
   load_tile<T, C>(ra, kbase, vbase, tile_at(0) * C::BC, a.Nk, tid);
   load_tile<T, C>(rb, kbase, vbase, tile_at(1) * C::BC, a.Nk, tid);
@@ -245,17 +253,19 @@ __device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, in
   auto step = [&](TileRegs<C>& mine, TileRegs<C>& next, int kt) {
     const int cur = kt & 1;
     load_tile<T, C>(mine, kbase, vbase, tile_at(kt + 2) * C::BC, a.Nk, tid);
-    f32x16 s[C::KB];
-    qk_tile<T, C>(s, qf, stK(cur), j, h2);
-    const int key0 = tile_at(kt) * C::BC;
-    if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
-    softmax_pv_step<T, C>(s, mrun, lrun, acc, stV(cur), j, h2, a.c);
+    if (!PAIRED || kt < ntiles) {
+      f32x16 s[C::KB];
+      qk_tile<T, C>(s, qf, stK(cur), j, h2);
+      const int key0 = tile_at(kt) * C::BC;
+      if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
+      softmax_pv_step<T, C>(s, mrun, lrun, acc, stV(cur), j, h2, a.c);
+    }
     store_tile<T, C>(next, stK(cur ^ 1), stV(cur ^ 1), tid);
     __syncthreads();
   };
-  for (int kt = 0; kt < ntiles; kt += 2) {
+  for (int kt = 0; kt < steps; kt += 2) {
     step(ra, rb, kt);
-    if (kt + 1 < ntiles) step(rb, ra, kt + 1);
+    if (kt + 1 < steps) step(rb, ra, kt + 1);
   }
 }
 
@@ -427,8 +437,79 @@ prefill_balanced_kernel(PrefillArgs a) {
   }
 }
 
+// Causal launches with about one unit pair per CU: workgroup g of 2*NW waves
+// runs the pair (qb = NQB-1-p, qb = p), p = g / nsl, of slice s = g % nsl;
+// every pair holds about the same number of key tiles, so a static
+// one-pair-per-workgroup schedule is balanced.  The two halves of the
+// workgroup (waves 0..NW-1 and NW..2NW-1) take the first and second half of
+// each unit's key tiles on LDS rings of their own, for the same columns;
+// the second half then hands its state (m, l, unnormalised O) to the first
+// through LDS, which merges the two in a fixed order and stores the rows.
+template <typename T, class C, bool CAUSAL>
+__global__ void __launch_bounds__(2 * C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+prefill_pair_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[4 * C::STAGE_BYTES];
+  static_assert(4 * C::STAGE_BYTES >= C::NT * (C::DB * 16 + 2) * 4, "hand-over area too small");
+
+  const int tid = threadIdx.x;
+  const int half = tid / C::NT;
+  const int w = (tid % C::NT) >> 6;
+  const int lane = tid & 63;
+  const int j = lane & 31;
+  const int h2 = lane >> 5;
+
+  const int g = blockIdx.x;
+  const int s = g % a.nsl;
+  const int p = g / a.nsl;
+  const int hb = s % a.HB;
+  const int kvg = s / a.HB;
+  const int hkv = kvg % a.Hkv;
+  const int b = kvg / a.Hkv;
+  char* ring = smem + half * 2 * C::STAGE_BYTES;
+  float* hand = reinterpret_cast<float*>(smem) + (w * 64 + lane);  // [DB*16 + 2][NT] floats
+
+  for (int u = 0; u < 2; ++u) {
+    const int qb = u == 0 ? a.NQB - 1 - p : p;
+    if (u == 1 && qb >= a.NQB - 1 - p) break;  // middle unit of an odd NQB: done once
+    const int n = unit_tiles<C, CAUSAL>(a, qb);
+    const int n0 = (n + 1) / 2;
+    const int tile0 = half ? n0 : 0;
+    const int nt = half ? n - n0 : n0;
+    const int rot = nt > 0 ? (int)((7u * (unsigned)g + 3u * (unsigned)u) % (unsigned)nt) : 0;
+    const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
+    float mrun, lrun;
+    f32x16 acc[C::DB];
+    run_segment<T, C, CAUSAL, true>(a, ring, b, hkv, qb, half ? min(n0, n - 1) : 0, nt, rot, col,
+                                    mrun, lrun, acc, n0);
+    // hand-over: the rings are free (run_segment ends on a barrier)
+    if (half) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hand[(db * 16 + r) * C::NT] = acc[db][r];
+      hand[(C::DB * 16) * C::NT] = mrun;
+      hand[(C::DB * 16 + 1) * C::NT] = lrun;
+    }
+    __syncthreads();
+    if (!half) {
+      const float m1 = hand[(C::DB * 16) * C::NT];
+      const float l1 = hand[(C::DB * 16 + 1) * C::NT];
+      const float M = fmaxf(mrun, m1);
+      const float w0 = mrun == kNegInf ? 0.f : fast_exp2((mrun - M) * a.c);
+      const float w1 = m1 == kNegInf ? 0.f : fast_exp2((m1 - M) * a.c);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[db][r] = w0 * acc[db][r] + w1 * hand[(db * 16 + r) * C::NT];
+      finish_row<T, C>(a, col, w0 * lrun + w1 * l1, acc, h2);
+    }
+    __syncthreads();  // the hand-over area is ring memory again
+  }
+}
+
 // Combines the pieces of each unit cut by the balanced schedule.  Block
-// ((c - 1) * nsl + s) * NW + w, of DB waves, looks at chunk boundary c of
+// (w * (Pp - 1) + c - 1) * nsl + s, of DB waves, looks at chunk boundary c of
 // slice s and, if it is the first boundary inside the unit it cuts, merges
 // that unit's pieces (those of chunks c - 1 .. c_hi) for the columns of
 // prefill wave w; wave i of the block takes accumulator block db = i.  The
@@ -445,10 +526,10 @@ __global__ void __launch_bounds__(64 * C::DB) prefill_merge_kernel(PrefillArgs a
   const int j = lane & 31;
   const int h2 = lane >> 5;
 
-  const int w = blockIdx.x % C::NW;
-  const int bs = blockIdx.x / C::NW;
-  const int s = bs % a.nsl;
-  const int c = bs / a.nsl + 1;  // boundary 1 .. Pp-1
+  const int nb = a.nsl * (a.Pp - 1);
+  const int w = blockIdx.x / nb;
+  const int s = blockIdx.x % a.nsl;
+  const int c = (blockIdx.x % nb) / a.nsl + 1;  // boundary 1 .. Pp-1
   const int X = chunk_bound(a, c);
   int pos, pre;
   locate_tile<C, CAUSAL>(a, X, lane, pos, pre);
