@@ -90,27 +90,35 @@ def traffic_from_counters():
 
 
 def _counter_means(directory: str, counter: str) -> dict:
-    """Mean per-dispatch value of one rocprofv3 counter, by kernel kind."""
+    """Mean per-dispatch value of one rocprofv3 counter, by kernel kind: the
+    d=128 bf16 causal prefill kernel(s) the bench workload launches, and the
+    calibration copy.  Also returns the prefill kernel names seen."""
     import csv
     import glob
     files = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no counter_collection.csv under {directory}")
     vals: dict = {}
+    names: set = set()
     for path in files:
         with open(path) as f:
             for row in csv.DictReader(f):
                 if row["Counter_Name"] != counter:
                     continue
                 name = row["Kernel_Name"]
-                if "prefill_kernel" in name and "128, 64, 4>, true" in name:
-                    kind = "prefill"
+                if "gqa::prefill" in name and "128, 32, 4>, true" in name:
+                    kind = name.split("(")[0].replace("void ", "")
+                    names.add(kind)
                 elif "neg_kernel" in name:
                     kind = "copy"
                 else:
                     continue
                 vals.setdefault(kind, []).append(float(row["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in vals.items()}
+    means = {k: sum(v) / len(v) for k, v in vals.items()}
+    # one prefill launch = one dispatch of each prefill kernel it uses
+    out = {"copy": means["copy"], "prefill": sum(means[n] for n in names),
+           "names": sorted(names)}
+    return out
 
 
 def summarize_counters(fetch_dir: str, write_dir: str) -> dict:
@@ -124,7 +132,7 @@ def summarize_counters(fetch_dir: str, write_dir: str) -> dict:
     write_factor = COPY_BYTES / (write["copy"] * 1024.0)
     traffic = fetch["prefill"] * 1024.0 * read_factor + write["prefill"] * 1024.0 * write_factor
     out = {
-        "kernel": "prefill_kernel<bf16, d128, 64-key tiles, 4 waves, causal>",
+        "kernel": ", ".join(fetch["names"]),
         "workload": "llama3_8b_prefill (B1 Hq32 Hkv8 N2048 d128 causal, bf16)",
         "fetch_kib_per_launch": round(fetch["prefill"], 1),
         "write_kib_per_launch": round(write["prefill"], 1),

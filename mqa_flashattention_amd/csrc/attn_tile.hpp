@@ -65,6 +65,20 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane l and lane l ^ 32 combined, in every lane: v_permlane32_swap with
+// both operands x leaves (x[l mod 32], x[l mod 32 + 32]) in the two results,
+// a VALU exchange of the half-waves instead of an LDS permute.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // K row read by MFMA row i of a 32-key block: bits 2 and 3 of i swapped.
 __device__ __forceinline__ int k_row_perm(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
@@ -314,7 +328,7 @@ __device__ __forceinline__ float tile_rowmax(const f32x16 (&s)[C::KB]) {
   for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
-  return fmaxf(mt, __shfl_xor(mt, 32));
+  return halves_max(mt);
 }
 
 // Raise the running reference to m_new = max(m, mt) and rescale l and acc by
@@ -339,7 +353,7 @@ template <class C>
 __device__ __forceinline__ float tile_weights(const f32x16 (&s)[C::KB], float m, float c,
                                               typename C::Frag (&pf)[C::KB][C::PF]) {
   const float mc = m == kNegInf ? 0.f : m * c;  // all-masked so far: every weight is 0
-  float lt = 0.f;
+  float lt = 0.f, lt2 = 0.f;
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) {
     if constexpr (C::F32) {
@@ -360,14 +374,16 @@ __device__ __forceinline__ float tile_weights(const f32x16 (&s)[C::KB], float m,
           bf16x2 pk;
           pk.x = (__bf16)p0;
           pk.y = (__bf16)p1;
-          lt = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, lt, false);
+          float& acc_l = (e & 1) ? lt2 : lt;  // two chains
+          acc_l = __builtin_amdgcn_fdot2_f32_bf16(pk, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, acc_l,
+                                                  false);
           w[e] = __builtin_bit_cast(uint32_t, pk);
         }
         pf[kb][hk] = __builtin_bit_cast(bf16x8, w);
       }
     }
   }
-  return lt;
+  return lt + lt2;
 }
 
 // acc[db] += V^T P^T for one tile (O^T rows 32*db .. 32*db+31).

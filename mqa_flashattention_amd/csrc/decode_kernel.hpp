@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     if (kt + 1 < ntiles) step(rb, kt + 1);
   }
 
-  const float lsum = lrun + __shfl_xor(lrun, 32);
+  const float lsum = halves_sum(lrun);
   if (valid) {
     float* part = a.ws + (((size_t)b * a.Hq + h) * a.NS + s_idx) * (C::D + 4);
 #pragma unroll

@@ -273,7 +273,7 @@ __device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, in
 template <typename T, class C>
 __device__ __forceinline__ void finish_row(const PrefillArgs& a, const Column& col, float lrun,
                                            const f32x16 (&acc)[C::DB], int h2) {
-  const float lsum = lrun + __shfl_xor(lrun, 32);
+  const float lsum = halves_sum(lrun);
   if (col.valid) store_out_row<T, C>(reinterpret_cast<T*>(a.o) + col.row_off, acc, 1.0f / lsum, h2);
 }
 
@@ -597,7 +597,7 @@ __global__ void __launch_bounds__(64 * C::DB) prefill_merge_kernel(PrefillArgs a
       }
     }
   }
-  const float lsum = l + __shfl_xor(l, 32);
+  const float lsum = halves_sum(l);
   if (col.valid)
     store_out_block<T, C>(reinterpret_cast<T*>(a.o) + col.row_off, acc[0], 1.0f / lsum, db, h2);
 }
