@@ -424,15 +424,24 @@ __device__ __forceinline__ void pv_tile(f32x16 (&acc)[C::DB],
 // bf16 range -- and acc / l is unchanged in exact arithmetic.
 constexpr float kRescaleSlack = 16.0f;
 
+// The softmax half of the step: raises the reference if needed and leaves
+// the weights in pf (for pv_tile) and their sum added to l.
+template <class C>
+__device__ __forceinline__ void softmax_step(const f32x16 (&s)[C::KB], float& m, float& l,
+                                             f32x16 (&acc)[C::DB],
+                                             typename C::Frag (&pf)[C::KB][C::PF], float c) {
+  const float mt = tile_rowmax<C>(s);
+  if (__any(m == kNegInf ? mt != kNegInf : (mt - m) * c > kRescaleSlack))
+    raise_reference<C>(m, l, acc, mt, c);
+  l += tile_weights<C>(s, m, c, pf);
+}
+
 template <typename T, class C>
 __device__ __forceinline__ void softmax_pv_step(f32x16 (&s)[C::KB], float& m, float& l,
                                                 f32x16 (&acc)[C::DB], const T* __restrict__ Vs,
                                                 int lane32, int h2, float c) {
-  const float mt = tile_rowmax<C>(s);
-  if (__any(m == kNegInf ? mt != kNegInf : (mt - m) * c > kRescaleSlack))
-    raise_reference<C>(m, l, acc, mt, c);
   typename C::Frag pf[C::KB][C::PF];
-  l += tile_weights<C>(s, m, c, pf);
+  softmax_step<C>(s, m, l, acc, pf, c);
   pv_tile<T, C>(acc, pf, Vs, lane32, h2);
 }
 

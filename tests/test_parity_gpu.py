@@ -282,3 +282,25 @@ def test_key_split_workspace_regrows_between_sizes():
               FwdShape(1, 4, 1, 32, 600, 64, False, 0)]
     for n, s in enumerate(shapes):
         _check_fwd(s, 40 + n)
+
+
+# ---------------------------------------------------------------- pair schedule
+# Causal launches with at least one heavy/light unit pair per CU run one pair
+# per 8-wave workgroup whose halves split each unit's keys (the LLaMA-shaped
+# prefill above is one); these cover an odd number of position blocks (the
+# middle unit runs alone), a chunk at an offset, and fp32.
+
+PAIR_SHAPES = [
+    FwdShape(2, 8, 8, 4100, 4100, 128, True, 0),
+    FwdShape(8, 32, 8, 256, 3000, 128, True, 2744),
+    FwdShape(4, 16, 2, 1030, 1030, 64, True, 0, torch.float32),
+]
+
+
+@pytest.mark.parametrize("s", PAIR_SHAPES, ids=["mha_odd_blocks", "gqa_chunk_offset", "f32_gqa"])
+def test_pair_schedule_sampled(s):
+    q, k, v, out = _check_fwd(s, 51, rows=512)
+    again = attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, q_offset=s.q_offset,
+                     scale=s.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(again.cpu(), out)
