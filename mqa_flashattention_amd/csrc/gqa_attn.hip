@@ -14,6 +14,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <utility>
 
 #include "decode_kernel.hpp"
@@ -186,6 +187,17 @@ using CfgBf16 = gqa::TileCfg<uint16_t, D, (D == 128 ? 32 : 64), kPrefillWaves>;
 template <int D>
 using CfgF32 = gqa::TileCfg<float, D, 32, kPrefillWaves>;
 
+// Unit decomposition for units of M columns: Gu = min(g, M) heads of a
+// group stacked over R = M / Gu positions, HB head blocks per group, NQB
+// position blocks, T units.
+void decompose(gqa::PrefillArgs& a, int M) {
+  a.Gu = a.g < M ? a.g : M;
+  a.R = M / a.Gu;
+  a.HB = (a.g + a.Gu - 1) / a.Gu;
+  a.NQB = (a.Nq + a.R - 1) / a.R;
+  a.T = a.B * a.Hkv * a.HB * a.NQB;
+}
+
 // Key tiles of the units of position block qb (host copy of the kernels'
 // unit_tiles).
 template <class C>
@@ -259,18 +271,29 @@ int launch_prefill(gqa::PrefillArgs& a, int dev_id, const DeviceInfo& dev, hipSt
   long long cuts = 0;
   const bool balanced = plan_balanced<C>(a, CAUSAL, slots, &cuts);
   // causal, with at least one heavy/light unit pair per CU: one pair per
-  // workgroup of two halves that split each unit's keys
-  const long long pairs = (long long)a.nsl * ((a.NQB + 1) / 2);
-  if (CAUSAL && balanced && pairs >= dev.cus) {
-    StreamState ss;
-    int st = stream_state(dev_id, stream, 0, &ss);
-    if (st != GQA_OK) return st;
-    (void)hipGetLastError();  // a stale error belongs to an earlier call
-    hipLaunchKernelGGL((gqa::prefill_pair_kernel<T, C, CAUSAL>), dim3((unsigned)pairs),
-                       dim3(2 * C::NT), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "prefill pair kernel launch");
-    return GQA_OK;
+  // workgroup of two 4-wave halves that split each unit's keys.  (Halves
+  // of 2 waves on 64-column units, two workgroups per CU, were measured
+  // slower: each staged tile then serves half as many columns.)
+  if constexpr (CAUSAL) {
+    using CP = C;
+    gqa::PrefillArgs p = a;
+    long long pairs = 0;
+    if (balanced) {
+      decompose(p, 32 * CP::NW);
+      p.nsl = p.B * p.Hkv * p.HB;
+      pairs = (long long)p.nsl * ((p.NQB + 1) / 2);
+    }
+    if (balanced && pairs >= dev.cus) {
+      StreamState ss;
+      int st = stream_state(dev_id, stream, 0, &ss);
+      if (st != GQA_OK) return st;
+      (void)hipGetLastError();  // a stale error belongs to an earlier call
+      hipLaunchKernelGGL((gqa::prefill_pair_kernel<T, CP, CAUSAL>), dim3((unsigned)pairs),
+                         dim3(2 * CP::NT), 0, stream, p);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "prefill pair kernel launch");
+      return GQA_OK;
+    }
   }
   const long long grid = balanced ? (long long)a.nsl * a.Pp : std::min<long long>(a.T, slots);
   const size_t ws_bytes = cuts > 0 ? (size_t)grid * 2 * gqa::part_floats<C>() * sizeof(float) : 0;

@@ -437,10 +437,11 @@ prefill_balanced_kernel(PrefillArgs a) {
   }
 }
 
-// Causal launches with about one unit pair per CU: workgroup g of 2*NW waves
-// runs the pair (qb = NQB-1-p, qb = p), p = g / nsl, of slice s = g % nsl;
-// every pair holds about the same number of key tiles, so a static
-// one-pair-per-workgroup schedule is balanced.  The two halves of the
+// Causal launches with about one unit pair per resident workgroup: workgroup
+// g of 2*NW waves runs the pair (qb = NQB-1-p, qb = p), p = g / nsl, of
+// slice s = g % nsl; every pair holds about the same number of key tiles, so
+// a static one-pair-per-workgroup schedule is balanced.  The units here have
+// 32*NW columns (the host decomposes for that width).  The two halves of the
 // workgroup (waves 0..NW-1 and NW..2NW-1) take the first and second half of
 // each unit's key tiles on LDS rings of their own, for the same columns;
 // the second half then hands its state (m, l, unnormalised O) to the first
@@ -466,14 +467,17 @@ prefill_pair_kernel(PrefillArgs a) {
   const int hkv = kvg % a.Hkv;
   const int b = kvg / a.Hkv;
   char* ring = smem + half * 2 * C::STAGE_BYTES;
-  float* hand = reinterpret_cast<float*>(smem) + (w * 64 + lane);  // [DB*16 + 2][NT] floats
+  // hand-over area: DB*4 rows of NT float4 (the accumulator), then NT float2
+  // (m, l); 16-byte accesses, consecutive lanes on consecutive addresses
+  float4* hand4 = reinterpret_cast<float4*>(smem) + (w * 64 + lane);
+  float2* hand2 = reinterpret_cast<float2*>(reinterpret_cast<float4*>(smem) + C::DB * 4 * C::NT) +
+                  (w * 64 + lane);
 
   for (int u = 0; u < 2; ++u) {
     const int qb = u == 0 ? a.NQB - 1 - p : p;
     if (u == 1 && qb >= a.NQB - 1 - p) break;  // middle unit of an odd NQB: done once
     const int n = unit_tiles<C, CAUSAL>(a, qb);
     const int n0 = (n + 1) / 2;
-    const int tile0 = half ? n0 : 0;
     const int nt = half ? n - n0 : n0;
     const int rot = nt > 0 ? (int)((7u * (unsigned)g + 3u * (unsigned)u) % (unsigned)nt) : 0;
     const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
@@ -486,23 +490,28 @@ prefill_pair_kernel(PrefillArgs a) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) hand[(db * 16 + r) * C::NT] = acc[db][r];
-      hand[(C::DB * 16) * C::NT] = mrun;
-      hand[(C::DB * 16 + 1) * C::NT] = lrun;
+        for (int r4 = 0; r4 < 4; ++r4)
+          hand4[(db * 4 + r4) * C::NT] = make_float4(acc[db][4 * r4], acc[db][4 * r4 + 1],
+                                                     acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]);
+      *hand2 = make_float2(mrun, lrun);
     }
     __syncthreads();
     if (!half) {
-      const float m1 = hand[(C::DB * 16) * C::NT];
-      const float l1 = hand[(C::DB * 16 + 1) * C::NT];
-      const float M = fmaxf(mrun, m1);
+      const float2 ml1 = *hand2;
+      const float M = fmaxf(mrun, ml1.x);
       const float w0 = mrun == kNegInf ? 0.f : fast_exp2((mrun - M) * a.c);
-      const float w1 = m1 == kNegInf ? 0.f : fast_exp2((m1 - M) * a.c);
+      const float w1 = ml1.x == kNegInf ? 0.f : fast_exp2((ml1.x - M) * a.c);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[db][r] = w0 * acc[db][r] + w1 * hand[(db * 16 + r) * C::NT];
-      finish_row<T, C>(a, col, w0 * lrun + w1 * l1, acc, h2);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 o1 = hand4[(db * 4 + r4) * C::NT];
+          acc[db][4 * r4] = w0 * acc[db][4 * r4] + w1 * o1.x;
+          acc[db][4 * r4 + 1] = w0 * acc[db][4 * r4 + 1] + w1 * o1.y;
+          acc[db][4 * r4 + 2] = w0 * acc[db][4 * r4 + 2] + w1 * o1.z;
+          acc[db][4 * r4 + 3] = w0 * acc[db][4 * r4 + 3] + w1 * o1.w;
+        }
+      finish_row<T, C>(a, col, w0 * lrun + w1 * ml1.y, acc, h2);
     }
     __syncthreads();  // the hand-over area is ring memory again
   }
