@@ -269,12 +269,58 @@ __device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, in
   }
 }
 
-// Normalises and stores the finished row of the lane's column.
+// Bytes of one wave's output staging area: its 32 rows of O with a
+// 16-byte pad per row (which spreads the rows over the LDS banks).
+template <class C>
+constexpr int stage_out_bytes() {
+  return 32 * (C::D * C::ESZ + 16);
+}
+
+// Normalises the lane's row of O by 1 / (the sum of its two half-waves) and
+// stores the wave's 32 rows through `stg`, the wave's own staging area in
+// LDS.  The rows go in as the MFMA layout holds them (4 elements per lane
+// per block) and come out as 16-byte chunks of whole rows, so every store
+// instruction writes complete rows: a direct store from the MFMA layout
+// would write 8 bytes into each of 32 rows per instruction, and those
+// partial-line writes are what an output costs most.
 template <typename T, class C>
-__device__ __forceinline__ void finish_row(const PrefillArgs& a, const Column& col, float lrun,
-                                           const f32x16 (&acc)[C::DB], int h2) {
-  const float lsum = halves_sum(lrun);
-  if (col.valid) store_out_row<T, C>(reinterpret_cast<T*>(a.o) + col.row_off, acc, 1.0f / lsum, h2);
+__device__ __forceinline__ void finish_rows(const PrefillArgs& a, char* stg, float lrun,
+                                            const f32x16 (&acc)[C::DB], int b, int hkv, int hb,
+                                            int qb, int w) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 31;
+  const int h2 = lane >> 5;
+  constexpr int RB = C::D * C::ESZ + 16;  // staging row stride, bytes
+  const float inv = 1.0f / halves_sum(lrun);
+  char* row = stg + j * RB;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * db + 8 * q4 + 4 * h2;
+      const float x0 = acc[db][4 * q4 + 0] * inv;
+      const float x1 = acc[db][4 * q4 + 1] * inv;
+      const float x2 = acc[db][4 * q4 + 2] * inv;
+      const float x3 = acc[db][4 * q4 + 3] * inv;
+      if constexpr (C::F32) {
+        *reinterpret_cast<float4*>(row + d0 * 4) = float4{x0, x1, x2, x3};
+      } else {
+        *reinterpret_cast<u32x2*>(row + d0 * 2) = u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  constexpr int CPR = C::D * C::ESZ / 16;  // 16-byte chunks per row
+  constexpr int CPI = 64 / CPR;            // rows per store instruction
+  const int ch = lane % CPR;
+#pragma unroll
+  for (int k = 0; k < 32 / CPI; ++k) {
+    const int c = k * CPI + lane / CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + c * RB + ch * 16);
+    const Column cc = lane_column<C>(a, b, hkv, hb, qb, w, c);
+    if (cc.valid)
+      *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.o) + cc.row_off * C::ESZ + ch * 16) = v;
+  }
 }
 
 // Writes the wave's partial state to a record: the accumulator registers as
@@ -297,6 +343,7 @@ template <typename T, class C, bool CAUSAL>
 __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+  static_assert(C::NW * stage_out_bytes<C>() <= 2 * C::STAGE_BYTES, "output staging too large");
   __shared__ int s_unit;
   __shared__ int s_queue;
 
@@ -374,7 +421,9 @@ prefill_kernel(PrefillArgs a) {
     float mrun, lrun;
     f32x16 acc[C::DB];
     run_segment<T, C, CAUSAL>(a, smem, b, hkv, qb, 0, ntiles, rot, col, mrun, lrun, acc);
-    finish_row<T, C>(a, col, lrun, acc, h2);
+    // the ring is free (run_segment ends on a barrier); the next fetch
+    // starts with a barrier before any wave writes it again
+    finish_rows<T, C>(a, smem + w * stage_out_bytes<C>(), lrun, acc, b, hkv, hb, qb, w);
   }
 
   // Leave the counters at zero for the next launch: the last workgroup out
@@ -397,6 +446,7 @@ template <typename T, class C, bool CAUSAL>
 __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_balanced_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+  static_assert(C::NW * stage_out_bytes<C>() <= 2 * C::STAGE_BYTES, "output staging too large");
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -427,9 +477,10 @@ prefill_balanced_kernel(PrefillArgs a) {
     float mrun, lrun;
     f32x16 acc[C::DB];
     run_segment<T, C, CAUSAL>(a, smem, b, hkv, qb, t0, ntiles, rot, col, mrun, lrun, acc);
-    if (t0 == 0 && t1 == n)
-      finish_row<T, C>(a, col, lrun, acc, h2);
-    else if (a.ws)  // the host provides records whenever a chunk boundary cuts a unit
+    if (t0 == 0 && t1 == n) {
+      finish_rows<T, C>(a, smem + w * stage_out_bytes<C>(), lrun, acc, b, hkv, hb, qb, w);
+      __syncthreads();  // the staging area is ring memory again
+    } else if (a.ws)  // the host provides records whenever a chunk boundary cuts a unit
       write_record<C>(part_record<C>(a, g, seg == 0 ? 0 : 1), mrun, lrun, acc, w, lane);
     x = pre + t1;
     pre += n;
@@ -467,11 +518,15 @@ prefill_pair_kernel(PrefillArgs a) {
   const int hkv = kvg % a.Hkv;
   const int b = kvg / a.Hkv;
   char* ring = smem + half * 2 * C::STAGE_BYTES;
-  // hand-over area: DB*4 rows of NT float4 (the accumulator), then NT float2
-  // (m, l); 16-byte accesses, consecutive lanes on consecutive addresses
-  float4* hand4 = reinterpret_cast<float4*>(smem) + (w * 64 + lane);
-  float2* hand2 = reinterpret_cast<float2*>(reinterpret_cast<float4*>(smem) + C::DB * 4 * C::NT) +
-                  (w * 64 + lane);
+  // hand-over area: one block per wave slot w, DB*4 rows of 64 float4 (the
+  // accumulator) then 64 float2 (m, l); consecutive lanes on consecutive
+  // 16-byte addresses.  After the merge, wave w of the first half stages its
+  // output rows in the same block.
+  constexpr int HAND_BYTES = (C::DB * 16 + 2) * 64 * 4;
+  static_assert(HAND_BYTES >= stage_out_bytes<C>(), "output staging exceeds the hand-over block");
+  char* hand = smem + w * HAND_BYTES;
+  float4* hand4 = reinterpret_cast<float4*>(hand) + lane;
+  float2* hand2 = reinterpret_cast<float2*>(hand + C::DB * 4 * 64 * 16) + lane;
 
   for (int u = 0; u < 2; ++u) {
     const int qb = u == 0 ? a.NQB - 1 - p : p;
@@ -491,8 +546,8 @@ prefill_pair_kernel(PrefillArgs a) {
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
-          hand4[(db * 4 + r4) * C::NT] = make_float4(acc[db][4 * r4], acc[db][4 * r4 + 1],
-                                                     acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]);
+          hand4[(db * 4 + r4) * 64] = make_float4(acc[db][4 * r4], acc[db][4 * r4 + 1],
+                                                  acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]);
       *hand2 = make_float2(mrun, lrun);
     }
     __syncthreads();
@@ -505,13 +560,13 @@ prefill_pair_kernel(PrefillArgs a) {
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const float4 o1 = hand4[(db * 4 + r4) * C::NT];
+          const float4 o1 = hand4[(db * 4 + r4) * 64];
           acc[db][4 * r4] = w0 * acc[db][4 * r4] + w1 * o1.x;
           acc[db][4 * r4 + 1] = w0 * acc[db][4 * r4 + 1] + w1 * o1.y;
           acc[db][4 * r4 + 2] = w0 * acc[db][4 * r4 + 2] + w1 * o1.z;
           acc[db][4 * r4 + 3] = w0 * acc[db][4 * r4 + 3] + w1 * o1.w;
         }
-      finish_row<T, C>(a, col, w0 * lrun + w1 * ml1.y, acc, h2);
+      finish_rows<T, C>(a, hand, w0 * lrun + w1 * ml1.y, acc, b, hkv, hb, qb, w);
     }
     __syncthreads();  // the hand-over area is ring memory again
   }
