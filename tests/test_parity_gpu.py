@@ -304,3 +304,43 @@ def test_pair_schedule_sampled(s):
                      scale=s.scale)
     torch.cuda.synchronize()
     assert torch.equal(again.cpu(), out)
+
+
+# ---------------------------------------------------------------- random shapes
+# Seeded random shapes against the oracle: small ones in full; larger ones
+# (sampled rows) sized so the persistent (many units), pair (causal, at least
+# one unit pair per CU) and balanced (few units) schedules all run.
+
+def _random_shapes():
+    rng = np.random.default_rng(2024)
+    shapes = []
+    for _ in range(24):
+        hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.choice([1, 2, 3, 4, 8]))
+        d = int(rng.choice([32, 64, 128]))
+        nq = int(rng.integers(1, 300))
+        nk = int(rng.integers(1, 400))
+        causal = bool(rng.random() < 0.6)
+        off = int(rng.integers(0, nk)) if causal else 0
+        dt = torch.float32 if rng.random() < 0.3 else torch.bfloat16
+        shapes.append((FwdShape(int(rng.integers(1, 4)), hkv * g, hkv, nq, nk, d, causal, off, dt),
+                       None))
+    # many units: persistent schedule
+    shapes.append((FwdShape(2, 32, 8, 2100, 2100, 128, True, 0), 256))
+    shapes.append((FwdShape(6, 24, 4, 1500, 1700, 64, False, 0), 256))
+    shapes.append((FwdShape(4, 40, 8, 1100, 1300, 128, True, 200, torch.float32), 256))
+    # causal, one pair per CU or more: pair schedule
+    shapes.append((FwdShape(1, 48, 12, 2000, 2000, 128, True, 0), 256))
+    shapes.append((FwdShape(2, 40, 8, 1100, 1300, 128, True, 200, torch.float32), 256))
+    # few units, cut chunks: balanced schedule
+    shapes.append((FwdShape(4, 8, 2, 1900, 2500, 64, True, 600), 256))
+    return shapes
+
+
+RANDOM_SHAPES = _random_shapes()
+
+
+@pytest.mark.parametrize("idx", range(len(RANDOM_SHAPES)))
+def test_random_shapes(idx):
+    s, rows = RANDOM_SHAPES[idx]
+    _check_fwd(s, 300 + idx, rows=rows)
