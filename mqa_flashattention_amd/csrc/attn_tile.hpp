@@ -145,27 +145,51 @@ struct TileRegs {
   u32x4 v[C::V_LOADS];
 };
 
-// Issue the global loads of one K/V tile -- keys key0 .. key0+BC-1 of one
-// head whose rows start at kbase / vbase -- into registers.  A row at or
-// beyond nkeys re-reads row nkeys-1: always valid memory with finite values,
-// and the caller masks those keys, so their weight is exactly 0 and the
-// duplicate never reaches the result.  (No per-row branch or zero-fill.)
-// For K, consecutive threads take consecutive 16-byte chunks of a row, so a
-// wave's load instruction covers whole rows.
+// p, declared wave-uniform (readfirstlane of both halves), so that values
+// derived from it stay in scalar registers -- in particular the buffer
+// resources below, which must be scalar.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+
+// A raw buffer resource over `bytes` bytes at p.  Buffer loads at offsets at
+// or beyond `bytes` return zeros without touching memory.  Stride 0; the
+// third-dword value sets the 32-bit data-format field, which untyped buffer
+// loads on this architecture need to be non-zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Issue the loads of one K/V tile -- keys key0 .. key0+BC-1 of one head
+// whose rows start at kbase / vbase -- into registers, as 16-byte buffer
+// loads through a resource that starts at row key0 and covers the rows below
+// nkeys (at most one tile).  Rows at or beyond nkeys read as zeros; the
+// caller masks those keys, so their weight is exactly 0.  The per-lane byte
+// offsets do not depend on the tile, so the loop computes them once; the
+// tile start is scalar work.  For K, consecutive threads take consecutive
+// 16-byte chunks of a row, so a wave's load instruction covers whole rows.
 template <typename T, class C>
 __device__ __forceinline__ void load_tile(TileRegs<C>& r, const T* __restrict__ kbase,
                                           const T* __restrict__ vbase, int key0, int nkeys,
                                           int tid) {
-  const int last = nkeys - 1;
+  constexpr int ROWB = C::D * C::ESZ;  // bytes per row
+  const int rows = nkeys - key0 < C::BC ? (nkeys - key0 > 0 ? nkeys - key0 : 0) : C::BC;
+  const size_t base = (size_t)key0 * C::D;
+  const auto krs = buffer_rsrc(kbase + base, (uint32_t)(rows * ROWB));
+  const auto vrs = buffer_rsrc(vbase + base, (uint32_t)(rows * ROWB));
 #pragma unroll
   for (int n = 0; n < C::K_PER_T; ++n) {
     const int id = tid + n * C::NT;
     if (C::K_CHUNKS % C::NT == 0 || id < C::K_CHUNKS) {
       const int row = id / C::ROW_CHUNKS;
       const int col = id % C::ROW_CHUNKS;
-      const size_t off = (size_t)min(key0 + row, last) * C::D + col * C::EPC;
-      r.k[n] = *reinterpret_cast<const u32x4*>(kbase + off);
-      if constexpr (C::F32) r.v[n] = *reinterpret_cast<const u32x4*>(vbase + off);
+      const int off = row * ROWB + col * 16;
+      r.k[n] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+      if constexpr (C::F32) r.v[n] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
     }
   }
   if constexpr (!C::F32) {
@@ -176,11 +200,9 @@ __device__ __forceinline__ void load_tile(TileRegs<C>& r, const T* __restrict__ 
         const int kg = id % C::KGROUPS;
         const int dc = id / C::KGROUPS;
 #pragma unroll
-        for (int e = 0; e < C::VK; ++e) {
-          const int key = min(key0 + kg * C::VK + e, last);
+        for (int e = 0; e < C::VK; ++e)
           r.v[n * C::VK + e] =
-              *reinterpret_cast<const u32x4*>(vbase + (size_t)key * C::D + dc * 8);
-        }
+              __builtin_amdgcn_raw_buffer_load_b128(vrs, (kg * C::VK + e) * ROWB + dc * 16, 0, 0);
       }
     }
   }
@@ -414,14 +436,15 @@ __device__ __forceinline__ void pv_tile(f32x16 (&acc)[C::DB],
 }
 
 // One online-softmax + PV step on a (masked) score tile s:
-//   if rowmax s exceeds the reference m by more than 2^kRescaleSlack in some
-//   lane: m' = max(m, rowmax s), l and acc scaled by 2^((m - m') c);
+//   if rowmax s exceeds m + thr in some lane (thr = kRescaleSlack / c, from
+//   the host): m' = max(m, rowmax s), l and acc scaled by 2^((m - m') c);
 //   p = 2^(s c - m c); l += sum p; acc += V^T P^T.
-// The reference is raised only when needed (a wave-uniform branch; the first
-// tile with a visible key always raises it from -inf).  Between raises the
-// weights are taken against a reference up to kRescaleSlack/c below the true
-// running max, so they stay below 2^kRescaleSlack -- far inside fp32 and
-// bf16 range -- and acc / l is unchanged in exact arithmetic.
+// The reference is raised only when needed (a wave-uniform branch; for
+// m = -inf the bound m + thr is -inf, so the first tile with a visible key
+// always raises it).  Between raises the weights are taken against a
+// reference up to thr below the true running max, so they stay below
+// 2^kRescaleSlack -- far inside fp32 and bf16 range -- and acc / l is
+// unchanged in exact arithmetic.
 constexpr float kRescaleSlack = 16.0f;
 
 // The softmax half of the step: raises the reference if needed and leaves
@@ -429,19 +452,19 @@ constexpr float kRescaleSlack = 16.0f;
 template <class C>
 __device__ __forceinline__ void softmax_step(const f32x16 (&s)[C::KB], float& m, float& l,
                                              f32x16 (&acc)[C::DB],
-                                             typename C::Frag (&pf)[C::KB][C::PF], float c) {
+                                             typename C::Frag (&pf)[C::KB][C::PF], float c,
+                                             float thr) {
   const float mt = tile_rowmax<C>(s);
-  if (__any(m == kNegInf ? mt != kNegInf : (mt - m) * c > kRescaleSlack))
-    raise_reference<C>(m, l, acc, mt, c);
+  if (__any(mt > m + thr)) raise_reference<C>(m, l, acc, mt, c);
   l += tile_weights<C>(s, m, c, pf);
 }
 
 template <typename T, class C>
 __device__ __forceinline__ void softmax_pv_step(f32x16 (&s)[C::KB], float& m, float& l,
                                                 f32x16 (&acc)[C::DB], const T* __restrict__ Vs,
-                                                int lane32, int h2, float c) {
+                                                int lane32, int h2, float c, float thr) {
   typename C::Frag pf[C::KB][C::PF];
-  softmax_step<C>(s, m, l, acc, pf, c);
+  softmax_step<C>(s, m, l, acc, pf, c, thr);
   pv_tile<T, C>(acc, pf, Vs, lane32, h2);
 }
 

@@ -35,6 +35,7 @@ struct DecodeArgs {
   int S_TOK;  // tokens per split (multiple of 32)
   int NS;     // splits per row, ceil(Smax / S_TOK)
   float c;    // |scale| * log2(e)
+  float thr;  // kRescaleSlack / c
   int negate_q;
 };
 
@@ -73,8 +74,8 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
                     a.negate_q != 0, h2);
 
   const size_t head_off = (((size_t)b * a.Hkv + hkv) * a.Smax + start) * C::D;
-  const T* kbase = reinterpret_cast<const T*>(a.kc) + head_off;
-  const T* vbase = reinterpret_cast<const T*>(a.vc) + head_off;
+  const T* kbase = uniform_ptr(reinterpret_cast<const T*>(a.kc) + head_off);
+  const T* vbase = uniform_ptr(reinterpret_cast<const T*>(a.vc) + head_off);
 
   float mrun = kNegInf, lrun = 0.f;
   f32x16 acc[C::DB];
@@ -98,7 +99,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
     qk_tile<T, C>(s, qf, Ks, j, h2);
     const int key0 = kt * 32;
     if (key0 + 32 > ntok) mask_tile<C>(s, key0, ntok - 1, h2);
-    softmax_pv_step<T, C>(s, mrun, lrun, acc, Vs, j, h2, a.c);
+    softmax_pv_step<T, C>(s, mrun, lrun, acc, Vs, j, h2, a.c, a.thr);
     __syncthreads();
   };
   for (int kt = 0; kt < ntiles; kt += 2) {

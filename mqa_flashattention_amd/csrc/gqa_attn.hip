@@ -466,6 +466,7 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, in
   a.T = (int)T;
   a.q_offset = causal ? q_offset : 0;
   a.c = softmax_coef(scale);
+  a.thr = gqa::kRescaleSlack / a.c;
   a.negate_q = scale < 0.f ? 1 : 0;
   if (dtype == GQA_DTYPE_BF16)
     return dispatch_prefill<uint16_t, CfgBf16>(a, d, causal, dev, info, hs);
@@ -524,6 +525,7 @@ int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
   a.S_TOK = decode_split_tokens(B, Hkv, a.NCB, Smax, info.cus);
   a.NS = (Smax + a.S_TOK - 1) / a.S_TOK;
   a.c = softmax_coef(scale);
+  a.thr = gqa::kRescaleSlack / a.c;
   a.negate_q = scale < 0.f ? 1 : 0;
   if ((long long)a.Hkv * a.NCB > 65535 || B > 65535)
     return fail(GQA_ERR_BAD_SHAPE, "grid too large (B=%d, Hkv*blocks=%d)", B, a.Hkv * a.NCB);

@@ -59,7 +59,8 @@ struct PrefillArgs {
   int NQB;  // position blocks, ceil(Nq / R)
   int T;    // units, B * Hkv * HB * NQB
   int q_offset;
-  float c;  // |scale| * log2(e)
+  float c;    // |scale| * log2(e)
+  float thr;  // kRescaleSlack / c: how far a tile max may exceed the reference
   int negate_q;
   // balanced schedule: slices, chunks per slice, key tiles per slice, and
   // two partial records per workgroup (first and last segment)
@@ -149,8 +150,8 @@ __device__ __forceinline__ void locate_tile(const PrefillArgs& a, int X, int lan
     pre += n;
     ++pos;
   }
-  pos_out = pos;
-  pre_out = pre;
+  pos_out = __builtin_amdgcn_readfirstlane(pos);  // the same in every lane
+  pre_out = __builtin_amdgcn_readfirstlane(pre);
 }
 
 // Partial record `slot` (0: first segment, 1: last segment) of workgroup g
@@ -222,8 +223,8 @@ __device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, in
 
   const T* __restrict__ Q = reinterpret_cast<const T*>(a.q);
   const size_t kv_off = ((size_t)b * a.Hkv + hkv) * a.Nk * C::D;
-  const T* kbase = reinterpret_cast<const T*>(a.k) + kv_off;
-  const T* vbase = reinterpret_cast<const T*>(a.v) + kv_off;
+  const T* kbase = uniform_ptr(reinterpret_cast<const T*>(a.k) + kv_off);
+  const T* vbase = uniform_ptr(reinterpret_cast<const T*>(a.v) + kv_off);
 
   typename C::Frag qf[C::QF];
   load_q_frag<T, C>(qf, Q + col.row_off, col.valid, a.negate_q != 0, h2);
@@ -258,7 +259,7 @@ __device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, in
       qk_tile<T, C>(s, qf, stK(cur), j, h2);
       const int key0 = tile_at(kt) * C::BC;
       if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
-      softmax_pv_step<T, C>(s, mrun, lrun, acc, stV(cur), j, h2, a.c);
+      softmax_pv_step<T, C>(s, mrun, lrun, acc, stV(cur), j, h2, a.c, a.thr);
     }
     store_tile<T, C>(next, stK(cur ^ 1), stV(cur ^ 1), tid);
     __syncthreads();
@@ -392,8 +393,9 @@ prefill_kernel(PrefillArgs a) {
       }
     }
     __syncthreads();
-    const int t = s_unit;
-    const int q = s_queue;
+    // workgroup-uniform; readfirstlane keeps what derives from them scalar
+    const int t = __builtin_amdgcn_readfirstlane(s_unit);
+    const int q = __builtin_amdgcn_readfirstlane(s_queue);
     if (t < 0) break;
 
     // ---- (queue, index) -> (b, hkv, hb, qb)
@@ -504,8 +506,9 @@ prefill_pair_kernel(PrefillArgs a) {
   static_assert(4 * C::STAGE_BYTES >= C::NT * (C::DB * 16 + 2) * 4, "hand-over area too small");
 
   const int tid = threadIdx.x;
-  const int half = tid / C::NT;
-  const int w = (tid % C::NT) >> 6;
+  // wave-uniform; readfirstlane keeps what derives from them scalar
+  const int half = __builtin_amdgcn_readfirstlane(tid / C::NT);
+  const int w = __builtin_amdgcn_readfirstlane((tid % C::NT) >> 6);
   const int lane = tid & 63;
   const int j = lane & 31;
   const int h2 = lane >> 5;
