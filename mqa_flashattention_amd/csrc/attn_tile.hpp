@@ -55,12 +55,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Low / high 16-bit halves of two words, packed (a's half first).
+// Low / high 16-bit halves of two words, packed (a's half first): one
+// v_perm_b32 each, whose selector picks bytes of {b, a} (a = bytes 0..3).
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
 }
 __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
