@@ -184,11 +184,61 @@ __device__ __forceinline__ Column lane_column(const PrefillArgs& a, int b, int h
   return c;
 }
 
-// Runs key tiles [tile0, tile0 + ntiles) of unit (b, hkv, hb, qb) for the
-// lane's column col: loads the Q fragment, streams the tiles through the LDS
-// ring and leaves the running state (reference m, per-lane sum l and
-// unnormalised O) in mrun, lrun, acc.  All threads of the workgroup call it
-// together; it ends on a barrier, so the LDS ring is free on return.
+// What a segment needs before its first step, in registers: the Q fragment
+// and the loads of its first two tiles.  Issuing them early (seg_begin) and
+// running the segment later (seg_run) lets a caller hide their latency
+// behind other work.
+template <class C>
+struct SegIn {
+  typename C::Frag qf[C::QF];
+  TileRegs<C> ra, rb;
+};
+
+// The tiles of a segment: [tile0, tile0 + ntiles) walked from rotation rot;
+// positions past the end repeat the last one.  An empty range (possible for
+// a paired half) always yields tile0, which must be a valid tile.
+struct SegTiles {
+  int tile0, ntiles, rot;
+  __device__ __forceinline__ int at(int pos) const {
+    if (ntiles == 0) return tile0;
+    const int x = (pos < ntiles ? pos : ntiles - 1) + rot;
+    return tile0 + (x >= ntiles ? x - ntiles : x);
+  }
+};
+
+template <typename T, class C>
+__device__ __forceinline__ void kv_bases(const PrefillArgs& a, int b, int hkv, const T*& kbase,
+                                         const T*& vbase) {
+  const size_t kv_off = ((size_t)b * a.Hkv + hkv) * a.Nk * C::D;
+  kbase = uniform_ptr(reinterpret_cast<const T*>(a.k) + kv_off);
+  vbase = uniform_ptr(reinterpret_cast<const T*>(a.v) + kv_off);
+}
+
+template <typename T, class C>
+__device__ __forceinline__ void seg_begin(const PrefillArgs& a, SegIn<C>& in, int b, int hkv,
+                                          const SegTiles& st, const Column& col) {
+  const int tid = threadIdx.x % C::NT;  // index within the loading group
+  const int h2 = (tid & 63) >> 5;
+  const T* kbase;
+  const T* vbase;
+  kv_bases<T, C>(a, b, hkv, kbase, vbase);
+  load_q_frag<T, C>(in.qf, reinterpret_cast<const T*>(a.q) + col.row_off, col.valid,
+                    a.negate_q != 0, h2);
+  load_tile<T, C>(in.ra, kbase, vbase, st.at(0) * C::BC, a.Nk, tid);
+  load_tile<T, C>(in.rb, kbase, vbase, st.at(1) * C::BC, a.Nk, tid);
+}
+
+// Runs key tiles st of unit (b, hkv, ., qb) for the lane's column col, from
+// the registers seg_begin filled, and leaves the running state (reference
+// m, per-lane sum l and unnormalised O) in mrun, lrun, acc.  All threads of
+// the workgroup call it together; it ends on a barrier, so the LDS ring is
+// free on return.
+//
+// PAIRED: two groups of NW waves (one per half of the workgroup) run the
+// function together on their own LDS rings, each over its own tile range;
+// both loop `steps` times (the longer range) so that they meet at every
+// barrier, and a group whose range is shorter skips the compute of its last
+// steps.
 //
 // Two LDS stages and two register staging sets: the global loads of tile
 // t+2 are issued at the start of tile t and written to LDS at the end of
@@ -203,31 +253,20 @@ __device__ __forceinline__ Column lane_column(const PrefillArgs& a, int b, int h
 // same moment.  The order of tiles does not change the result in exact
 // arithmetic (masking is per key, and a lane whose first tiles are all
 // masked keeps an empty state until a visible key comes).
-//
-// PAIRED: two groups of NW waves (one per half of the workgroup) run the
-// function together on their own LDS rings, each over its own tile range;
-// both loop `steps` times (the longer range) so that they meet at every
-// barrier, and a group whose range is shorter (possibly empty: then tile0
-// must still be a valid tile) skips the compute of its last steps.
 template <typename T, class C, bool CAUSAL, bool PAIRED = false>
-__device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, int b, int hkv,
-                                            int qb, int tile0, int ntiles, int rot,
-                                            const Column& col, float& mrun, float& lrun,
-                                            f32x16 (&acc)[C::DB], int steps = 0) {
+__device__ __forceinline__ void seg_run(const PrefillArgs& a, char* smem, SegIn<C>& in, int b,
+                                        int hkv, int qb, const SegTiles& st, const Column& col,
+                                        float& mrun, float& lrun, f32x16 (&acc)[C::DB],
+                                        int steps) {
   const int tid = threadIdx.x % C::NT;  // index within the loading group
   const int lane = tid & 63;
   const int j = lane & 31;
   const int h2 = lane >> 5;
-  auto stK = [&](int st) { return reinterpret_cast<T*>(smem + st * C::STAGE_BYTES); };
-  auto stV = [&](int st) { return stK(st) + C::K_ELEMS; };
-
-  const T* __restrict__ Q = reinterpret_cast<const T*>(a.q);
-  const size_t kv_off = ((size_t)b * a.Hkv + hkv) * a.Nk * C::D;
-  const T* kbase = uniform_ptr(reinterpret_cast<const T*>(a.k) + kv_off);
-  const T* vbase = uniform_ptr(reinterpret_cast<const T*>(a.v) + kv_off);
-
-  typename C::Frag qf[C::QF];
-  load_q_frag<T, C>(qf, Q + col.row_off, col.valid, a.negate_q != 0, h2);
+  auto stK = [&](int sg) { return reinterpret_cast<T*>(smem + sg * C::STAGE_BYTES); };
+  auto stV = [&](int sg) { return stK(sg) + C::K_ELEMS; };
+  const T* kbase;
+  const T* vbase;
+  kv_bases<T, C>(a, b, hkv, kbase, vbase);
 
   // keys below full_lim are visible to every column of the unit; lim is the
   // last key this lane's query may see
@@ -239,25 +278,17 @@ __device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, in
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
-  auto tile_at = [&](int pos) {
-    if (PAIRED && ntiles == 0) return tile0;
-    const int x = (pos < ntiles ? pos : ntiles - 1) + rot;
-    return tile0 + (x >= ntiles ? x - ntiles : x);
-  };
-  if (!PAIRED) steps = ntiles;
-  TileRegs<C> ra, rb;
-  load_tile<T, C>(ra, kbase, vbase, tile_at(0) * C::BC, a.Nk, tid);
-  load_tile<T, C>(rb, kbase, vbase, tile_at(1) * C::BC, a.Nk, tid);
-  store_tile<T, C>(ra, stK(0), stV(0), tid);
+  if (!PAIRED) steps = st.ntiles;
+  store_tile<T, C>(in.ra, stK(0), stV(0), tid);
   __syncthreads();
 
   auto step = [&](TileRegs<C>& mine, TileRegs<C>& next, int kt) {
     const int cur = kt & 1;
-    load_tile<T, C>(mine, kbase, vbase, tile_at(kt + 2) * C::BC, a.Nk, tid);
-    if (!PAIRED || kt < ntiles) {
+    load_tile<T, C>(mine, kbase, vbase, st.at(kt + 2) * C::BC, a.Nk, tid);
+    if (!PAIRED || kt < st.ntiles) {
       f32x16 s[C::KB];
-      qk_tile<T, C>(s, qf, stK(cur), j, h2);
-      const int key0 = tile_at(kt) * C::BC;
+      qk_tile<T, C>(s, in.qf, stK(cur), j, h2);
+      const int key0 = st.at(kt) * C::BC;
       if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
       softmax_pv_step<T, C>(s, mrun, lrun, acc, stV(cur), j, h2, a.c, a.thr);
     }
@@ -265,9 +296,21 @@ __device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, in
     __syncthreads();
   };
   for (int kt = 0; kt < steps; kt += 2) {
-    step(ra, rb, kt);
-    if (kt + 1 < steps) step(rb, ra, kt + 1);
+    step(in.ra, in.rb, kt);
+    if (kt + 1 < steps) step(in.rb, in.ra, kt + 1);
   }
+}
+
+// seg_begin + seg_run back to back.
+template <typename T, class C, bool CAUSAL>
+__device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, int b, int hkv,
+                                            int qb, int tile0, int ntiles, int rot,
+                                            const Column& col, float& mrun, float& lrun,
+                                            f32x16 (&acc)[C::DB]) {
+  SegIn<C> in;
+  const SegTiles st{tile0, ntiles, rot};
+  seg_begin<T, C>(a, in, b, hkv, st, col);
+  seg_run<T, C, CAUSAL>(a, smem, in, b, hkv, qb, st, col, mrun, lrun, acc, ntiles);
 }
 
 // Bytes of one wave's output staging area: its 32 rows of O with a
@@ -531,19 +574,35 @@ prefill_pair_kernel(PrefillArgs a) {
   float4* hand4 = reinterpret_cast<float4*>(hand) + lane;
   float2* hand2 = reinterpret_cast<float2*>(hand + C::DB * 4 * 64 * 16) + lane;
 
-  for (int u = 0; u < 2; ++u) {
-    const int qb = u == 0 ? a.NQB - 1 - p : p;
-    if (u == 1 && qb >= a.NQB - 1 - p) break;  // middle unit of an odd NQB: done once
-    const int n = unit_tiles<C, CAUSAL>(a, qb);
-    const int n0 = (n + 1) / 2;
+  // unit u of the pair (u = 1 absent for the middle unit of an odd NQB)
+  const int nunits = (a.NQB - 1 - p) > p ? 2 : 1;
+  auto unit_qb = [&](int u) { return u == 0 ? a.NQB - 1 - p : p; };
+  auto unit_seg = [&](int u, int& n0) {
+    const int n = unit_tiles<C, CAUSAL>(a, unit_qb(u));
+    n0 = (n + 1) / 2;
     const int nt = half ? n - n0 : n0;
     const int rot = nt > 0 ? (int)((7u * (unsigned)g + 3u * (unsigned)u) % (unsigned)nt) : 0;
-    const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
+    return SegTiles{half ? min(n0, n - 1) : 0, nt, rot};
+  };
+
+  SegIn<C> in;
+  int n0;
+  SegTiles st = unit_seg(0, n0);
+  Column col = lane_column<C>(a, b, hkv, hb, unit_qb(0), w, j);
+  seg_begin<T, C>(a, in, b, hkv, st, col);
+  for (int u = 0; u < nunits; ++u) {
+    const int qb = unit_qb(u);
     float mrun, lrun;
     f32x16 acc[C::DB];
-    run_segment<T, C, CAUSAL, true>(a, ring, b, hkv, qb, half ? min(n0, n - 1) : 0, nt, rot, col,
-                                    mrun, lrun, acc, n0);
-    // hand-over: the rings are free (run_segment ends on a barrier)
+    seg_run<T, C, CAUSAL, true>(a, ring, in, b, hkv, qb, st, col, mrun, lrun, acc, n0);
+    if (u + 1 < nunits) {
+      // issue the next unit's Q fragment and first tiles now: their latency
+      // hides behind this unit's hand-over
+      st = unit_seg(u + 1, n0);
+      col = lane_column<C>(a, b, hkv, hb, unit_qb(u + 1), w, j);
+      seg_begin<T, C>(a, in, b, hkv, st, col);
+    }
+    // hand-over: the rings are free (seg_run ends on a barrier)
     if (half) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
