@@ -314,14 +314,22 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const typename C::Fr
   for (int kb = 0; kb < C::KB; ++kb) {
     f32x16 a = {};
     const T* krow = Ks + (32 * kb + k_row_perm(lane32)) * C::KSTR;
+    if constexpr (C::F32) {
 #pragma unroll
-    for (int ks = 0; ks < C::QF; ++ks) {
-      if constexpr (C::F32) {
+      for (int ks = 0; ks < C::QF; ++ks)
         a = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[2 * ks + h2], qf[ks], a, 0, 0, 0);
-      } else {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * ks + 8 * h2);
-        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], a, 0, 0, 0);
-      }
+    } else {
+      // all K fragments are requested before the first MFMA (the scheduling
+      // barrier keeps them there), so the LDS latency is paid once per block
+      // instead of once per pair of MFMAs
+      bf16x8 kf[C::QF];
+#pragma unroll
+      for (int ks = 0; ks < C::QF; ++ks)
+        kf[ks] = *reinterpret_cast<const bf16x8*>(krow + 16 * ks + 8 * h2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < C::QF; ++ks)
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], a, 0, 0, 0);
     }
     s[kb] = a;
   }
