@@ -14,7 +14,11 @@ fp32 values are exactly representable in fp64).
 What it computes, with its sources, is written at the top of ``attn_oracle.c``:
 the definition O = softmax(scale * Q K^T [causal, q_offset]) V with query head
 h reading K/V head h // (Hq // Hkv) (BootstrapAI evolution log, "Kernel 9 --
-GQA Flash Attention"), evaluated as max / exp-sum / weighted sum per row.
+GQA Flash Attention"), evaluated as max / exp-sum / weighted sum per row.  The decode step with
+append first writes each active row's new K/V rows at its position (the
+single-launch K/V store and per-row position table of the microLLM-rocm
+optimization log, experiments 025, 083/084 and 098) and then attends slots
+[0, position].
 
 Parity status: pinned (see tests/test_oracle.py -- library attention routine
 on random shapes, closed forms, invariants, and planted-mistake checks).
@@ -71,8 +75,11 @@ def load(path: str = LIBRARY, build_if_missing: bool = True) -> ctypes.CDLL:
                                           _lp, _lp, _lp, _dp]
         lib.oracle_attn_decode.argtypes = [_dp, _dp, _dp, ctypes.POINTER(ctypes.c_int32),
                                            _dp, _lp, _lp, _lp, _lp, _lp, ctypes.c_double]
+        lib.oracle_attn_decode_append.argtypes = [_dp, _dp, _dp, _dp, _dp,
+                                                  ctypes.POINTER(ctypes.c_int32), _dp,
+                                                  _lp, _lp, _lp, _lp, _lp, ctypes.c_double]
         for name in ("oracle_attn_fwd", "oracle_attn_fwd_rows", "oracle_attn_probs",
-                     "oracle_attn_decode", "oracle_num_threads"):
+                     "oracle_attn_decode", "oracle_attn_decode_append", "oracle_num_threads"):
             getattr(lib, name).restype = ctypes.c_int
         _libs[path] = lib
         return lib
@@ -160,6 +167,35 @@ def attn_decode(q, kcache, vcache, seqlens, *, scale: float | None = None,
                                   sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _ptr(o),
                                   B, Hq, Hkv, Smax, d, float(scale)), "attn_decode")
     return o
+
+
+def attn_decode_append(q, k_new, v_new, kcache, vcache, positions, *,
+                       scale: float | None = None, lib: ctypes.CDLL | None = None):
+    """Decode step with append: returns (O[B,Hq,d], K cache, V cache) as float64.
+
+    q[B,Hq,d], k_new/v_new[B,Hkv,d], caches [B,Hkv,Smax,d], positions int[B].
+    Row b with 0 <= positions[b] < Smax writes its new K/V rows into slot
+    positions[b] and attends slots [0, positions[b]]; other rows are inactive
+    (no write, zero output).  The input caches are not modified: the updated
+    caches are returned as new arrays."""
+    lib = lib or load()
+    q, kn, vn = _f64(q), _f64(k_new), _f64(v_new)
+    kc, vc = _f64(kcache).copy(), _f64(vcache).copy()
+    if hasattr(positions, "detach"):
+        positions = positions.detach().to("cpu").numpy()
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    B, Hq, d = q.shape
+    Hkv, Smax = kc.shape[1], kc.shape[2]
+    if kn.shape != (B, Hkv, d) or vn.shape != (B, Hkv, d) or pos.shape != (B,):
+        raise ValueError("attn_decode_append: k_new/v_new must be [B,Hkv,d], positions [B]")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty_like(q)
+    _check(lib.oracle_attn_decode_append(_ptr(q), _ptr(kn), _ptr(vn), _ptr(kc), _ptr(vc),
+                                         pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                         _ptr(o), B, Hq, Hkv, Smax, d, float(scale)),
+           "attn_decode_append")
+    return o, kc, vc
 
 
 def num_threads(lib: ctypes.CDLL | None = None) -> int:

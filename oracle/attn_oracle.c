@@ -39,6 +39,11 @@
  *   n == 0 gives an all-zero output row (documented reading; the pages are
  *   silent on empty caches).
  *
+ *   Decode with append (oracle_attn_decode_append): the new token's K/V rows
+ *   are first written to cache slot pos = positions[b] of each K/V head,
+ *   then the row attends slots [0, pos]; rows with pos outside [0, Smax) are
+ *   inactive (no write, zero output).  Sources at that function.
+ *
  * Inputs are the exact values the GPU consumes, widened to double by the
  * caller (fp32 as is, bf16 by appending 16 zero bits).  Layout is contiguous
  * row-major: q,o [B,Hq,Nq,d]; k,v [B,Hkv,Nk,d]; caches [B,Hkv,Smax,d].
@@ -255,6 +260,51 @@ int oracle_attn_decode(const double* q, const double* kc, const double* vc,
     }
   }
   return failed ? -2 : 0;
+}
+
+/*
+ * Decode step that first appends the new token's K/V at a per-row position.
+ *
+ * Sources: the microLLM-rocm optimization log, experiment 025 (the K and V
+ * cache stores of one position done together, in one launch) and the
+ * per-row position table of experiments 083/084 and 098 (rows at different
+ * positions decode in one batch, each through its own small metadata entry;
+ * an inactive row is skipped explicitly, experiment 097).
+ *
+ * Steps, in that order:
+ *   1. append: for every row b whose position pos = positions[b] lies in
+ *      [0, Smax), and every K/V head hk, cache slot pos of head hk takes the
+ *      new rows: kc[b,hk,pos,:] = k_new[b,hk,:], vc[b,hk,pos,:] = v_new[b,hk,:];
+ *   2. attend: each query head of row b attends slots [0, pos] -- the new
+ *      token included, so n = pos + 1 -- by the decode definition above.
+ * A row with pos < 0 or pos >= Smax is inactive (documented reading: the
+ * pages fix no behaviour at the capacity boundary): nothing is written and
+ * its output rows are zero.  kc and vc are updated in place.
+ */
+int oracle_attn_decode_append(const double* q, const double* knew, const double* vnew,
+                              double* kc, double* vc, const int32_t* positions, double* o,
+                              long B, long Hq, long Hkv, long Smax, long d, double scale) {
+  if (!q || !knew || !vnew || !kc || !vc || !positions || !o) return -1;
+  if (check_shapes(B, Hq, Hkv, 1, Smax, d)) return -1;
+  int32_t* lens = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);
+  if (!lens) return -2;
+  for (long b = 0; b < B; ++b) {
+    const long pos = positions[b];
+    const int active = pos >= 0 && pos < Smax;
+    lens[b] = active ? (int32_t)(pos + 1) : 0;
+    if (!active) continue;
+    for (long hk = 0; hk < Hkv; ++hk) {
+      const double* ksrc = knew + (b * Hkv + hk) * d;
+      const double* vsrc = vnew + (b * Hkv + hk) * d;
+      double* kdst = kc + ((b * Hkv + hk) * Smax + pos) * d;
+      double* vdst = vc + ((b * Hkv + hk) * Smax + pos) * d;
+      memcpy(kdst, ksrc, sizeof(double) * (size_t)d);
+      memcpy(vdst, vsrc, sizeof(double) * (size_t)d);
+    }
+  }
+  const int rc = oracle_attn_decode(q, kc, vc, lens, o, B, Hq, Hkv, Smax, d, scale);
+  free(lens);
+  return rc;
 }
 
 /* Number of OpenMP threads a parallel region would use (for reporting). */

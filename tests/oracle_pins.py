@@ -306,6 +306,74 @@ def pin_decode_semantics(lib):
     assert np.all(z[0] == 0) and np.all(z[1] == 0)
 
 
+def _append_case(seed, B, Hkv, g, Smax, d):
+    return (_rand((B, Hkv * g, d), seed), _rand((B, Hkv, d), seed + 1), _rand((B, Hkv, d), seed + 2),
+            _rand((B, Hkv, Smax, d), seed + 3), _rand((B, Hkv, Smax, d), seed + 4))
+
+
+def pin_append_library(lib):
+    """Decode with append vs the library routine: row b attends the first pos cache slots
+    followed by its new K/V row (n = pos + 1); the returned caches equal the inputs except
+    slot pos of each K/V head of an active row, which holds the new rows; rows with
+    pos < 0 or pos >= Smax are inactive (zero output, caches untouched)."""
+    rng = np.random.default_rng(91)
+    for t in range(8):
+        B = int(rng.integers(3, 6))
+        Hkv = int(rng.choice([1, 2, 3]))
+        g = int(rng.choice([1, 2, 6]))
+        Smax = int(rng.integers(2, 40))
+        d = int(rng.choice([8, 32]))
+        q, kn, vn, kc, vc = _append_case(900 + 10 * t, B, Hkv, g, Smax, d)
+        pos = rng.integers(0, Smax, size=B).astype(np.int32)
+        pos[0] = Smax - 1
+        pos[1] = -1 - int(rng.integers(0, 3))
+        pos[2] = Smax + int(rng.integers(0, 3))
+        scale = 1.0 / math.sqrt(d)
+        o, ko, vo = oracle.attn_decode_append(q, kn, vn, kc, vc, pos, scale=scale, lib=lib)
+        for b in range(B):
+            p = int(pos[b])
+            if p < 0 or p >= Smax:
+                assert np.all(o[b] == 0), f"case {t} row {b}: inactive row not zero"
+                assert np.array_equal(ko[b], kc[b]) and np.array_equal(vo[b], vc[b])
+                continue
+            kk = np.concatenate([kc[b, :, :p], kn[b, :, None, :]], axis=1)
+            vv = np.concatenate([vc[b, :, :p], vn[b, :, None, :]], axis=1)
+            ref = _sdpa(q[b:b + 1, :, None, :], kk[None], vv[None], False, 0, scale)[0, :, 0, :]
+            err = _maxerr(o[b], ref)
+            assert err <= TOL, f"case {t} row {b}: err {err}"
+            others = [j for j in range(Smax) if j != p]
+            assert np.array_equal(ko[b][:, others], kc[b][:, others])
+            assert np.array_equal(vo[b][:, others], vc[b][:, others])
+            assert np.array_equal(ko[b][:, p], kn[b]) and np.array_equal(vo[b][:, p], vn[b])
+
+
+def pin_append_first_slot(lib):
+    """pos = 0: the query sees only its own new key, whose softmax weight is exactly 1,
+    so every query head of K/V head hk returns v_new[b, hk] exactly."""
+    B, Hkv, g, Smax, d = 3, 2, 3, 9, 16
+    q, kn, vn, kc, vc = _append_case(171, B, Hkv, g, Smax, d)
+    o, _, _ = oracle.attn_decode_append(q, kn, vn, kc, vc, np.zeros(B, np.int32), lib=lib)
+    for h in range(Hkv * g):
+        assert np.array_equal(o[:, h], vn[:, h // g]), f"head {h}"
+
+
+def pin_append_equal_keys_mean(lib):
+    """Every visible key equal to the new key: all scores tie, the weights are uniform,
+    and the output is the mean of the pos cached V rows and the new V row."""
+    B, Hkv, g, Smax, d = 4, 2, 2, 13, 8
+    q, kn, vn, kc, vc = _append_case(181, B, Hkv, g, Smax, d)
+    pos = np.array([3, 12, 7, 1], dtype=np.int32)
+    for b in range(B):
+        kc[b, :, :pos[b]] = kn[b, :, None, :]
+    o, _, _ = oracle.attn_decode_append(q, kn, vn, kc, vc, pos, lib=lib)
+    for b in range(B):
+        p = int(pos[b])
+        for h in range(Hkv * g):
+            hk = h // g
+            ref = (vc[b, hk, :p].sum(axis=0) + vn[b, hk]) / (p + 1)
+            assert _maxerr(o[b, h], ref) <= 1e-12, f"row {b} head {h}"
+
+
 PINS = [
     pin_library_attention,
     pin_decode_library,
@@ -325,6 +393,9 @@ PINS = [
     pin_hardmax_limit,
     pin_rows_match_full,
     pin_decode_semantics,
+    pin_append_library,
+    pin_append_first_slot,
+    pin_append_equal_keys_mean,
 ]
 
 

@@ -126,6 +126,15 @@ MUTANTS = [
     ("decode clamp missing", "if (n > Smax) n = Smax;", "", 1),
     ("probabilities not normalised", "probs[j] = (j <= last) ? scores[j] / l : 0.0;",
      "probs[j] = (j <= last) ? scores[j] : 0.0;", 1),
+    ("append length excludes the new token", "lens[b] = active ? (int32_t)(pos + 1) : 0;",
+     "lens[b] = active ? (int32_t)pos : 0;", 1),
+    ("append slot off by one", "double* kdst = kc + ((b * Hkv + hk) * Smax + pos) * d;",
+     "double* kdst = kc + ((b * Hkv + hk) * Smax + pos - 1) * d;", 1),
+    ("new V not appended", "memcpy(vdst, vsrc, sizeof(double) * (size_t)d);", "", 1),
+    ("new K/V of head 0 for every head", "const double* ksrc = knew + (b * Hkv + hk) * d;",
+     "const double* ksrc = knew + b * Hkv * d;", 1),
+    ("capacity boundary not checked", "const int active = pos >= 0 && pos < Smax;",
+     "const int active = pos >= 0;", 1),
 ]
 
 
