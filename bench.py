@@ -72,6 +72,13 @@ def decode_bytes(s, lens) -> float:
     return kv + 2.0 * s.B * s.Hq * s.d * elem + 4.0 * s.B
 
 
+def append_bytes(s, positions) -> float:
+    """Decode bytes over positions + 1 slots, plus the new K/V rows read and stored."""
+    elem = 2 if str(s.dtype).endswith("bfloat16") else 4
+    lens = [int(p) + 1 for p in positions if 0 <= int(p) < s.Smax]
+    return decode_bytes(s, lens) + 4.0 * len(lens) * s.Hkv * s.d * elem
+
+
 def fwd_bytes(s) -> float:
     elem = 2 if str(s.dtype).endswith("bfloat16") else 4
     return elem * (2.0 * s.B * s.Hq * s.Nq * s.d + 2.0 * s.B * s.Hkv * s.Nk * s.d)
@@ -172,6 +179,53 @@ def time_fwd_workload(s, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def time_append_workload(s, steps, warmup):
+    """Event-timed average duration (ms) of one gqa_attn_decode_append call,
+    each call on a different one of DECODE_SETS cache pairs (HBM-cold), after
+    a parity check of the first call against the oracle (outputs and caches)."""
+    import numpy as np
+    import torch
+
+    import oracle  # test infrastructure: parity gate only
+    from mqa_flashattention_amd import attn_decode_append, decode_workspace_bytes
+    from mqa_flashattention_amd.workloads import append_inputs
+    dev = torch.device("cuda:0")
+    q_h, kn_h, vn_h, kc_h, vc_h, pos_h = append_inputs(s, 0)
+    q, kn, vn, pos = q_h.to(dev), kn_h.to(dev), vn_h.to(dev), pos_h.to(dev)
+    kcs, vcs = [kc_h.to(dev)], [vc_h.to(dev)]
+    gen = torch.Generator(device=dev).manual_seed(2)
+    for _ in range(DECODE_SETS - 1):
+        kcs.append(torch.randn(kc_h.shape, generator=gen, device=dev).to(s.dtype))
+        vcs.append(torch.randn(vc_h.shape, generator=gen, device=dev).to(s.dtype))
+    o = torch.empty_like(q)
+    ws = torch.empty(decode_workspace_bytes(s.B, s.Hq, s.Hkv, s.Smax, s.d), dtype=torch.uint8,
+                     device=dev)
+    attn_decode_append(q, kn, vn, kcs[0], vcs[0], pos, scale=s.scale, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    ref, kref, vref = oracle.attn_decode_append(q_h, kn_h, vn_h, kc_h, vc_h, pos_h, scale=s.scale)
+    check(o, ref, 2e-2, "decode_append")
+    if not (np.array_equal(kcs[0].cpu().double().numpy(), kref)
+            and np.array_equal(vcs[0].cpu().double().numpy(), vref)):
+        raise SystemExit("decode_append: updated caches differ from the oracle")
+    for i in range(warmup):
+        attn_decode_append(q, kn, vn, kcs[i % DECODE_SETS], vcs[i % DECODE_SETS], pos,
+                           scale=s.scale, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    # a short spin kernel ahead of the calls keeps the GPU behind the host, so
+    # every event pair brackets GPU work only (one call takes less GPU time
+    # than the host needs to issue it)
+    torch.cuda._sleep(50_000_000)
+    for i in range(steps):
+        ev[i][0].record()
+        attn_decode_append(q, kn, vn, kcs[(i + 1) % DECODE_SETS], vcs[(i + 1) % DECODE_SETS],
+                           pos, scale=s.scale, out=o, workspace=ws)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])), pos_h.tolist()
 
 
 def main(argv=None):
@@ -342,6 +396,14 @@ def main(argv=None):
                 tf = prefill_flops(s) / (ms * 1e-3) / 1e12
                 extra[f"{name}[Hkv={s.Hkv}]"] = {"ms": round(ms, 5), "tflops": round(tf, 2),
                                                  "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        sa = WORKLOADS["kv_decode_append_b8"].decode
+        ms, positions = time_append_workload(sa, max(20, K), 5)
+        gb = append_bytes(sa, positions) / (ms * 1e-3) / 1e9
+        extra["kv_decode_append_b8"] = {
+            "ms": round(ms, 5), "value": round(gb, 2), "unit": "GB/s",
+            "frac_hbm_peak": round(gb / PEAK_HBM_GBPS, 4),
+            "algorithmic_mb": round(append_bytes(sa, positions) / 1e6, 4),
+            "note": "store of the new K/V rows + split + combine, one call, HBM-cold caches"}
         result["other_workloads"] = extra
 
     print(json.dumps(result), flush=True)

@@ -115,6 +115,37 @@ int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
                     int B, int Hq, int Hkv, int Smax, int d, float scale,
                     int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode step that also appends the new token's K/V to the caches, in the
+ * same launch.
+ *
+ *   q, o            : [B, Hq, d]
+ *   k_new, v_new    : [B, Hkv, d]        the new token's key / value rows
+ *   kcache, vcache  : [B, Hkv, Smax, d]  read, and written at the positions
+ *   positions       : int32[B], device memory
+ *
+ * Row b with p = positions[b] in [0, Smax) stores k_new[b, hk, :] and
+ * v_new[b, hk, :] into cache slot p of every K/V head hk, and its query
+ * heads attend slots [0, p] -- the new token included.  Any other p marks
+ * the row inactive: nothing is stored and its output rows are zero.  Slots
+ * > p are never read.  The positions are neither checked on the host nor
+ * advanced: the caller moves each active row to p + 1 for the next step.
+ * This is the single-launch store of one position's K and V (microLLM-rocm
+ * optimization log, experiment 025) with a per-row position table, so rows
+ * at different positions decode in one batch (its experiments 083/084 and
+ * 098; inactive rows skipped explicitly as in experiment 097).  The
+ * attention itself is that of gqa_attn_decode with seqlens[b] = p + 1.
+ *
+ * k_new, v_new, kcache and vcache must not overlap.  Workspace, stream,
+ * status codes and error behaviour are those of gqa_attn_decode (same
+ * workspace size).  On an error return nothing has been launched and the
+ * caches are unchanged.
+ */
+int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new,
+                           void* kcache, void* vcache, const int32_t* positions, void* o,
+                           int B, int Hq, int Hkv, int Smax, int d, float scale,
+                           int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static English name of a status code (never NULL). */
 const char* gqa_status_string(int status);
 

@@ -5,11 +5,13 @@ C ABI, declared in ``include/gqa_attn.h``).  ``binding`` is a thin ctypes layer
 over it: argument checks and marshalling only, no compute and no fallback.
 
 Importing this package does not load the library; the first use of
-``attn_fwd`` / ``attn_decode`` does, and raises if it has not been built.
+``attn_fwd`` / ``attn_decode`` / ``attn_decode_append`` does, and raises if it
+has not been built.
 """
 from __future__ import annotations
 
-__all__ = ["attn_fwd", "attn_decode", "decode_workspace_bytes", "library_path", "GqaError"]
+__all__ = ["attn_fwd", "attn_decode", "attn_decode_append", "decode_workspace_bytes",
+           "library_path", "GqaError"]
 
 
 def __getattr__(name):

@@ -26,8 +26,8 @@ STATUS_NAMES = {
     0: "GQA_OK", 1: "GQA_ERR_NULL_POINTER", 2: "GQA_ERR_BAD_SHAPE", 3: "GQA_ERR_HEAD_GROUPING",
     4: "GQA_ERR_UNSUPPORTED", 5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_NO_DEVICE", 7: "GQA_ERR_HIP",
 }
-EXPORTED = ("gqa_attn_fwd", "gqa_attn_decode", "gqa_attn_decode_workspace_bytes",
-            "gqa_status_string", "gqa_last_error_string")
+EXPORTED = ("gqa_attn_fwd", "gqa_attn_decode", "gqa_attn_decode_append",
+            "gqa_attn_decode_workspace_bytes", "gqa_status_string", "gqa_last_error_string")
 
 
 class GqaError(RuntimeError):
@@ -49,6 +49,9 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_decode_workspace_bytes.restype = sz
     lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.gqa_attn_decode.restype = i
+    lib.gqa_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp,
+                                           sz, vp]
+    lib.gqa_attn_decode_append.restype = i
     lib.gqa_status_string.argtypes = [i]
     lib.gqa_status_string.restype = ctypes.c_char_p
     lib.gqa_last_error_string.argtypes = []
@@ -166,5 +169,58 @@ def attn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                                  float(scale), _DTYPES[q.dtype], workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(),
                                  _stream_handle(dev))
+    _raise(st)
+    return out
+
+
+def attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                       kcache: torch.Tensor, vcache: torch.Tensor, positions: torch.Tensor, *,
+                       scale: float | None = None, out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode step with append via gqa_attn_decode_append.
+
+    q [B, Hq, d]; k_new, v_new [B, Hkv, d]; kcache, vcache [B, Hkv, Smax, d]
+    (written in place); positions int32 [B] on the same GPU.  Row b with
+    p = positions[b] in [0, Smax) stores its new K/V rows in slot p and
+    attends slots [0, p]; other rows are inactive (zero output, no store).
+    The positions are not advanced."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _check_tensor("q", q, 3, q.dtype, dev)
+    _check_tensor("k_new", k_new, 3, q.dtype, dev)
+    _check_tensor("v_new", v_new, 3, q.dtype, dev)
+    _check_tensor("kcache", kcache, 4, q.dtype, dev)
+    _check_tensor("vcache", vcache, 4, q.dtype, dev)
+    _check_tensor("positions", positions, 1, torch.int32, dev)
+    B, Hq, d = q.shape
+    _, Hkv, Smax, _ = kcache.shape
+    if kcache.shape[0] != B or kcache.shape[3] != d or tuple(vcache.shape) != tuple(kcache.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} kcache{tuple(kcache.shape)}")
+    if tuple(k_new.shape) != (B, Hkv, d) or tuple(v_new.shape) != (B, Hkv, d):
+        raise ValueError(f"k_new and v_new must be [B, Hkv, d] = {(B, Hkv, d)}")
+    if positions.shape[0] != B:
+        raise ValueError("positions must have B entries")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, 3, q.dtype, dev)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must have the shape of q")
+    need = decode_workspace_bytes(B, Hq, Hkv, Smax, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the GPU of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(dev):
+        st = lib.gqa_attn_decode_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                        kcache.data_ptr(), vcache.data_ptr(),
+                                        positions.data_ptr(), out.data_ptr(), B, Hq, Hkv, Smax,
+                                        d, float(scale), _DTYPES[q.dtype],
+                                        workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream_handle(dev))
     _raise(st)
     return out

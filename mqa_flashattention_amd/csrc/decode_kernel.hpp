@@ -16,6 +16,15 @@
 //   M = max_s m_s,  w_s = 2^(m_s - M),  O = sum_s w_s acc_s / sum_s w_s l_s
 // (m is kept in base-2 scaled units).  The fixed order makes the result
 // bit-reproducible run to run.
+//
+// Decode with append (APPEND = true) folds the cache store of the new token
+// into the same launch -- the K and V stores of one position done together
+// (microLLM-rocm experiment 025) -- with a per-row position table (its
+// experiments 083/084 and 098): row b's new K/V rows go to slot
+// p = positions[b] and the row attends slots [0, p].  Only the split that
+// holds slot p reads it, and that split takes the new rows straight from the
+// inputs (patched into its staged LDS tile), so the store and the read of
+// the slot need no ordering; its first column block performs the store.
 #pragma once
 
 #include "attn_tile.hpp"
@@ -26,7 +35,11 @@ struct DecodeArgs {
   const void* q;
   const void* kc;
   const void* vc;
-  const int32_t* seqlens;
+  const int32_t* seqlens;  // cached lengths; with append, the positions
+  const void* knew;        // append: new K rows [B][Hkv][D]
+  const void* vnew;        // append: new V rows [B][Hkv][D]
+  void* kc_out;            // append: the K cache again, written at the positions
+  void* vc_out;            // append: the V cache again
   void* o;
   float* ws;  // [B][Hq][NS][D + 4]: acc[D], m (scaled), l, 2 pad (16-byte records)
   int B, Hq, Hkv, Smax;
@@ -43,8 +56,34 @@ __device__ __forceinline__ int clamp_len(int32_t n, int smax) {
   return n < 0 ? 0 : (n > smax ? smax : n);
 }
 
-// grid (NS, Hkv * NCB, B), one wavefront per block.
+// Cache slots row b attends: the cached length clamped to [0, Smax]; with
+// append, position p in [0, Smax) gives p + 1 (the new token included) and
+// any other position marks an inactive row (0: no store, zero output).
+template <bool APPEND>
+__device__ __forceinline__ int row_len(const DecodeArgs& a, int b) {
+  const int32_t x = a.seqlens[b];
+  if constexpr (APPEND) return (x >= 0 && x < a.Smax) ? x + 1 : 0;
+  else return clamp_len(x, a.Smax);
+}
+
+// Overwrite key row r of a staged tile with a new row held as 16-byte
+// chunks: lane c < D*ESZ/16 holds chunk c of the K row in kc and of the V
+// row in vc.  K is row-major; V is row-major (fp32) or V^T[d][key] (bf16).
 template <typename T, class C>
+__device__ __forceinline__ void patch_row(T* __restrict__ Ks, T* __restrict__ Vs, int r, int c,
+                                          const u32x4& kc, const u32x4& vc) {
+  *reinterpret_cast<u32x4*>(Ks + r * C::KSTR + c * C::EPC) = kc;
+  if constexpr (C::F32) {
+    *reinterpret_cast<u32x4*>(Vs + r * C::VSTR + c * C::EPC) = vc;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      Vs[(8 * c + e) * C::VSTR + r] = (T)(vc[e >> 1] >> (16 * (e & 1)));
+  }
+}
+
+// grid (NS, Hkv * NCB, B), one wavefront per block.
+template <typename T, class C, bool APPEND>
 __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   static_assert(C::NW == 1 && C::BC == 32, "decode works in single-wave 32-token tiles");
   __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
@@ -55,13 +94,37 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   const int hkv = blockIdx.y / a.NCB;
   const int cb = blockIdx.y % a.NCB;
   const int b = blockIdx.z;
-  const int n = clamp_len(a.seqlens[b], a.Smax);
+  const int n = row_len<APPEND>(a, b);
   const int start = s_idx * a.S_TOK;
   if (start >= n) return;
   const int end = min(n, start + a.S_TOK);
   const int ntok = end - start;
 
   const int lane = threadIdx.x;
+
+  // append: the split holding the new token's slot (the row's last) loads
+  // the new rows, stores them into the caches (first column block only) and
+  // later patches them into the staged tile that holds the slot
+  constexpr int CH = C::D * C::ESZ / 16;  // 16-byte chunks per row
+  u32x4 nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
+  int new_tile = -1, new_row = 0;
+  if constexpr (APPEND) {
+    if (end == n) {
+      const int pos = n - 1;
+      new_tile = (pos - start) / 32;
+      new_row = (pos - start) % 32;
+      if (lane < CH) {
+        const size_t src = ((size_t)b * a.Hkv + hkv) * C::D;
+        nk = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.knew) + src)[lane];
+        nv = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.vnew) + src)[lane];
+        if (cb == 0) {
+          const size_t dst = (((size_t)b * a.Hkv + hkv) * a.Smax + pos) * C::D;
+          reinterpret_cast<u32x4*>(reinterpret_cast<T*>(a.kc_out) + dst)[lane] = nk;
+          reinterpret_cast<u32x4*>(reinterpret_cast<T*>(a.vc_out) + dst)[lane] = nv;
+        }
+      }
+    }
+  }
   const int j = lane & 31;
   const int h2 = lane >> 5;
   const int hig = cb * 32 + j;
@@ -93,6 +156,9 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
 
   auto step = [&](TileRegs<C>& regs, int kt) {
     store_tile<T, C>(regs, Ks, Vs, lane);
+    if constexpr (APPEND) {
+      if (kt == new_tile && lane < CH) patch_row<T, C>(Ks, Vs, new_row, lane, nk, nv);
+    }
     __syncthreads();
     if (kt + 2 < ntiles) load_tile<T, C>(regs, kbase, vbase, (kt + 2) * 32, ntok, lane);
     f32x16 s[C::KB];
@@ -130,7 +196,7 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
 // first the split maxima (one per thread), then the accumulators, with
 // thread t taking 16-byte chunk t % (D/4) of the splits s = t / (D/4) mod G;
 // the G group sums are added through LDS in fixed order.
-template <typename T, int D>
+template <typename T, int D, bool APPEND>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
   constexpr int REC = D + 4;    // floats per partial record
   constexpr int CH = D / 4;     // float4 chunks per record
@@ -143,7 +209,7 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int n = clamp_len(a.seqlens[b], a.Smax);
+  const int n = row_len<APPEND>(a, b);
   T* orow = reinterpret_cast<T*>(a.o) + ((size_t)b * a.Hq + h) * D;
   if (n == 0) {
     for (int d = tid; d < D; d += 256) {

@@ -363,31 +363,98 @@ int decode_split_tokens(int B, int Hkv, int ncb, int smax, int cus) {
   return (int)(tiles_per_split * 32);
 }
 
-template <typename T, class C>
+template <typename T, class C, bool APPEND>
 int launch_decode(gqa::DecodeArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)a.NS, (unsigned)(a.Hkv * a.NCB), (unsigned)a.B);
-  hipLaunchKernelGGL((gqa::decode_split_kernel<T, C>), grid, dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((gqa::decode_split_kernel<T, C, APPEND>), grid, dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode split kernel launch");
-  hipLaunchKernelGGL((gqa::decode_combine_kernel<T, C::D>), dim3((unsigned)a.Hq, (unsigned)a.B),
-                     dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((gqa::decode_combine_kernel<T, C::D, APPEND>),
+                     dim3((unsigned)a.Hq, (unsigned)a.B), dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode combine kernel launch");
   return GQA_OK;
 }
 
-template <typename T, template <int> class Cfg>
+template <typename T, template <int> class Cfg, bool APPEND>
 int dispatch_decode(gqa::DecodeArgs& a, int d, hipStream_t s) {
   switch (d) {
-    case 32: return launch_decode<T, Cfg<32>>(a, s);
-    case 64: return launch_decode<T, Cfg<64>>(a, s);
-    default: return launch_decode<T, Cfg<128>>(a, s);
+    case 32: return launch_decode<T, Cfg<32>, APPEND>(a, s);
+    case 64: return launch_decode<T, Cfg<64>, APPEND>(a, s);
+    default: return launch_decode<T, Cfg<128>, APPEND>(a, s);
   }
 }
 
 size_t decode_ws_bytes(int B, int Hq, int smax, int d, int split) {
   const size_t ns = (size_t)((smax + split - 1) / split);
   return (size_t)B * Hq * ns * (size_t)(d + 4) * sizeof(float);
+}
+
+// Shared body of the two decode entry points.  knew == NULL: plain decode
+// over the cached lengths in lens; otherwise append (lens are positions, the
+// caches are written at them).
+int decode_entry(const void* q, const void* kcache, const void* vcache, const int32_t* lens,
+                 const void* knew, const void* vnew, void* kc_out, void* vc_out, void* o, int B,
+                 int Hq, int Hkv, int Smax, int d, float scale, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  const bool append = knew != nullptr;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Smax < 1 || d < 1)
+    return fail(GQA_ERR_BAD_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Smax=%d d=%d)", B, Hq,
+                Hkv, Smax, d);
+  if (Hq % Hkv != 0)
+    return fail(GQA_ERR_HEAD_GROUPING, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+  if (!std::isfinite(scale)) return fail(GQA_ERR_UNSUPPORTED, "scale must be finite");
+  if ((long long)Smax * d > kIntMax)
+    return fail(GQA_ERR_BAD_SHAPE, "cache capacity too large for 32-bit in-head indexing");
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o) ||
+      (append && (!aligned16(knew) || !aligned16(vnew))))
+    return fail(GQA_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+  const size_t need = decode_ws_bytes(B, Hq, Smax, d, kMinSplit);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(GQA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+
+  int dev = 0;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != GQA_OK) return st;
+
+  const int g = Hq / Hkv;
+  gqa::DecodeArgs a;
+  a.q = q;
+  a.kc = kcache;
+  a.vc = vcache;
+  a.seqlens = lens;
+  a.knew = knew;
+  a.vnew = vnew;
+  a.kc_out = kc_out;
+  a.vc_out = vc_out;
+  a.o = o;
+  a.ws = reinterpret_cast<float*>(workspace);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Smax = Smax;
+  a.g = g;
+  a.NCB = (g + 31) / 32;
+  a.S_TOK = decode_split_tokens(B, Hkv, a.NCB, Smax, info.cus);
+  a.NS = (Smax + a.S_TOK - 1) / a.S_TOK;
+  a.c = softmax_coef(scale);
+  a.thr = gqa::kRescaleSlack / a.c;
+  a.negate_q = scale < 0.f ? 1 : 0;
+  if ((long long)a.Hkv * a.NCB > 65535 || B > 65535)
+    return fail(GQA_ERR_BAD_SHAPE, "grid too large (B=%d, Hkv*blocks=%d)", B, a.Hkv * a.NCB);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (append) {
+    if (dtype == GQA_DTYPE_BF16) return dispatch_decode<uint16_t, DecCfgBf16, true>(a, d, hs);
+    return dispatch_decode<float, DecCfgF32, true>(a, d, hs);
+  }
+  if (dtype == GQA_DTYPE_BF16) return dispatch_decode<uint16_t, DecCfgBf16, false>(a, d, hs);
+  return dispatch_decode<float, DecCfgF32, false>(a, d, hs);
 }
 
 }  // namespace
@@ -485,54 +552,20 @@ int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
   g_last_error.clear();
   if (!q || !kcache || !vcache || !seqlens || !o)
     return fail(GQA_ERR_NULL_POINTER, "q, kcache, vcache, seqlens and o must be non-NULL");
-  if (B < 1 || Hq < 1 || Hkv < 1 || Smax < 1 || d < 1)
-    return fail(GQA_ERR_BAD_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Smax=%d d=%d)", B, Hq,
-                Hkv, Smax, d);
-  if (Hq % Hkv != 0)
-    return fail(GQA_ERR_HEAD_GROUPING, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
-    return fail(GQA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
-  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
-  if (!std::isfinite(scale)) return fail(GQA_ERR_UNSUPPORTED, "scale must be finite");
-  if ((long long)Smax * d > kIntMax)
-    return fail(GQA_ERR_BAD_SHAPE, "cache capacity too large for 32-bit in-head indexing");
-  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o))
-    return fail(GQA_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
-  const size_t need = decode_ws_bytes(B, Hq, Smax, d, kMinSplit);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace))
-    return fail(GQA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need,
-                workspace ? workspace_bytes : (size_t)0);
+  return decode_entry(q, kcache, vcache, seqlens, nullptr, nullptr, nullptr, nullptr, o, B, Hq,
+                      Hkv, Smax, d, scale, dtype, workspace, workspace_bytes, stream);
+}
 
-  int dev = 0;
-  DeviceInfo info;
-  int st = current_device(&dev, &info);
-  if (st != GQA_OK) return st;
-
-  const int g = Hq / Hkv;
-  gqa::DecodeArgs a;
-  a.q = q;
-  a.kc = kcache;
-  a.vc = vcache;
-  a.seqlens = seqlens;
-  a.o = o;
-  a.ws = reinterpret_cast<float*>(workspace);
-  a.B = B;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.Smax = Smax;
-  a.g = g;
-  a.NCB = (g + 31) / 32;
-  a.S_TOK = decode_split_tokens(B, Hkv, a.NCB, Smax, info.cus);
-  a.NS = (Smax + a.S_TOK - 1) / a.S_TOK;
-  a.c = softmax_coef(scale);
-  a.thr = gqa::kRescaleSlack / a.c;
-  a.negate_q = scale < 0.f ? 1 : 0;
-  if ((long long)a.Hkv * a.NCB > 65535 || B > 65535)
-    return fail(GQA_ERR_BAD_SHAPE, "grid too large (B=%d, Hkv*blocks=%d)", B, a.Hkv * a.NCB);
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  if (dtype == GQA_DTYPE_BF16) return dispatch_decode<uint16_t, DecCfgBf16>(a, d, hs);
-  return dispatch_decode<float, DecCfgF32>(a, d, hs);
+int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new, void* kcache,
+                           void* vcache, const int32_t* positions, void* o, int B, int Hq,
+                           int Hkv, int Smax, int d, float scale, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k_new || !v_new || !kcache || !vcache || !positions || !o)
+    return fail(GQA_ERR_NULL_POINTER,
+                "q, k_new, v_new, kcache, vcache, positions and o must be non-NULL");
+  return decode_entry(q, kcache, vcache, positions, k_new, v_new, kcache, vcache, o, B, Hq, Hkv,
+                      Smax, d, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -101,6 +101,11 @@ WORKLOADS = {
         "kv_decode_b8",
         "KV-cache decode, bf16 cache: B=8 Hq=12 Hkv=2 d=128, lengths U[512,2048], Smax=2048",
         decode=DecodeShape(8, 12, 2, 2048, 128, 512, 2048)),
+    "kv_decode_append_b8": Workload(
+        "kv_decode_append_b8",
+        "KV-cache decode with the new token's K/V appended in the same launch, bf16: B=8 Hq=12 "
+        "Hkv=2 d=128, positions U[511,2047] (lengths U[512,2048] after the append), Smax=2048",
+        decode=DecodeShape(8, 12, 2, 2048, 128, 512, 2048)),
     "chunked_prefill_4k": Workload(
         "chunked_prefill_4k",
         "Chunked prefill, bf16, causal: B=1 Hq=32 Hkv=8 d=128, Nq=512 at q_offset=3584, Nk=4096",
@@ -125,6 +130,19 @@ def decode_inputs(s: DecodeShape, seed: int = 0):
     vc = torch.randn((s.B, s.Hkv, s.Smax, s.d), generator=g, dtype=torch.float32)
     lens = torch.randint(s.len_lo, s.len_hi + 1, (s.B,), generator=g, dtype=torch.int64)
     return q.to(s.dtype), kc.to(s.dtype), vc.to(s.dtype), lens.to(torch.int32)
+
+
+def append_inputs(s: DecodeShape, seed: int = 0):
+    """CPU tensors (q, k_new, v_new, kcache, vcache, positions[int32]) for a
+    decode-with-append step: q and the caches as decode_inputs(s, seed), the
+    position of row b one less than its drawn length (so the row attends
+    that many slots after the append), then the new K and V rows from their
+    own generator seeded seed + 7919, in that order."""
+    q, kc, vc, lens = decode_inputs(s, seed)
+    g = torch.Generator(device="cpu").manual_seed(seed + 7919)
+    kn = torch.randn((s.B, s.Hkv, s.d), generator=g, dtype=torch.float32).to(s.dtype)
+    vn = torch.randn((s.B, s.Hkv, s.d), generator=g, dtype=torch.float32).to(s.dtype)
+    return q, kn, vn, kc, vc, (lens - 1).to(torch.int32)
 
 
 def random_tensor(shape, seed: int, dtype=torch.float32, scale: float = 1.0):

@@ -103,6 +103,30 @@ def test_decode_rejects_invalid_arguments(kw, code):
     assert binding.lib.gqa_last_error_string()
 
 
+def app(q=P[0], kn=P[6], vn=P[7], kc=P[1], vc=P[2], pos=P[4], o=P[3], B=8, Hq=12, Hkv=2,
+        Smax=2048, d=128, scale=0.09, dtype=BF16, ws=P[5], ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = binding.decode_workspace_bytes(B, Hq, Hkv, Smax, d)
+    return binding.lib.gqa_attn_decode_append(q, kn, vn, kc, vc, pos, o, B, Hq, Hkv, Smax, d,
+                                              ctypes.c_float(scale), dtype, ws, ws_bytes, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(kn=None), NULLP), (dict(vn=None), NULLP),
+    (dict(kc=None), NULLP), (dict(vc=None), NULLP), (dict(pos=None), NULLP),
+    (dict(o=None), NULLP),
+    (dict(B=0), SHAPE), (dict(Smax=0), SHAPE), (dict(Hq=-2), SHAPE),
+    (dict(Smax=2 ** 25, d=128), SHAPE),
+    (dict(Hq=12, Hkv=5), GROUP),
+    (dict(d=48), UNSUP), (dict(dtype=3), UNSUP), (dict(scale=float("nan")), UNSUP),
+    (dict(kn=ctypes.c_void_p(0x30004)), UNSUP), (dict(vn=ctypes.c_void_p(0x30008)), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=64), WS),
+])
+def test_decode_append_rejects_invalid_arguments(kw, code):
+    assert app(**kw) == code
+    assert binding.lib.gqa_last_error_string()
+
+
 def test_decode_workspace_bytes():
     ws = binding.decode_workspace_bytes
     # B * Hq * ceil(Smax / 32) partial records of d accumulators + max + sum,
@@ -119,6 +143,7 @@ def test_valid_call_without_gpu_reports_no_device():
     assert fwd() == NODEV
     assert b"device" in binding.lib.gqa_last_error_string()
     assert dec() == NODEV
+    assert app() == NODEV
 
 
 def test_binding_checks_tensors_before_the_library():
