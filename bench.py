@@ -113,7 +113,8 @@ def _counter_means(directory: str, counter: str) -> dict:
                 if row["Counter_Name"] != counter:
                     continue
                 name = row["Kernel_Name"]
-                if "gqa::prefill" in name and "128, 32, 4>, true" in name:
+                # the LLaMA launch: bf16 d=128, 32-key tiles, contiguous K/V, causal
+                if "gqa::prefill" in name and "128, 32, 4, false>, true" in name:
                     kind = name.split("(")[0].replace("void ", "")
                     names.add(kind)
                 elif "neg_kernel" in name:
@@ -162,20 +163,25 @@ def check(out, ref, tol, what):
     return err
 
 
-def time_fwd_workload(s, steps, warmup):
-    """Event-timed average duration (ms) of one gqa_attn_fwd launch."""
+def time_fwd_workload(s, steps, warmup, bthd=False):
+    """Event-timed average duration (ms) of one gqa_attn_fwd launch; with bthd,
+    of one gqa_attn_fwd_strided launch on token-major [B, N, H, d] tensors."""
     import torch
-    from mqa_flashattention_amd import attn_fwd
+    from mqa_flashattention_amd import attn_fwd, attn_fwd_strided
     from mqa_flashattention_amd.workloads import fwd_inputs
     q, k, v = (t.cuda() for t in fwd_inputs(s, 0))
-    out = torch.empty_like(q)
+    fn = attn_fwd
+    if bthd:
+        q, k, v = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))
+        fn = attn_fwd_strided
+    out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     for _ in range(warmup):
-        attn_fwd(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale, out=out)
+        fn(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale, out=out)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        attn_fwd(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale, out=out)
+        fn(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale, out=out)
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
@@ -396,6 +402,12 @@ def main(argv=None):
                 tf = prefill_flops(s) / (ms * 1e-3) / 1e12
                 extra[f"{name}[Hkv={s.Hkv}]"] = {"ms": round(ms, 5), "tflops": round(tf, 2),
                                                  "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        ms = time_fwd_workload(ps, max(10, K // 2), 3, bthd=True)
+        tf = prefill_flops(ps) / (ms * 1e-3) / 1e12
+        extra["llama3_8b_prefill[bthd]"] = {
+            "ms": round(ms, 5), "tflops": round(tf, 2),
+            "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "note": "token-major [B, N, H, d] Q/K/V/O through gqa_attn_fwd_strided, no copies"}
         sa = WORKLOADS["kv_decode_append_b8"].decode
         ms, positions = time_append_workload(sa, max(20, K), 5)
         gb = append_bytes(sa, positions) / (ms * 1e-3) / 1e9

@@ -84,6 +84,37 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o,
                  int dtype, void* stream);
 
 /*
+ * The same forward over strided tensors, e.g. token-major [B, N, H, d]
+ * (BTHD) activations used in place, with no layout copy.
+ *
+ *   q_strides  : host pointer to 3 int64 element strides of Q and O, in the
+ *                order {batch, head, token}
+ *   kv_strides : host pointer to 3 int64 element strides of K and V, same order
+ *
+ * Element (b, h, i, c) of Q sits at q + b*q_strides[0] + h*q_strides[1] +
+ * i*q_strides[2] + c, and likewise for O; K and V use kv_strides.  The head
+ * dimension is always contiguous.  Contiguous [B, H, N, d] is {H*N*d, N*d,
+ * d}; BTHD is {N*H*d, d, H*d}.  Two stride sets, one for the query side and
+ * one for the KV side, as in the GQA launcher of the BootstrapAI evolution
+ * log ("Kernel 9"); token-major attention that removes the layout copies
+ * around the kernel follows the microLLM-rocm optimization log (experiments
+ * 162-164 and 201-204).
+ *
+ * Additional requirements (else nothing is launched):
+ *   strides >= 0 (GQA_ERR_BAD_SHAPE) and multiples of 16 bytes
+ *   (GQA_ERR_UNSUPPORTED); the Q/O strides must describe non-overlapping
+ *   output rows (GQA_ERR_BAD_SHAPE); the K/V token stride below 2^25 bytes
+ *   (GQA_ERR_BAD_SHAPE).  K and V may overlap or repeat (a zero stride
+ *   broadcasts); O must not overlap Q, K or V.  Everything else as
+ *   gqa_attn_fwd, whose result this equals bit for bit for the same values.
+ */
+int gqa_attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                         const int64_t* q_strides, const int64_t* kv_strides,
+                         int causal, int q_offset, float scale,
+                         int dtype, void* stream);
+
+/*
  * Bytes of device workspace gqa_attn_decode needs for these sizes (an upper
  * bound that does not depend on seqlens).  Returns 0 for invalid sizes.
  */

@@ -26,8 +26,9 @@ STATUS_NAMES = {
     0: "GQA_OK", 1: "GQA_ERR_NULL_POINTER", 2: "GQA_ERR_BAD_SHAPE", 3: "GQA_ERR_HEAD_GROUPING",
     4: "GQA_ERR_UNSUPPORTED", 5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_NO_DEVICE", 7: "GQA_ERR_HIP",
 }
-EXPORTED = ("gqa_attn_fwd", "gqa_attn_decode", "gqa_attn_decode_append",
-            "gqa_attn_decode_workspace_bytes", "gqa_status_string", "gqa_last_error_string")
+EXPORTED = ("gqa_attn_fwd", "gqa_attn_fwd_strided", "gqa_attn_decode",
+            "gqa_attn_decode_append", "gqa_attn_decode_workspace_bytes", "gqa_status_string",
+            "gqa_last_error_string")
 
 
 class GqaError(RuntimeError):
@@ -45,6 +46,10 @@ def _load() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.gqa_attn_fwd.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
     lib.gqa_attn_fwd.restype = i
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.gqa_attn_fwd_strided.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i, i, f,
+                                         i, vp]
+    lib.gqa_attn_fwd_strided.restype = i
     lib.gqa_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.gqa_attn_decode_workspace_bytes.restype = sz
     lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -72,7 +77,8 @@ def _raise(status: int) -> None:
         raise GqaError(status, detail or lib.gqa_status_string(status).decode())
 
 
-def _check_tensor(name: str, t: torch.Tensor, ndim: int, dtype: torch.dtype, device) -> None:
+def _check_tensor(name: str, t: torch.Tensor, ndim: int, dtype: torch.dtype, device,
+                  contiguous: bool = True) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dim() != ndim:
@@ -81,8 +87,10 @@ def _check_tensor(name: str, t: torch.Tensor, ndim: int, dtype: torch.dtype, dev
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if t.device != device or t.device.type != "cuda":
         raise ValueError(f"{name} must be on {device} (a GPU device), got {t.device}")
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if not contiguous and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last (head) dimension must be contiguous")
 
 
 def _stream_handle(device) -> ctypes.c_void_p:
@@ -119,6 +127,47 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
         st = lib.gqa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), int(q_offset),
                               float(scale), _DTYPES[q.dtype], _stream_handle(dev))
+    _raise(st)
+    return out
+
+
+def attn_fwd_strided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                     q_offset: int = 0, scale: float | None = None,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """attn_fwd over strided views, via gqa_attn_fwd_strided.
+
+    q [B, Hq, Nq, d] and k, v [B, Hkv, Nk, d] are indexed as logical
+    (batch, head, token, d) views with any strides whose last one is 1, e.g.
+    ``x.transpose(1, 2)`` of a token-major [B, N, H, d] tensor: no copy is
+    made.  k and v must share their strides; out must have the strides of q
+    (it is allocated with them when not given)."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _check_tensor("q", q, 4, q.dtype, dev, contiguous=False)
+    _check_tensor("k", k, 4, q.dtype, dev, contiguous=False)
+    _check_tensor("v", v, 4, q.dtype, dev, contiguous=False)
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if k.shape[0] != B or k.shape[3] != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if k.stride() != v.stride():
+        raise ValueError(f"k and v must share strides, got {k.stride()} and {v.stride()}")
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=dev)
+    else:
+        _check_tensor("out", out, 4, q.dtype, dev, contiguous=False)
+        if tuple(out.shape) != tuple(q.shape) or out.stride() != q.stride():
+            raise ValueError("out must have the shape and strides of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    qs = (ctypes.c_int64 * 3)(q.stride(0), q.stride(1), q.stride(2))
+    kvs = (ctypes.c_int64 * 3)(k.stride(0), k.stride(1), k.stride(2))
+    with torch.cuda.device(dev):
+        st = lib.gqa_attn_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      B, Hq, Hkv, Nq, Nk, d, qs, kvs, int(bool(causal)),
+                                      int(q_offset), float(scale), _DTYPES[q.dtype],
+                                      _stream_handle(dev))
     _raise(st)
     return out
 

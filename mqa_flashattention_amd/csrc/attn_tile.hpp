@@ -95,12 +95,16 @@ __device__ __forceinline__ constexpr int key_of_reg(int r, int h2) {
 //   D  : head dimension (32, 64, 128)
 //   BC : keys per tile (multiple of 32)
 //   NW : wavefronts sharing one K/V tile
-template <typename T, int D_, int BC_, int NW_>
+//   KVS: K/V key rows at a run-time stride (token-major or padded layouts);
+//        false: rows are contiguous, D elements apart (a compile-time stride,
+//        so load offsets fold into the instructions)
+template <typename T, int D_, int BC_, int NW_, bool KVS_ = false>
 struct TileCfg {
   static constexpr bool F32 = std::is_same<T, float>::value;
   static constexpr int D = D_;
   static constexpr int BC = BC_;
   static constexpr int NW = NW_;
+  static constexpr bool KVS = KVS_;
   static constexpr int NT = 64 * NW;
   static constexpr int KB = BC / 32;  // 32-key blocks per tile
   static constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -173,15 +177,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uin
 // offsets do not depend on the tile, so the loop computes them once; the
 // tile start is scalar work.  For K, consecutive threads take consecutive
 // 16-byte chunks of a row, so a wave's load instruction covers whole rows.
+// rowb: bytes from one key row to the next, a multiple of 16; used only when
+// C::KVS (otherwise the rows are D * ESZ bytes apart).
 template <typename T, class C>
 __device__ __forceinline__ void load_tile(TileRegs<C>& r, const T* __restrict__ kbase,
                                           const T* __restrict__ vbase, int key0, int nkeys,
-                                          int tid) {
-  constexpr int ROWB = C::D * C::ESZ;  // bytes per row
+                                          int tid, int rowb) {
+  const int ROWB = C::KVS ? rowb : C::D * C::ESZ;
   const int rows = nkeys - key0 < C::BC ? (nkeys - key0 > 0 ? nkeys - key0 : 0) : C::BC;
-  const size_t base = (size_t)key0 * C::D;
-  const auto krs = buffer_rsrc(kbase + base, (uint32_t)(rows * ROWB));
-  const auto vrs = buffer_rsrc(vbase + base, (uint32_t)(rows * ROWB));
+  // unsigned 32 x 32 -> 64-bit byte offset: scalar multiplies (a signed
+  // 64-bit product would be done on the vector unit)
+  const uint64_t base = (uint64_t)(uint32_t)key0 * (uint32_t)ROWB;
+  // the range is uniform; readfirstlane keeps it (and so the resource) in
+  // scalar registers -- a vector value here makes every load a waterfall loop
+  const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)(rows * ROWB));
+  const auto krs = buffer_rsrc(reinterpret_cast<const char*>(kbase) + base, bytes);
+  const auto vrs = buffer_rsrc(reinterpret_cast<const char*>(vbase) + base, bytes);
 #pragma unroll
   for (int n = 0; n < C::K_PER_T; ++n) {
     const int id = tid + n * C::NT;

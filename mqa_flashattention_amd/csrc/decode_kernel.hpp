@@ -151,8 +151,8 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   // register set (an indexed pair would be placed in scratch memory).
   const int ntiles = (ntok + 31) / 32;
   TileRegs<C> ra, rb;
-  load_tile<T, C>(ra, kbase, vbase, 0, ntok, lane);
-  if (ntiles > 1) load_tile<T, C>(rb, kbase, vbase, 32, ntok, lane);
+  load_tile<T, C>(ra, kbase, vbase, 0, ntok, lane, C::D * C::ESZ);
+  if (ntiles > 1) load_tile<T, C>(rb, kbase, vbase, 32, ntok, lane, C::D * C::ESZ);
 
   auto step = [&](TileRegs<C>& regs, int kt) {
     store_tile<T, C>(regs, Ks, Vs, lane);
@@ -160,7 +160,8 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
       if (kt == new_tile && lane < CH) patch_row<T, C>(Ks, Vs, new_row, lane, nk, nv);
     }
     __syncthreads();
-    if (kt + 2 < ntiles) load_tile<T, C>(regs, kbase, vbase, (kt + 2) * 32, ntok, lane);
+    if (kt + 2 < ntiles)
+      load_tile<T, C>(regs, kbase, vbase, (kt + 2) * 32, ntok, lane, C::D * C::ESZ);
     f32x16 s[C::KB];
     qk_tile<T, C>(s, qf, Ks, j, h2);
     const int key0 = kt * 32;

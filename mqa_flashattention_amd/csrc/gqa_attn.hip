@@ -186,6 +186,11 @@ template <int D>
 using CfgBf16 = gqa::TileCfg<uint16_t, D, (D == 128 ? 32 : 64), kPrefillWaves>;
 template <int D>
 using CfgF32 = gqa::TileCfg<float, D, 32, kPrefillWaves>;
+// the same with a run-time K/V key-row stride (token-major or padded K/V)
+template <int D>
+using CfgBf16S = gqa::TileCfg<uint16_t, D, (D == 128 ? 32 : 64), kPrefillWaves, true>;
+template <int D>
+using CfgF32S = gqa::TileCfg<float, D, 32, kPrefillWaves, true>;
 
 // Unit decomposition for units of M columns: Gu = min(g, M) heads of a
 // group stacked over R = M / Gu positions, HB head blocks per group, NQB
@@ -390,6 +395,83 @@ size_t decode_ws_bytes(int B, int Hq, int smax, int d, int split) {
   return (size_t)B * Hq * ns * (size_t)(d + 4) * sizeof(float);
 }
 
+// Shared body of the two forward entry points: qs / kvs are element strides
+// {batch, head, token} of Q and O / of K and V (the head dimension is
+// contiguous); pointers and strides are already checked for NULL.
+int fwd_entry(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+              int Nq, int Nk, int d, const int64_t* qs, const int64_t* kvs, int causal,
+              int q_offset, float scale, int dtype, void* stream) {
+  // ---- validation: host only, before any HIP call
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1)
+    return fail(GQA_ERR_BAD_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d)", B,
+                Hq, Hkv, Nq, Nk, d);
+  if (causal && q_offset < 0) return fail(GQA_ERR_BAD_SHAPE, "q_offset=%d < 0", q_offset);
+  if (Hq % Hkv != 0)
+    return fail(GQA_ERR_HEAD_GROUPING, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+  if (!std::isfinite(scale)) return fail(GQA_ERR_UNSUPPORTED, "scale must be finite");
+  if ((long long)Nq * d > kIntMax || (long long)Nk * d > kIntMax ||
+      (causal && (long long)q_offset + Nq > kIntMax))
+    return fail(GQA_ERR_BAD_SHAPE, "sequence too long for 32-bit in-head indexing");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(GQA_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+
+  const int M = 32 * kPrefillWaves;
+  const int g = Hq / Hkv;
+  const int Gu = g < M ? g : M;
+  const int R = M / Gu;
+  const int HB = (g + Gu - 1) / Gu;
+  const long long NQB = ((long long)Nq + R - 1) / R;
+  const long long T = (long long)B * Hkv * HB * NQB;
+  if (T > kIntMax) return fail(GQA_ERR_BAD_SHAPE, "too many work units (%lld)", T);
+
+  // ---- device
+  int dev = 0;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != GQA_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+
+  const int esz = dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  gqa::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.q_sb = qs[0];
+  a.q_sh = qs[1];
+  a.q_sn = qs[2];
+  a.kv_sb = kvs[0];
+  a.kv_sh = kvs[1];
+  a.kv_rowb = (int)(kvs[2] * esz);
+  a.g = g;
+  a.Gu = Gu;
+  a.R = R;
+  a.HB = HB;
+  a.NQB = (int)NQB;
+  a.T = (int)T;
+  a.q_offset = causal ? q_offset : 0;
+  a.c = softmax_coef(scale);
+  a.thr = gqa::kRescaleSlack / a.c;
+  a.negate_q = scale < 0.f ? 1 : 0;
+  // K/V rows D elements apart: the compile-time stride
+  if (kvs[2] == d) {
+    if (dtype == GQA_DTYPE_BF16)
+      return dispatch_prefill<uint16_t, CfgBf16>(a, d, causal, dev, info, hs);
+    return dispatch_prefill<float, CfgF32>(a, d, causal, dev, info, hs);
+  }
+  if (dtype == GQA_DTYPE_BF16)
+    return dispatch_prefill<uint16_t, CfgBf16S>(a, d, causal, dev, info, hs);
+  return dispatch_prefill<float, CfgF32S>(a, d, causal, dev, info, hs);
+}
+
 // Shared body of the two decode entry points.  knew == NULL: plain decode
 // over the cached lengths in lens; otherwise append (lens are positions, the
 // caches are written at them).
@@ -481,63 +563,53 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, in
                  int Nq, int Nk, int d, int causal, int q_offset, float scale, int dtype,
                  void* stream) {
   g_last_error.clear();
-  // ---- validation: host only, before any HIP call
   if (!q || !k || !v || !o) return fail(GQA_ERR_NULL_POINTER, "q, k, v and o must be non-NULL");
-  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1)
-    return fail(GQA_ERR_BAD_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d)", B,
-                Hq, Hkv, Nq, Nk, d);
-  if (causal && q_offset < 0) return fail(GQA_ERR_BAD_SHAPE, "q_offset=%d < 0", q_offset);
-  if (Hq % Hkv != 0)
-    return fail(GQA_ERR_HEAD_GROUPING, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
-    return fail(GQA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
-  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
-  if (!std::isfinite(scale)) return fail(GQA_ERR_UNSUPPORTED, "scale must be finite");
-  if ((long long)Nq * d > kIntMax || (long long)Nk * d > kIntMax ||
-      (causal && (long long)q_offset + Nq > kIntMax))
-    return fail(GQA_ERR_BAD_SHAPE, "sequence too long for 32-bit in-head indexing");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(GQA_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+  // contiguous [B, H, N, d]
+  const int64_t qs[3] = {(int64_t)Hq * Nq * d, (int64_t)Nq * d, (int64_t)d};
+  const int64_t kvs[3] = {(int64_t)Hkv * Nk * d, (int64_t)Nk * d, (int64_t)d};
+  return fwd_entry(q, k, v, o, B, Hq, Hkv, Nq, Nk, d, qs, kvs, causal, q_offset, scale, dtype,
+                   stream);
+}
 
-  const int M = 32 * kPrefillWaves;
-  const int g = Hq / Hkv;
-  const int Gu = g < M ? g : M;
-  const int R = M / Gu;
-  const int HB = (g + Gu - 1) / Gu;
-  const long long NQB = ((long long)Nq + R - 1) / R;
-  const long long T = (long long)B * Hkv * HB * NQB;
-  if (T > kIntMax) return fail(GQA_ERR_BAD_SHAPE, "too many work units (%lld)", T);
-
-  // ---- device
-  int dev = 0;
-  DeviceInfo info;
-  int st = current_device(&dev, &info);
-  if (st != GQA_OK) return st;
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-
-  gqa::PrefillArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.B = B;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.Nq = Nq;
-  a.Nk = Nk;
-  a.g = g;
-  a.Gu = Gu;
-  a.R = R;
-  a.HB = HB;
-  a.NQB = (int)NQB;
-  a.T = (int)T;
-  a.q_offset = causal ? q_offset : 0;
-  a.c = softmax_coef(scale);
-  a.thr = gqa::kRescaleSlack / a.c;
-  a.negate_q = scale < 0.f ? 1 : 0;
-  if (dtype == GQA_DTYPE_BF16)
-    return dispatch_prefill<uint16_t, CfgBf16>(a, d, causal, dev, info, hs);
-  return dispatch_prefill<float, CfgF32>(a, d, causal, dev, info, hs);
+int gqa_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, int B, int Hq,
+                         int Hkv, int Nq, int Nk, int d, const int64_t* q_strides,
+                         const int64_t* kv_strides, int causal, int q_offset, float scale,
+                         int dtype, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !q_strides || !kv_strides)
+    return fail(GQA_ERR_NULL_POINTER, "q, k, v, o, q_strides and kv_strides must be non-NULL");
+  for (int i = 0; i < 3; ++i)
+    if (q_strides[i] < 0 || kv_strides[i] < 0)
+      return fail(GQA_ERR_BAD_SHAPE, "strides must be >= 0");
+  const int64_t esz = dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  for (int i = 0; i < 3; ++i)
+    if ((q_strides[i] * esz) % 16 != 0 || (kv_strides[i] * esz) % 16 != 0)
+      return fail(GQA_ERR_UNSUPPORTED, "strides must be multiples of 16 bytes");
+  // O is written through the Q strides: its rows must not overlap.  Sorted by
+  // stride, every dimension of extent > 1 must step past the whole extent of
+  // the ones inside it (the head dimension, stride 1, innermost).
+  if (B >= 1 && Hq >= 1 && Nq >= 1 && d >= 1) {
+    int64_t st[3] = {q_strides[0], q_strides[1], q_strides[2]};
+    int64_t ex[3] = {B, Hq, Nq};
+    for (int x = 0; x < 3; ++x)
+      for (int y = x + 1; y < 3; ++y)
+        if (st[y] < st[x]) {
+          std::swap(st[x], st[y]);
+          std::swap(ex[x], ex[y]);
+        }
+    int64_t span = d;  // elements covered by the dimensions inside
+    for (int x = 0; x < 3; ++x) {
+      if (ex[x] == 1) continue;
+      if (st[x] < span)
+        return fail(GQA_ERR_BAD_SHAPE, "q/o strides make output rows overlap");
+      span = st[x] * ex[x];
+    }
+  }
+  if (kv_strides[2] * esz * 64 > kIntMax)
+    return fail(GQA_ERR_BAD_SHAPE, "k/v token stride too large (%lld elements)",
+                (long long)kv_strides[2]);
+  return fwd_entry(q, k, v, o, B, Hq, Hkv, Nq, Nk, d, q_strides, kv_strides, causal, q_offset,
+                   scale, dtype, stream);
 }
 
 size_t gqa_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Smax, int d) {

@@ -52,6 +52,11 @@ struct PrefillArgs {
   const void* v;
   void* o;
   int B, Hq, Hkv, Nq, Nk;
+  // element strides (batch, head, token; d is contiguous): one set for Q and
+  // O, one for K and V
+  long long q_sb, q_sh, q_sn;
+  long long kv_sb, kv_sh;
+  int kv_rowb;  // K/V token stride in bytes
   int g;    // Hq / Hkv
   int Gu;   // query heads per unit
   int R;    // query positions per unit
@@ -180,7 +185,7 @@ __device__ __forceinline__ Column lane_column(const PrefillArgs& a, int b, int h
   c.i = qb * a.R + p;
   c.valid = (r < a.Gu) && (hig < a.g) && (c.i < a.Nq);
   const int h = hkv * a.g + hig;
-  c.row_off = c.valid ? (((size_t)b * a.Hq + h) * a.Nq + c.i) * C::D : 0;
+  c.row_off = c.valid ? (size_t)(b * a.q_sb + h * a.q_sh + c.i * a.q_sn) : 0;
   return c;
 }
 
@@ -209,7 +214,7 @@ struct SegTiles {
 template <typename T, class C>
 __device__ __forceinline__ void kv_bases(const PrefillArgs& a, int b, int hkv, const T*& kbase,
                                          const T*& vbase) {
-  const size_t kv_off = ((size_t)b * a.Hkv + hkv) * a.Nk * C::D;
+  const size_t kv_off = (size_t)(b * a.kv_sb + hkv * a.kv_sh);
   kbase = uniform_ptr(reinterpret_cast<const T*>(a.k) + kv_off);
   vbase = uniform_ptr(reinterpret_cast<const T*>(a.v) + kv_off);
 }
@@ -224,8 +229,8 @@ __device__ __forceinline__ void seg_begin(const PrefillArgs& a, SegIn<C>& in, in
   kv_bases<T, C>(a, b, hkv, kbase, vbase);
   load_q_frag<T, C>(in.qf, reinterpret_cast<const T*>(a.q) + col.row_off, col.valid,
                     a.negate_q != 0, h2);
-  load_tile<T, C>(in.ra, kbase, vbase, st.at(0) * C::BC, a.Nk, tid);
-  load_tile<T, C>(in.rb, kbase, vbase, st.at(1) * C::BC, a.Nk, tid);
+  load_tile<T, C>(in.ra, kbase, vbase, st.at(0) * C::BC, a.Nk, tid, a.kv_rowb);
+  load_tile<T, C>(in.rb, kbase, vbase, st.at(1) * C::BC, a.Nk, tid, a.kv_rowb);
 }
 
 // Runs key tiles st of unit (b, hkv, ., qb) for the lane's column col, from
@@ -284,7 +289,7 @@ __device__ __forceinline__ void seg_run(const PrefillArgs& a, char* smem, SegIn<
 
   auto step = [&](TileRegs<C>& mine, TileRegs<C>& next, int kt) {
     const int cur = kt & 1;
-    load_tile<T, C>(mine, kbase, vbase, st.at(kt + 2) * C::BC, a.Nk, tid);
+    load_tile<T, C>(mine, kbase, vbase, st.at(kt + 2) * C::BC, a.Nk, tid, a.kv_rowb);
     if (!PAIRED || kt < st.ntiles) {
       f32x16 s[C::KB];
       qk_tile<T, C>(s, in.qf, stK(cur), j, h2);

@@ -103,6 +103,38 @@ def test_decode_rejects_invalid_arguments(kw, code):
     assert binding.lib.gqa_last_error_string()
 
 
+def fwd_s(q=P[0], k=P[1], v=P[2], o=P[3], B=2, Hq=8, Hkv=2, Nq=64, Nk=96, d=64, qs=None,
+          kvs=None, causal=1, q_offset=0, scale=0.17, dtype=BF16, stream=None):
+    """Strided forward; default strides are BTHD (token-major)."""
+    I3 = ctypes.c_int64 * 3
+    qs = I3(*(qs if qs is not None else (Nq * Hq * d, d, Hq * d)))
+    kvs = I3(*(kvs if kvs is not None else (Nk * Hkv * d, d, Hkv * d)))
+    return binding.lib.gqa_attn_fwd_strided(q, k, v, o, B, Hq, Hkv, Nq, Nk, d, qs, kvs, causal,
+                                            q_offset, ctypes.c_float(scale), dtype, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(o=None), NULLP),
+    (dict(qs=(-1, 64, 512)), SHAPE), (dict(kvs=(0, 64, -128)), SHAPE),
+    (dict(qs=(64 * 8 * 64, 64, 8 * 64 + 4)), UNSUP),   # token stride not 16-byte aligned
+    (dict(kvs=(3, 64, 128)), UNSUP),                    # batch stride not 16-byte aligned
+    (dict(qs=(64 * 8 * 64, 64, 32)), SHAPE),            # output rows overlap (token < d)
+    (dict(qs=(0, 64, 512)), SHAPE),                     # batches alias in the output
+    (dict(qs=(64 * 8 * 64, 0, 512)), SHAPE),            # heads alias in the output
+    (dict(kvs=(0, 64, 2 ** 24)), SHAPE),                # K/V token stride too large
+    (dict(Hq=6, Hkv=4), GROUP), (dict(d=48), UNSUP), (dict(B=0), SHAPE),
+    (dict(q=ctypes.c_void_p(0x10008)), UNSUP),
+])
+def test_fwd_strided_rejects_invalid_arguments(kw, code):
+    assert fwd_s(**kw) == code
+    assert binding.lib.gqa_last_error_string()
+
+
+def test_fwd_strided_null_stride_arrays():
+    assert binding.lib.gqa_attn_fwd_strided(P[0], P[1], P[2], P[3], 1, 4, 2, 8, 8, 32, None, None,
+                                            0, 0, ctypes.c_float(0.1), BF16, None) == NULLP
+
+
 def app(q=P[0], kn=P[6], vn=P[7], kc=P[1], vc=P[2], pos=P[4], o=P[3], B=8, Hq=12, Hkv=2,
         Smax=2048, d=128, scale=0.09, dtype=BF16, ws=P[5], ws_bytes=None, stream=None):
     if ws_bytes is None:
@@ -144,6 +176,9 @@ def test_valid_call_without_gpu_reports_no_device():
     assert b"device" in binding.lib.gqa_last_error_string()
     assert dec() == NODEV
     assert app() == NODEV
+    assert fwd_s() == NODEV
+    # zero K/V batch stride (broadcast reads) is valid
+    assert fwd_s(kvs=(0, 64, 128)) == NODEV
 
 
 def test_binding_checks_tensors_before_the_library():
