@@ -163,6 +163,17 @@ def check(out, ref, tol, what):
     return err
 
 
+def head_start(steps):
+    """Queue a spin kernel of about 5 ms + 50 us per call on the current stream.
+
+    The host needs longer to issue one decode call (Python argument checks,
+    event records) than the call takes on the GPU; without a head start the
+    GPU catches up and idles, and an event pair around a call then also
+    counts the host time spent issuing it."""
+    import torch
+    torch.cuda._sleep(int(2.4e9 * (5e-3 + 50e-6 * steps)))
+
+
 def time_fwd_workload(s, steps, warmup, bthd=False):
     """Event-timed average duration (ms) of one gqa_attn_fwd launch; with bthd,
     of one gqa_attn_fwd_strided launch on token-major [B, N, H, d] tensors."""
@@ -221,10 +232,7 @@ def time_append_workload(s, steps, warmup):
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
-    # a short spin kernel ahead of the calls keeps the GPU behind the host, so
-    # every event pair brackets GPU work only (one call takes less GPU time
-    # than the host needs to issue it)
-    torch.cuda._sleep(50_000_000)
+    head_start(steps)
     for i in range(steps):
         ev[i][0].record()
         attn_decode_append(q, kn, vn, kcs[(i + 1) % DECODE_SETS], vcs[(i + 1) % DECODE_SETS],
@@ -317,6 +325,9 @@ def main(argv=None):
         prefill()
         decode(i % DECODE_SETS)
     torch.cuda.synchronize()
+    # Each launch between an event pair of its own, steps interleaved as a
+    # serving loop would issue them; the host issues a step faster than the
+    # GPU runs it, so the pairs bracket GPU work only.
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -182,6 +182,7 @@ int occupancy(const void* kernel, int threads) {
 // two waves per SIMD), 64-key tiles below; fp32: 32-key tiles.  Four waves
 // per workgroup, 128 query columns per unit.
 constexpr int kPrefillWaves = 4;
+constexpr int kLdsBytes = 160 * 1024;  // LDS of one gfx950 CU
 template <int D>
 using CfgBf16 = gqa::TileCfg<uint16_t, D, (D == 128 ? 32 : 64), kPrefillWaves>;
 template <int D>
@@ -273,6 +274,26 @@ int launch_prefill(gqa::PrefillArgs& a, int dev_id, const DeviceInfo& dev, hipSt
   const void* kern = reinterpret_cast<const void*>(&gqa::prefill_kernel<T, C, CAUSAL>);
   const int per_cu = occupancy(kern, C::NT);
   const long long slots = (long long)dev.cus * per_cu;
+  // Fewer 128-column units than CUs, but 3/4 to 1 of them per CU as
+  // 64-column units with >= 8 key tiles each: one 8-wave workgroup per
+  // 64-column unit whose four 2-wave groups split the unit's keys and merge
+  // in LDS -- no partial records, no merge pass.  (Needs eight 2-wave ring
+  // stages in LDS.)
+  using CQ = gqa::TileCfg<T, C::D, C::BC, 2, C::KVS>;
+  if constexpr (8 * CQ::STAGE_BYTES <= kLdsBytes) {
+    gqa::PrefillArgs q = a;
+    decompose(q, 64);
+    const long long t64 = q.T;
+    const long long min_tiles = unit_tiles<CQ>(q, CAUSAL, 0);  // the lightest unit
+    if (a.T < dev.cus && 4 * t64 >= 3LL * dev.cus && t64 <= dev.cus && min_tiles >= 8) {
+      (void)hipGetLastError();  // a stale error belongs to an earlier call
+      hipLaunchKernelGGL((gqa::prefill_quad_kernel<T, CQ, CAUSAL>), dim3((unsigned)t64),
+                         dim3(4 * CQ::NT), 0, stream, q);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(e, "prefill quad kernel launch");
+      return GQA_OK;
+    }
+  }
   long long cuts = 0;
   const bool balanced = plan_balanced<C>(a, CAUSAL, slots, &cuts);
   // causal, with at least one heavy/light unit pair per CU: one pair per

@@ -400,7 +400,6 @@ prefill_kernel(PrefillArgs a) {
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int j = lane & 31;
-  const int h2 = lane >> 5;
 
   const int home = blockIdx.x % kNumQueues;
   const int nkv = a.B * a.Hkv;
@@ -502,7 +501,6 @@ prefill_balanced_kernel(PrefillArgs a) {
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int j = lane & 31;
-  const int h2 = lane >> 5;
 
   const int g = blockIdx.x;
   const int s = g % a.nsl;
@@ -559,7 +557,6 @@ prefill_pair_kernel(PrefillArgs a) {
   const int w = __builtin_amdgcn_readfirstlane((tid % C::NT) >> 6);
   const int lane = tid & 63;
   const int j = lane & 31;
-  const int h2 = lane >> 5;
 
   const int g = blockIdx.x;
   const int s = g % a.nsl;
@@ -731,6 +728,108 @@ __global__ void __launch_bounds__(64 * C::DB) prefill_merge_kernel(PrefillArgs a
   const float lsum = halves_sum(l);
   if (col.valid)
     store_out_block<T, C>(reinterpret_cast<T*>(a.o) + col.row_off, acc[0], 1.0f / lsum, db, h2);
+}
+
+// Key-split schedule for few units: one 8-wave workgroup per 64-column unit,
+// as NG = 4 groups of two waves.  Group q runs the q-th quarter of the unit's
+// key tiles on an LDS ring of its own; groups 1..3 then hand their states
+// (m, l, unnormalised O) to group 0 through LDS, which merges the four in
+// group order and stores the rows.  No partial state leaves the workgroup,
+// so there is no merge pass.  Unit i / 8-th of the list runs on the XCD
+// that takes block i mod 8 (when T is a multiple of 8), so the units of one
+// K/V head share one L2.
+template <typename T, class C, bool CAUSAL>
+__global__ void __launch_bounds__(4 * C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+prefill_quad_kernel(PrefillArgs a) {
+  static_assert(C::NW == 2, "quad groups are two waves");
+  constexpr int NG = 4;
+  __shared__ __attribute__((aligned(16))) char smem[NG * 2 * C::STAGE_BYTES];
+  // hand-over block of one wave: DB*4 rows of 64 float4 (the accumulator),
+  // then 64 float2 (m, l); consecutive lanes on consecutive 16-byte words
+  constexpr int HAND_BYTES = (C::DB * 16 + 2) * 64 * 4;
+  constexpr int STAGE_OFF = (NG - 1) * C::NW * HAND_BYTES;
+  static_assert(STAGE_OFF + C::NW * stage_out_bytes<C>() <= NG * 2 * C::STAGE_BYTES,
+                "hand-over and output staging exceed the rings");
+
+  const int tid = threadIdx.x;
+  // wave-uniform; readfirstlane keeps what derives from them scalar
+  const int grp = __builtin_amdgcn_readfirstlane(tid / C::NT);
+  const int w = __builtin_amdgcn_readfirstlane((tid % C::NT) >> 6);
+  const int lane = tid & 63;
+  const int j = lane & 31;
+
+  const int i = blockIdx.x;
+  const int t = (a.T % 8 == 0) ? (i % 8) * (a.T / 8) + i / 8 : i;
+  const int qb = t % a.NQB;
+  const int rest = t / a.NQB;
+  const int hb = rest % a.HB;
+  const int kvg = rest / a.HB;
+  const int hkv = kvg % a.Hkv;
+  const int b = kvg / a.Hkv;
+
+  const int n = unit_tiles<C, CAUSAL>(a, qb);  // >= 1
+  const int q0 = n * grp / NG;
+  const int nt = n * (grp + 1) / NG - q0;
+  const int steps = (n + NG - 1) / NG;  // the longest group range
+  const int rot = nt > 0 ? (int)((7u * (unsigned)t + 3u * (unsigned)grp) % (unsigned)nt) : 0;
+  const SegTiles st{min(q0, n - 1), nt, rot};
+  const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
+
+  SegIn<C> in;
+  seg_begin<T, C>(a, in, b, hkv, st, col);
+  float mrun, lrun;
+  f32x16 acc[C::DB];
+  seg_run<T, C, CAUSAL, true>(a, smem + grp * 2 * C::STAGE_BYTES, in, b, hkv, qb, st, col,
+                              mrun, lrun, acc, steps);
+  // seg_run ends on a barrier: every ring is free
+  if (grp > 0) {
+    char* hand = smem + ((grp - 1) * C::NW + w) * HAND_BYTES;
+    float4* hand4 = reinterpret_cast<float4*>(hand) + lane;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        hand4[(db * 4 + r4) * 64] = make_float4(acc[db][4 * r4], acc[db][4 * r4 + 1],
+                                                acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]);
+    reinterpret_cast<float2*>(hand + C::DB * 4 * 64 * 16)[lane] = make_float2(mrun, lrun);
+  }
+  __syncthreads();
+  if (grp == 0) {
+    float2 ml[NG - 1];
+#pragma unroll
+    for (int q = 1; q < NG; ++q)
+      ml[q - 1] = reinterpret_cast<const float2*>(smem + ((q - 1) * C::NW + w) * HAND_BYTES +
+                                                  C::DB * 4 * 64 * 16)[lane];
+    float M = mrun;
+#pragma unroll
+    for (int q = 1; q < NG; ++q) M = fmaxf(M, ml[q - 1].x);
+    // a state whose keys were all masked (m = -inf) has nothing to add
+    const float w0 = mrun == kNegInf ? 0.f : fast_exp2((mrun - M) * a.c);
+    float l = w0 * lrun;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= w0;
+#pragma unroll
+    for (int q = 1; q < NG; ++q) {
+      const float wq = ml[q - 1].x == kNegInf ? 0.f : fast_exp2((ml[q - 1].x - M) * a.c);
+      l += wq * ml[q - 1].y;
+      const float4* h4 =
+          reinterpret_cast<const float4*>(smem + ((q - 1) * C::NW + w) * HAND_BYTES) + lane;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 o = h4[(db * 4 + r4) * 64];
+          acc[db][4 * r4] += wq * o.x;
+          acc[db][4 * r4 + 1] += wq * o.y;
+          acc[db][4 * r4 + 2] += wq * o.z;
+          acc[db][4 * r4 + 3] += wq * o.w;
+        }
+    }
+    finish_rows<T, C>(a, smem + STAGE_OFF + w * stage_out_bytes<C>(), l, acc, b, hkv, hb, qb,
+                      w);
+  }
 }
 
 }  // namespace gqa

@@ -311,6 +311,26 @@ def test_pair_schedule_sampled(s):
 # (sampled rows) sized so the persistent (many units), pair (causal, at least
 # one unit pair per CU) and balanced (few units) schedules all run.
 
+# Shapes with fewer 128-column units than CUs but 192-256 64-column units of
+# >= 8 key tiles: on a 256-CU MI355X they run on the quad schedule (one
+# 8-wave workgroup per 64-column unit, keys split four ways, merged in LDS).
+QUAD_SHAPES = [
+    FwdShape(2, 32, 8, 256, 1024, 128, True, 768),
+    FwdShape(2, 32, 8, 256, 600, 64, True, 344, torch.float32),
+    FwdShape(1, 32, 1, 400, 600, 64, False, 0),
+    FwdShape(1, 160, 1, 70, 570, 64, True, 500),
+    FwdShape(2, 16, 4, 512, 1024, 32, True, 512),
+]
+
+
+@pytest.mark.parametrize("s", QUAD_SHAPES, ids=["gqa_d128_offset", "f32_d64_offset", "mqa_g32",
+                                                "g160_three_head_blocks", "d32_offset"])
+def test_quad_schedule(s):
+    q, k, v, out = _check_fwd(s, 13, rows=800)
+    again = _fwd_gpu(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale)
+    assert torch.equal(out, again), "quad schedule not bitwise reproducible"
+
+
 def _random_shapes():
     rng = np.random.default_rng(2024)
     shapes = []
