@@ -193,15 +193,18 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// grid (Hq, B), 256 threads.  Every partial of the row is read in parallel:
-// first the split maxima (one per thread), then the accumulators, with
-// thread t taking 16-byte chunk t % (D/4) of the splits s = t / (D/4) mod G;
-// the G group sums are added through LDS in fixed order.
+// grid (Hq, B), 256 threads.  Thread t takes 16-byte chunk t % (D/4) of
+// the splits s = t / (D/4) (mod G).  When every thread has at most SPT
+// splits (the common case) it loads their maxima, sums and chunks in one
+// memory round trip and keeps them in registers; otherwise the maxima are
+// read first and the chunks in a second pass.  The G group sums are added
+// through LDS in fixed order.
 template <typename T, int D, bool APPEND>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
   constexpr int REC = D + 4;    // floats per partial record
   constexpr int CH = D / 4;     // float4 chunks per record
   constexpr int G = 256 / CH;   // split groups
+  constexpr int SPT = 4;        // splits per thread held in registers
   constexpr bool F32 = std::is_same<T, float>::value;
   __shared__ float s_red[4];
   __shared__ float4 s_acc[G][CH];
@@ -221,31 +224,66 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
   }
   const int ns = (n + a.S_TOK - 1) / a.S_TOK;
   const float* part = a.ws + ((size_t)b * a.Hq + h) * a.NS * REC;
-
-  // ---- M = max over splits of the scaled maxima
-  float mloc = kNegInf;
-  for (int s = tid; s < ns; s += 256) mloc = fmaxf(mloc, part[(size_t)s * REC + D]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-  if ((tid & 63) == 0) s_red[tid >> 6] = mloc;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-
-  // ---- weighted sums, G split groups in parallel
   const int c = tid % CH;
   const int grp = tid / CH;
+
+  // ---- M = max over splits of the scaled maxima (block-wide)
+  auto block_max = [&](float mloc) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+    if ((tid & 63) == 0) s_red[tid >> 6] = mloc;
+    __syncthreads();
+    return fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  };
+
   float4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
+  if (ns <= SPT * G) {
+    // one round trip: everything this thread needs, then the reductions
+    float m[SPT], l[SPT];
+    float4 v[SPT];
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int s = grp + k * G;
+      m[k] = kNegInf;
+      l[k] = 0.f;
+      v[k] = float4{0.f, 0.f, 0.f, 0.f};
+      if (s < ns) {
+        const float* ps = part + (size_t)s * REC;
+        v[k] = *reinterpret_cast<const float4*>(ps + 4 * c);
+        m[k] = ps[D];
+        l[k] = ps[D + 1];
+      }
+    }
+    float mloc = m[0];
+#pragma unroll
+    for (int k = 1; k < SPT; ++k) mloc = fmaxf(mloc, m[k]);
+    const float M = block_max(mloc);
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      // absent splits (m = -inf) weigh exactly 0
+      const float wgt = fast_exp2(m[k] - M);
+      acc.x += wgt * v[k].x;
+      acc.y += wgt * v[k].y;
+      acc.z += wgt * v[k].z;
+      acc.w += wgt * v[k].w;
+      L += wgt * l[k];
+    }
+  } else {
+    float mloc = kNegInf;
+    for (int s = tid; s < ns; s += 256) mloc = fmaxf(mloc, part[(size_t)s * REC + D]);
+    const float M = block_max(mloc);
 #pragma unroll 4
-  for (int s = grp; s < ns; s += G) {
-    const float* ps = part + (size_t)s * REC;
-    const float wgt = fast_exp2(ps[D] - M);
-    const float4 v = *reinterpret_cast<const float4*>(ps + 4 * c);
-    acc.x += wgt * v.x;
-    acc.y += wgt * v.y;
-    acc.z += wgt * v.z;
-    acc.w += wgt * v.w;
-    L += wgt * ps[D + 1];
+    for (int s = grp; s < ns; s += G) {
+      const float* ps = part + (size_t)s * REC;
+      const float wgt = fast_exp2(ps[D] - M);
+      const float4 v = *reinterpret_cast<const float4*>(ps + 4 * c);
+      acc.x += wgt * v.x;
+      acc.y += wgt * v.y;
+      acc.z += wgt * v.z;
+      acc.w += wgt * v.w;
+      L += wgt * ps[D + 1];
+    }
   }
   s_acc[grp][c] = acc;
   if (c == 0) s_l[grp] = L;
