@@ -216,21 +216,39 @@ def test_output_guard_bands_untouched():
     assert _err(out, ref) <= 2e-2
 
 
-def test_bitwise_deterministic_runs():
-    """The atomic scheduler only changes which workgroup runs a unit; each
-    output's arithmetic order is fixed, so repeated runs agree bit for bit."""
-    s = WORKLOADS["llama3_8b_prefill"].fwd[0]
+@pytest.mark.parametrize("name,variant", [("llama3_8b_prefill", 0), ("mha_gqa_mqa_sweep", 1),
+                                          ("chunked_prefill_4k", 0)],
+                         ids=["pair", "persistent_atomic", "quad"])
+def test_bitwise_deterministic_runs(name, variant):
+    """Each output's arithmetic order is fixed -- the persistent schedule's
+    atomics only change which workgroup runs a unit, and every merge runs in
+    a fixed order -- so 20 repeated runs agree bit for bit, on each schedule
+    the named workloads use."""
+    s = WORKLOADS[name].fwd[variant]
     q, k, v = (t.to(DEV) for t in fwd_inputs(s, 0))
-    first = attn_fwd(q, k, v, causal=True)
-    for _ in range(10):
-        again = attn_fwd(q, k, v, causal=True)
+    first = attn_fwd(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale)
+    for _ in range(20):
+        again = attn_fwd(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale)
         assert torch.equal(first, again)
+    torch.cuda.synchronize()
+
+
+def test_decode_bitwise_deterministic_runs():
     ds = WORKLOADS["kv_decode_b8"].decode
     dq, dk, dv, dl = (t.to(DEV) for t in decode_inputs(ds, 0))
     d1 = attn_decode(dq, dk, dv, dl)
-    for _ in range(10):
+    for _ in range(20):
         assert torch.equal(d1, attn_decode(dq, dk, dv, dl))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n", [127, 1000])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_ragged_tails(n, causal):
+    """Sequence lengths one short of a tile multiple and far from one."""
+    for d, dtype in ((128, torch.bfloat16), (64, torch.bfloat16), (32, torch.float32)):
+        s = FwdShape(1, 8, 2, n, n, d, causal, 0, dtype)
+        _check_fwd(s, 40 + d, rows=None if n < 500 else 400)
 
 
 def test_two_streams_keep_separate_schedulers():
