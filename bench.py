@@ -242,6 +242,78 @@ def time_append_workload(s, steps, warmup):
     return float(np.mean([a.elapsed_time(b) for a, b in ev])), pos_h.tolist()
 
 
+# Supplementary decode sweep: the batch-8 shape (Hq 12, Hkv 2, d 128) at more
+# rows and longer contexts, lengths uniform in [Smax/4, Smax] as for the
+# batch-8 workload's [512, 2048].  It shows how close the decode kernels come
+# to HBM bandwidth once a call moves enough bytes to hide launch and latency.
+DECODE_SWEEP = [(b, smax) for smax in (2048, 8192) for b in (8, 32, 128)]
+SWEEP_COLD_BYTES = 768 * 1024 * 1024  # caches cycled per sweep point (> Infinity Cache)
+
+
+def time_decode_sweep(steps, warmup):
+    """Event-timed decode calls at each DECODE_SWEEP point, HBM-cold caches.
+
+    Inputs are N(0,1) bf16 drawn on the GPU from a seeded generator, lengths
+    from a seeded CPU generator.  Before timing, rows 0 and B-1 of the first
+    call are checked against the oracle."""
+    import numpy as np
+    import torch
+
+    import oracle  # test infrastructure: parity gate only
+    from mqa_flashattention_amd import attn_decode, decode_workspace_bytes
+    from mqa_flashattention_amd.workloads import DecodeShape
+
+    dev = torch.device("cuda:0")
+    out = {}
+    for B, smax in DECODE_SWEEP:
+        s = DecodeShape(B, 12, 2, smax, 128, smax // 4, smax)
+        gen = torch.Generator(device=dev).manual_seed(100 + B + smax)
+        lens_h = torch.randint(s.len_lo, s.len_hi + 1, (B,),
+                               generator=torch.Generator().manual_seed(B + smax),
+                               dtype=torch.int64).to(torch.int32)
+        lens = lens_h.to(dev)
+        q = torch.randn((B, s.Hq, s.d), generator=gen, device=dev).to(torch.bfloat16)
+        shape = (B, s.Hkv, smax, s.d)
+        set_bytes = 2 * B * s.Hkv * smax * s.d * 2
+        nsets = max(2, -(-SWEEP_COLD_BYTES // set_bytes))
+        kcs = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+               for _ in range(nsets)]
+        vcs = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+               for _ in range(nsets)]
+        o = torch.empty_like(q)
+        ws = torch.empty(decode_workspace_bytes(B, s.Hq, s.Hkv, smax, s.d), dtype=torch.uint8,
+                         device=dev)
+        attn_decode(q, kcs[0], vcs[0], lens, scale=s.scale, out=o, workspace=ws)
+        torch.cuda.synchronize()
+        for r in sorted({0, B - 1}):
+            ref = oracle.attn_decode(q[r:r + 1].cpu(), kcs[0][r:r + 1].cpu(),
+                                     vcs[0][r:r + 1].cpu(), lens_h[r:r + 1], scale=s.scale)
+            check(o[r:r + 1], ref, 2e-2, f"decode sweep B{B} Smax{smax} row {r}")
+        for i in range(warmup):
+            attn_decode(q, kcs[i % nsets], vcs[i % nsets], lens, scale=s.scale, out=o,
+                        workspace=ws)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        head_start(steps)
+        for i in range(steps):
+            ev[i][0].record()
+            attn_decode(q, kcs[(i + 1) % nsets], vcs[(i + 1) % nsets], lens, scale=s.scale,
+                        out=o, workspace=ws)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        nbytes = decode_bytes(s, lens_h.tolist())
+        gb = nbytes / (ms * 1e-3) / 1e9
+        out[f"decode_sweep[B={B},Smax={smax}]"] = {
+            "ms": round(ms, 5), "value": round(gb, 1), "unit": "GB/s",
+            "frac_hbm_peak": round(gb / PEAK_HBM_GBPS, 4),
+            "algorithmic_mb": round(nbytes / 1e6, 3), "cache_sets": nsets}
+        del kcs, vcs, q, o, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -427,6 +499,7 @@ def main(argv=None):
             "frac_hbm_peak": round(gb / PEAK_HBM_GBPS, 4),
             "algorithmic_mb": round(append_bytes(sa, positions) / 1e6, 4),
             "note": "store of the new K/V rows + split + combine, one call, HBM-cold caches"}
+        extra.update(time_decode_sweep(20, 3))
         result["other_workloads"] = extra
 
     print(json.dumps(result), flush=True)

@@ -195,16 +195,16 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
 
 // grid (Hq, B), 256 threads.  Thread t takes 16-byte chunk t % (D/4) of
 // the splits s = t / (D/4) (mod G).  When every thread has at most SPT
-// splits (the common case) it loads their maxima, sums and chunks in one
-// memory round trip and keeps them in registers; otherwise the maxima are
-// read first and the chunks in a second pass.  The G group sums are added
-// through LDS in fixed order.
+// splits (at d = 128: rows of up to 8 x 8 = 64 splits) it loads their
+// maxima, sums and chunks in one memory round trip and keeps them in
+// registers; otherwise the maxima are read first and the chunks in a second
+// pass.  The G group sums are added through LDS in fixed order.
 template <typename T, int D, bool APPEND>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeArgs a) {
   constexpr int REC = D + 4;    // floats per partial record
   constexpr int CH = D / 4;     // float4 chunks per record
   constexpr int G = 256 / CH;   // split groups
-  constexpr int SPT = 4;        // splits per thread held in registers
+  constexpr int SPT = 8;        // splits per thread held in registers
   constexpr bool F32 = std::is_same<T, float>::value;
   __shared__ float s_red[4];
   __shared__ float4 s_acc[G][CH];

@@ -377,12 +377,15 @@ using DecCfgBf16 = gqa::TileCfg<uint16_t, D, 32, 1>;
 template <int D>
 using DecCfgF32 = gqa::TileCfg<float, D, 32, 1>;
 
-// Tokens per split: enough splits to put about two waves on every CU when
-// every row is full, in whole 32-token tiles.
+// Tokens per split: enough splits to put one wave on every SIMD (four per
+// CU) when every row is full, in whole 32-token tiles.  The split kernel's
+// registers allow one resident wave per SIMD; more, shorter splits only run
+// in a second round (measured slower from batch 32 up, as were two waves
+// per CU).
 int decode_split_tokens(int B, int Hkv, int ncb, int smax, int cus) {
   const long long tiles_per_row = (smax + 31) / 32;
   const long long heads = (long long)B * Hkv * ncb;
-  const long long target = 2LL * cus;
+  const long long target = 4LL * cus;
   long long tiles_per_split = (heads * tiles_per_row + target - 1) / target;
   if (tiles_per_split < 1) tiles_per_split = 1;
   if (tiles_per_split > tiles_per_row) tiles_per_split = tiles_per_row;

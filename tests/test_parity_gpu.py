@@ -172,6 +172,60 @@ def test_decode_matches_single_query_forward():
         assert float((f[0, :, 0].double() - dec[b]).abs().max()) <= 2e-2
 
 
+# Decode shapes large enough for splits of several 32-token tiles and many
+# splits per row, with lengths on and around tile and split boundaries.
+@pytest.mark.parametrize("B,Hq,Hkv,Smax,d,dtype", [
+    (24, 12, 2, 2048, 128, torch.bfloat16),
+    (64, 8, 1, 4096, 64, torch.bfloat16),
+    (16, 40, 1, 2048, 32, torch.float32),     # two 32-head column blocks
+], ids=["b24_d128", "b64_d64", "b16_g40_f32"])
+def test_decode_multi_tile_splits(B, Hq, Hkv, Smax, d, dtype):
+    g = torch.Generator().manual_seed(B + Smax + d)
+    special = [1, 31, 32, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513, Smax - 1, Smax]
+    lens = torch.randint(1, Smax + 1, (B,), generator=g, dtype=torch.int32)
+    lens[:len(special)] = torch.tensor(special[:B], dtype=torch.int32)
+    q = random_tensor((B, Hq, d), 91, dtype)
+    kc = random_tensor((B, Hkv, Smax, d), 92, dtype)
+    vc = random_tensor((B, Hkv, Smax, d), 93, dtype)
+    out = attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), lens.to(DEV))
+    torch.cuda.synchronize()
+    assert _err(out, oracle.attn_decode(q, kc, vc, lens)) <= TOL[dtype]
+
+
+def test_decode_across_sizes_and_streams():
+    """Calls of growing and shrinking row counts on one stream, then the same
+    inputs on two streams: every output equals the first call's, bit for bit."""
+    cases = []
+    for B, Smax in ((2, 600), (40, 1500), (3, 600)):
+        s = DecodeShape(B, 12, 2, Smax, 128, 1, Smax)
+        q, kc, vc, lens = decode_inputs(s, 30 + B)
+        dev = tuple(t.to(DEV) for t in (q, kc, vc, lens))
+        out = attn_decode(*dev)
+        torch.cuda.synchronize()
+        assert _err(out, oracle.attn_decode(q, kc, vc, lens)) <= 2e-2
+        cases.append((dev, out))
+    for dev, out in cases:
+        assert torch.equal(attn_decode(*dev), out)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    res = []
+    for st in (s1, s2):
+        with torch.cuda.stream(st):
+            res.append([attn_decode(*dev) for dev, _ in cases for _ in range(2)])
+    torch.cuda.synchronize()
+    for group in res:
+        for i, o in enumerate(group):
+            assert torch.equal(o, cases[i // 2][1])
+
+
+def test_decode_bitwise_deterministic_many_splits():
+    s = DecodeShape(24, 12, 2, 2048, 128, 1, 2048)
+    dq, dk, dv, dl = (t.to(DEV) for t in decode_inputs(s, 5))
+    d1 = attn_decode(dq, dk, dv, dl)
+    for _ in range(20):
+        assert torch.equal(d1, attn_decode(dq, dk, dv, dl))
+    torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------- properties / edge cases
 
 def test_causal_row0_and_constant_v_exact():
