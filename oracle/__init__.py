@@ -18,7 +18,9 @@ GQA Flash Attention"), evaluated as max / exp-sum / weighted sum per row.  The d
 append first writes each active row's new K/V rows at its position (the
 single-launch K/V store and per-row position table of the microLLM-rocm
 optimization log, experiments 025, 083/084 and 098) and then attends slots
-[0, position].
+[0, position].  The backward gives dQ, dK, dV of a loss with dL/dO given,
+the K/V gradients reduced over each K/V head's query heads (microLLM-rocm
+optimization log, experiments 044 and 051-054).
 
 Parity status: pinned (see tests/test_oracle.py -- library attention routine
 on random shapes, closed forms, invariants, and planted-mistake checks).
@@ -78,8 +80,11 @@ def load(path: str = LIBRARY, build_if_missing: bool = True) -> ctypes.CDLL:
         lib.oracle_attn_decode_append.argtypes = [_dp, _dp, _dp, _dp, _dp,
                                                   ctypes.POINTER(ctypes.c_int32), _dp,
                                                   _lp, _lp, _lp, _lp, _lp, ctypes.c_double]
+        lib.oracle_attn_bwd.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _lp, _lp, _lp, _lp,
+                                        _lp, _lp, ctypes.c_int, _lp, ctypes.c_double]
         for name in ("oracle_attn_fwd", "oracle_attn_fwd_rows", "oracle_attn_probs",
-                     "oracle_attn_decode", "oracle_attn_decode_append", "oracle_num_threads"):
+                     "oracle_attn_decode", "oracle_attn_decode_append", "oracle_attn_bwd",
+                     "oracle_num_threads"):
             getattr(lib, name).restype = ctypes.c_int
         _libs[path] = lib
         return lib
@@ -196,6 +201,26 @@ def attn_decode_append(q, k_new, v_new, kcache, vcache, positions, *,
                                          _ptr(o), B, Hq, Hkv, Smax, d, float(scale)),
            "attn_decode_append")
     return o, kc, vc
+
+
+def attn_bwd(q, k, v, dout, *, causal: bool = False, q_offset: int = 0,
+             scale: float | None = None, lib: ctypes.CDLL | None = None):
+    """(dQ, dK, dV) as float64 for a loss with dL/dO = dout: dQ has the shape
+    of q [B,Hq,Nq,d]; dK, dV that of k and v [B,Hkv,Nk,d], each summed over
+    the query heads that share the K/V head."""
+    lib = lib or load()
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if do.shape != q.shape:
+        raise ValueError("attn_bwd: dout must have the shape of q")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    _check(lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk),
+                               _ptr(dv), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                               int(q_offset), float(scale)), "attn_bwd")
+    return dq, dk, dv
 
 
 def num_threads(lib: ctypes.CDLL | None = None) -> int:

@@ -44,6 +44,10 @@
  *   then the row attends slots [0, pos]; rows with pos outside [0, Smax) are
  *   inactive (no write, zero output).  Sources at that function.
  *
+ *   Backward (oracle_attn_bwd): dQ, dK, dV of a loss with dL/dO given, the
+ *   K/V gradients summed over the query heads of each K/V head.  Formulas
+ *   and sources at that function.
+ *
  * Inputs are the exact values the GPU consumes, widened to double by the
  * caller (fp32 as is, bf16 by appending 16 zero bits).  Layout is contiguous
  * row-major: q,o [B,Hq,Nq,d]; k,v [B,Hkv,Nk,d]; caches [B,Hkv,Smax,d].
@@ -305,6 +309,102 @@ int oracle_attn_decode_append(const double* q, const double* knew, const double*
   const int rc = oracle_attn_decode(q, kc, vc, lens, o, B, Hq, Hkv, Smax, d, scale);
   free(lens);
   return rc;
+}
+
+/*
+ * Backward of the forward definition, for a scalar loss L whose gradient
+ * with respect to O is dout (layout of o).
+ *
+ * Source: the microLLM-rocm optimization log, experiments 044 and 051-054:
+ * one forward/backward boundary for QK, causal softmax, PV and the GQA head
+ * mapping, with K/V heads never copied; the backward recomputes each row's
+ * probabilities and reduces the K/V gradients over the query heads that
+ * share a K/V head (first with atomics, exp. 051; then as an explicit
+ * reduction, exps. 052/054).  The formulas are the chain rule through the
+ * definition above, for query head h, K/V head hk = h / g and visible keys
+ * J of row i:
+ *
+ *   P_ij  = softmax over J of s_ij            (the forward's weights)
+ *   dP_ij = sum_c dout[b,h,i,c] * v[b,hk,j,c]
+ *   D_i   = sum_{j in J} P_ij * dP_ij
+ *   dS_ij = P_ij * (dP_ij - D_i)              (softmax Jacobian)
+ *   dq[b,h,i,:]  = scale * sum_{j in J} dS_ij * k[b,hk,j,:]
+ *   dk[b,hk,j,:] = scale * sum over h with h / g = hk, rows i: dS_ij * q[b,h,i,:]
+ *   dv[b,hk,j,:] =         sum over h with h / g = hk, rows i: P_ij * dout[b,h,i,:]
+ *
+ * Masked keys get no gradient.  Each (b, hk) is one task (its g query heads
+ * in ascending order, rows ascending), so every sum has a fixed order.
+ * dq has the layout of q, dk and dv that of k and v.
+ */
+int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
+                    double* dq, double* dk, double* dv,
+                    long B, long Hq, long Hkv, long Nq, long Nk, long d,
+                    int causal, long q_offset, double scale) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
+  if (check_shapes(B, Hq, Hkv, Nq, Nk, d)) return -1;
+  if (causal && q_offset < 0) return -1;
+  const long g = Hq / Hkv;
+  const long tasks = B * Hkv;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* scores = (double*)malloc(sizeof(double) * (size_t)Nk);
+    double* probs = (double*)malloc(sizeof(double) * (size_t)Nk);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)Nk);
+    double* orow = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!scores || !probs || !dp || !orow) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long t = 0; t < tasks; ++t) {
+        const long b = t / Hkv;
+        const long hk = t % Hkv;
+        const double* kbase = k + (b * Hkv + hk) * Nk * d;
+        const double* vbase = v + (b * Hkv + hk) * Nk * d;
+        double* dkbase = dk + (b * Hkv + hk) * Nk * d;
+        double* dvbase = dv + (b * Hkv + hk) * Nk * d;
+        for (long x = 0; x < Nk * d; ++x) {
+          dkbase[x] = 0.0;
+          dvbase[x] = 0.0;
+        }
+        for (long r = 0; r < g; ++r) {
+          const long h = hk * g + r;
+          for (long i = 0; i < Nq; ++i) {
+            const long row = (b * Hq + h) * Nq + i;
+            const double* qrow = q + row * d;
+            const double* dorow = dout + row * d;
+            double* dqrow = dq + row * d;
+            attend_row(q, k, v, B, Hq, Hkv, Nq, Nk, d, causal, q_offset, scale, b, h, i,
+                       scores, orow, probs);
+            long last = Nk - 1;
+            if (causal && q_offset + i < last) last = q_offset + i;
+            double D = 0.0;
+            for (long j = 0; j <= last; ++j) {
+              double dot = 0.0;
+              for (long c = 0; c < d; ++c) dot += dorow[c] * vbase[j * d + c];
+              dp[j] = dot;
+              D += probs[j] * dot;
+            }
+            for (long c = 0; c < d; ++c) dqrow[c] = 0.0;
+            for (long j = 0; j <= last; ++j) {
+              const double ds = probs[j] * (dp[j] - D);
+              for (long c = 0; c < d; ++c) {
+                dqrow[c] += scale * ds * kbase[j * d + c];
+                dkbase[j * d + c] += scale * ds * qrow[c];
+                dvbase[j * d + c] += probs[j] * dorow[c];
+              }
+            }
+          }
+        }
+      }
+    }
+    free(scores);
+    free(probs);
+    free(dp);
+    free(orow);
+  }
+  return failed ? -2 : 0;
 }
 
 /* Number of OpenMP threads a parallel region would use (for reporting). */

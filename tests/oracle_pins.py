@@ -10,7 +10,10 @@ Used two ways:
 What pins what (each pin names the passage or mathematical fact it rests on):
   library    -- torch's scaled_dot_product_attention in fp64 on the CPU, with
                 K/V heads replicated by repeat_interleave; for q_offset = 0 its
-                own is_causal mask (top-left aligned) is used.
+                own is_causal mask (top-left aligned) is used.  For the
+                backward, torch autograd through the same routine.
+  finite differences -- the backward against central differences of the
+                (separately pinned) forward.
   closed forms and invariants -- see each function's docstring.
 Inputs are numpy/torch draws with fixed seeds; nothing comes from the GPU.
 """
@@ -374,6 +377,122 @@ def pin_append_equal_keys_mean(lib):
             assert _maxerr(o[b, h], ref) <= 1e-12, f"row {b} head {h}"
 
 
+# --------------------------------------------------------------------------- backward
+
+def _sdpa_grads(q, k, v, dout, causal, q_offset, scale):
+    """dQ, dK, dV by torch autograd (fp64) through its attention routine, K/V
+    heads replicated by repeat_interleave -- whose own backward sums the
+    replicas' gradients, i.e. the reduction over each K/V head's query heads."""
+    import torch
+    import torch.nn.functional as F
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)).requires_grad_(True)
+                  for x in (q, k, v))
+    g = qt.shape[1] // kt.shape[1]
+    kr, vr = kt.repeat_interleave(g, dim=1), vt.repeat_interleave(g, dim=1)
+    Nq, Nk = qt.shape[2], kt.shape[2]
+    mask = None
+    if causal:
+        i = torch.arange(Nq)[:, None]
+        j = torch.arange(Nk)[None, :]
+        mask = j <= q_offset + i
+    out = F.scaled_dot_product_attention(qt, kr, vr, attn_mask=mask, scale=scale)
+    out.backward(torch.from_numpy(np.ascontiguousarray(dout)))
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def pin_bwd_library(lib):
+    """dQ, dK, dV vs torch autograd through its attention routine (fp64) on
+    random tiny shapes: MHA, GQA, MQA, causal offsets 0 / 1 / Nk-Nq / past the end."""
+    cases = [(1, 2, 2, 5, 5, 4, False, 0), (2, 4, 2, 6, 9, 8, True, 3),
+             (1, 6, 1, 7, 7, 8, True, 0), (1, 4, 4, 3, 8, 4, True, 5),
+             (2, 8, 2, 4, 6, 4, True, 1), (1, 3, 1, 5, 4, 8, True, 9)]
+    for n, (B, Hq, Hkv, Nq, Nk, d, causal, off) in enumerate(cases):
+        q, k, v = _case(600 + n, B, Hq, Hkv, Nq, Nk, d)
+        do = _rand(q.shape, 700 + n)
+        sc = 0.7 / math.sqrt(d)
+        got = oracle.attn_bwd(q, k, v, do, causal=causal, q_offset=off, scale=sc, lib=lib)
+        want = _sdpa_grads(q, k, v, do, causal, off, sc)
+        for a, b_ in zip(got, want):
+            assert _maxerr(a, b_) <= 1e-11, (n, _maxerr(a, b_))
+
+
+def pin_bwd_finite_differences(lib):
+    """Each gradient vs central differences of L = sum(dout * O) computed with
+    the forward oracle (pinned on its own), at random coordinates of q, k, v."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 5, 7, 4
+    q, k, v = _case(810, B, Hq, Hkv, Nq, Nk, d)
+    do = _rand(q.shape, 811)
+    sc, off = 0.6, 2
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, causal=True, q_offset=off, scale=sc, lib=lib)
+
+    def loss(qq, kk, vv):
+        o = oracle.attn_fwd(qq, kk, vv, causal=True, q_offset=off, scale=sc, lib=lib)
+        return float(np.sum(do * o))
+
+    rng = np.random.default_rng(812)
+    h = 1e-5
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for _ in range(8):
+            idx = tuple(int(rng.integers(0, n)) for n in grad.shape)
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += h
+            up = loss(*args)
+            args[which][idx] -= 2 * h
+            dn = loss(*args)
+            fd = (up - dn) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-8 * max(1.0, abs(fd)), (which, idx, fd, grad[idx])
+
+
+def pin_bwd_closed_forms(lib):
+    """Nk = 1: every weight is 1, so dQ = dK = 0 and dV = the sum of dout over
+    the group's heads and rows.  scale = 0: weights are uniform over the
+    visible keys, dQ = dK = 0 and dV[j] = sum over rows i seeing j of dout[i] / |J_i|."""
+    B, Hq, Hkv, Nq, d = 2, 6, 2, 4, 8
+    q, k, v = _case(820, B, Hq, Hkv, Nq, 1, d)
+    do = _rand(q.shape, 821)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, causal=False, scale=0.9, lib=lib)
+    g = Hq // Hkv
+    assert np.max(np.abs(dq)) <= TOL and np.max(np.abs(dk)) <= TOL
+    want = do.reshape(B, Hkv, g, Nq, d).sum(axis=(2, 3))[:, :, None, :]
+    assert _maxerr(dv, want) <= TOL
+    Nk, off = 6, 1
+    q, k, v = _case(822, B, Hq, Hkv, Nq, Nk, d)
+    do = _rand(q.shape, 823)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, causal=True, q_offset=off, scale=0.0, lib=lib)
+    assert np.max(np.abs(dq)) <= TOL and np.max(np.abs(dk)) <= TOL
+    want = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Nq):
+                n = min(Nk, off + i + 1)
+                want[b, h // g, :n] += do[b, h, i] / n
+    assert _maxerr(dv, want) <= TOL
+
+
+def pin_bwd_key_sum_zero(lib):
+    """Adding one vector to every key shifts a row's scores by a constant and
+    leaves O unchanged, so the key gradients of each K/V head sum to zero."""
+    q, k, v = _case(830, 2, 4, 2, 6, 9, 8)
+    do = _rand(q.shape, 831)
+    _, dk, _ = oracle.attn_bwd(q, k, v, do, causal=True, q_offset=2, scale=0.8, lib=lib)
+    assert np.max(np.abs(dk.sum(axis=2))) <= 1e-11
+
+
+def pin_bwd_gqa_equals_replicated_mha(lib):
+    """GQA backward = MHA backward on K/V heads replicated g times, with the
+    replicas' dK, dV summed back (and the same dQ)."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 6, 2, 5, 7, 4
+    q, k, v = _case(840, B, Hq, Hkv, Nq, Nk, d)
+    do = _rand(q.shape, 841)
+    g = Hq // Hkv
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, causal=True, q_offset=1, scale=0.5, lib=lib)
+    kr, vr = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    dq2, dk2, dv2 = oracle.attn_bwd(q, kr, vr, do, causal=True, q_offset=1, scale=0.5, lib=lib)
+    assert _maxerr(dq, dq2) <= TOL
+    assert _maxerr(dk, dk2.reshape(B, Hkv, g, Nk, d).sum(axis=2)) <= TOL
+    assert _maxerr(dv, dv2.reshape(B, Hkv, g, Nk, d).sum(axis=2)) <= TOL
+
+
 PINS = [
     pin_library_attention,
     pin_decode_library,
@@ -396,6 +515,11 @@ PINS = [
     pin_append_library,
     pin_append_first_slot,
     pin_append_equal_keys_mean,
+    pin_bwd_library,
+    pin_bwd_finite_differences,
+    pin_bwd_closed_forms,
+    pin_bwd_key_sum_zero,
+    pin_bwd_gqa_equals_replicated_mha,
 ]
 
 

@@ -135,6 +135,20 @@ MUTANTS = [
      "const double* ksrc = knew + b * Hkv * d;", 1),
     ("capacity boundary not checked", "const int active = pos >= 0 && pos < Smax;",
      "const int active = pos >= 0;", 1),
+    ("backward: D term dropped", "const double ds = probs[j] * (dp[j] - D);",
+     "const double ds = probs[j] * dp[j];", 1),
+    ("backward: softmax Jacobian sign flipped", "const double ds = probs[j] * (dp[j] - D);",
+     "const double ds = probs[j] * (D - dp[j]);", 1),
+    ("backward: dK scale dropped", "dkbase[j * d + c] += scale * ds * qrow[c];",
+     "dkbase[j * d + c] += ds * qrow[c];", 1),
+    ("backward: dQ from V instead of K", "dqrow[c] += scale * ds * kbase[j * d + c];",
+     "dqrow[c] += scale * ds * vbase[j * d + c];", 1),
+    ("backward: dV weighted by dS", "dvbase[j * d + c] += probs[j] * dorow[c];",
+     "dvbase[j * d + c] += ds * dorow[c];", 1),
+    ("backward: only the group's first head reduced", "for (long r = 0; r < g; ++r) {",
+     "for (long r = 0; r < 1; ++r) {", 1),
+    ("backward: dP from K", "for (long c = 0; c < d; ++c) dot += dorow[c] * vbase[j * d + c];",
+     "for (long c = 0; c < d; ++c) dot += dorow[c] * kbase[j * d + c];", 1),
 ]
 
 
