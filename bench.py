@@ -47,7 +47,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_llama3_8b_counters.json")
-KERNEL_SOURCES = ["attn_tile.hpp", "prefill_kernel.hpp", "decode_kernel.hpp", "gqa_attn.hip"]
+KERNEL_SOURCES = ["attn_tile.hpp", "prefill_kernel.hpp", "decode_kernel.hpp", "backward_kernel.hpp",
+                  "gqa_attn.hip"]
 DECODE_SETS = 48  # 48 x 16 MiB of caches > 256 MB Infinity Cache
 COPY_BYTES = 256 * 1024 * 1024  # calibration copy: reads and writes this many bytes
 

@@ -177,6 +177,44 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new,
                            int B, int Hq, int Hkv, int Smax, int d, float scale,
                            int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace gqa_attn_bwd needs: two fp32 values per query
+ * row (B * Hq * Nq rows).  Returns 0 for invalid sizes.
+ */
+size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Nq);
+
+/*
+ * Backward of gqa_attn_fwd: the gradients dq, dk, dv of a loss L given
+ * dout = dL/do, for the forward with the same q, k, v, causal, q_offset and
+ * scale, whose output o the caller passes back in.
+ *
+ *   q, o, dout, dq     : [B, Hq, Nq, d]
+ *   k, v, dk, dv       : [B, Hkv, Nk, d]   (same dtype for all; contiguous)
+ *
+ * With P the forward's softmax weights, dP = dout V^T, D = rowsum(dout o)
+ * and dS = P (dP - D):  dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dout,
+ * where dk and dv of K/V head hk are summed over its g query heads
+ * h = hk*g .. hk*g + g-1.  This is the backward boundary of the
+ * microLLM-rocm optimization log: experiment 044 (QK, causal softmax, PV
+ * and the GQA head mapping under one forward/backward boundary, no T x T
+ * probabilities kept, no K/V head copies) and experiments 051-054 (each
+ * row's probabilities recomputed; the K/V gradients reduced over the heads
+ * that share a K/V head -- here in registers, without atomics, so the
+ * result is run-to-run reproducible).
+ *
+ * workspace: device memory of at least gqa_attn_bwd_workspace_bytes(B, Hq,
+ * Nq) bytes, owned by the caller, contents on entry irrelevant; it receives
+ * each row's log-sum-exp and D.  scale must be finite and > 0
+ * (GQA_ERR_UNSUPPORTED otherwise).  Outputs must not alias inputs.  Other
+ * status codes and error behaviour as gqa_attn_fwd (plus GQA_ERR_WORKSPACE).
+ * Two launches on the stream: dq (with the row statistics), then dk and dv.
+ */
+int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 int causal, int q_offset, float scale,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static English name of a status code (never NULL). */
 const char* gqa_status_string(int status);
 

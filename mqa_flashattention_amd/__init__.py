@@ -10,8 +10,8 @@ has not been built.
 """
 from __future__ import annotations
 
-__all__ = ["attn_fwd", "attn_fwd_strided", "attn_decode", "attn_decode_append",
-           "decode_workspace_bytes", "library_path", "GqaError"]
+__all__ = ["attn_fwd", "attn_fwd_strided", "attn_decode", "attn_decode_append", "attn_bwd",
+           "decode_workspace_bytes", "bwd_workspace_bytes", "library_path", "GqaError"]
 
 
 def __getattr__(name):

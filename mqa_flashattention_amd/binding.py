@@ -27,8 +27,8 @@ STATUS_NAMES = {
     4: "GQA_ERR_UNSUPPORTED", 5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_NO_DEVICE", 7: "GQA_ERR_HIP",
 }
 EXPORTED = ("gqa_attn_fwd", "gqa_attn_fwd_strided", "gqa_attn_decode",
-            "gqa_attn_decode_append", "gqa_attn_decode_workspace_bytes", "gqa_status_string",
-            "gqa_last_error_string")
+            "gqa_attn_decode_append", "gqa_attn_decode_workspace_bytes", "gqa_attn_bwd",
+            "gqa_attn_bwd_workspace_bytes", "gqa_status_string", "gqa_last_error_string")
 
 
 class GqaError(RuntimeError):
@@ -57,6 +57,11 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp,
                                            sz, vp]
     lib.gqa_attn_decode_append.restype = i
+    lib.gqa_attn_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.gqa_attn_bwd_workspace_bytes.restype = sz
+    lib.gqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp,
+                                 sz, vp]
+    lib.gqa_attn_bwd.restype = i
     lib.gqa_status_string.argtypes = [i]
     lib.gqa_status_string.restype = ctypes.c_char_p
     lib.gqa_last_error_string.argtypes = []
@@ -170,6 +175,48 @@ def attn_fwd_strided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
                                       _stream_handle(dev))
     _raise(st)
     return out
+
+
+def bwd_workspace_bytes(B: int, Hq: int, Nq: int) -> int:
+    return int(lib.gqa_attn_bwd_workspace_bytes(B, Hq, Nq))
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+             dout: torch.Tensor, *, causal: bool = False, q_offset: int = 0,
+             scale: float | None = None, workspace: torch.Tensor | None = None):
+    """(dq, dk, dv) of a loss with dL/do = dout, via gqa_attn_bwd.
+
+    q, o, dout [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d]; all of one dtype,
+    contiguous, on one GPU; o is the output of attn_fwd on the same inputs and
+    options.  dk, dv are summed over the query heads of each K/V head.
+    scale defaults to 1/sqrt(d) and must be > 0."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, 4, q.dtype, dev)
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if k.shape[0] != B or k.shape[3] != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have the shape of q")
+    need = bwd_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the GPU of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(dev):
+        st = lib.gqa_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                              B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), int(q_offset),
+                              float(scale), _DTYPES[q.dtype], workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), _stream_handle(dev))
+    _raise(st)
+    return dq, dk, dv
 
 
 def decode_workspace_bytes(B: int, Hq: int, Hkv: int, Smax: int, d: int) -> int:

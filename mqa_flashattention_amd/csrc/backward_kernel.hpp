@@ -1,0 +1,283 @@
+// backward_kernel.hpp -- attention backward: dQ, dK, dV with the K/V
+// gradients reduced over the query heads of each K/V head.
+//
+// The backward boundary of the microLLM-rocm optimization log (experiment
+// 044: QK, causal softmax, PV and the GQA head mapping under one
+// forward/backward boundary, no T x T probabilities kept and no K/V head
+// copies; experiments 051-054: each row's probabilities recomputed, the K/V
+// gradients reduced over the heads sharing a K/V head).  With row
+// statistics lse = m c + log2 l (base 2, scaled) and D = sum_c dO O:
+//
+//   P  = 2^(S c - lse)          dP = dO V^T          dS = P (dP - D)
+//   dQ = scale dS K             dK = scale dS^T Q    dV = P^T dO
+//
+// Two kernels, both on the forward's MFMA tile code with the operands
+// swapped around, no atomics, fixed summation order:
+//  * bwd_dq_kernel: one 128-column unit of query rows (the forward's units:
+//    the group's heads stacked over positions).  Pass 1 over the unit's key
+//    tiles gives each row's lse; pass 2 forms dS^T = P^T (dP^T - D) from
+//    S^T = K Q^T and dP^T = V dO^T and accumulates dQ^T += K^T dS^T.  It
+//    writes lse and D of its rows for the second kernel.
+//  * bwd_dkdv_kernel: 32 keys per wave of one K/V head.  The wave walks
+//    the query tiles of every query head of the group (this is the GQA
+//    reduction, done in registers), with S = Q K^T and dP = dO V^T, and
+//    accumulates dV^T += dO^T P and dK^T += Q^T dS.
+// In both, a staged tile occupies two LDS stages: one holds the first
+// operand row-major (the A operand of S or S^T) with the second transposed,
+// the other the second operand row-major with the first transposed.
+#pragma once
+
+#include "prefill_kernel.hpp"
+
+namespace gqa {
+
+struct BwdArgs {
+  PrefillArgs f;  // shapes, contiguous strides, the dQ kernel's unit decomposition, c
+  const void* o;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* lse;  // [B][Hq][Nq]: m c + log2 l of each query row
+  float* dd;   // [B][Hq][Nq]: D = sum_c dO O
+  float scale;
+};
+
+// Sum over this lane's elements of x * y (two B-operand fragments of one
+// column); the other half-wave holds the rest of the row.
+template <class C>
+__device__ __forceinline__ float frag_dot(const typename C::Frag (&x)[C::QF],
+                                          const typename C::Frag (&y)[C::QF]) {
+  float s = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::QF; ++ks) {
+    if constexpr (C::F32) {
+      s += x[ks] * y[ks];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += (float)x[ks][e] * (float)y[ks][e];
+    }
+  }
+  return s;
+}
+
+// fp32 accumulator tile (16 values of one column per 32-row block) -> the
+// B-operand fragments of the second MFMA, rounded to bf16 in the bf16 path
+// (the packing of tile_weights).
+template <class C>
+__device__ __forceinline__ void to_frag(const f32x16 (&x)[C::KB],
+                                        typename C::Frag (&pf)[C::KB][C::PF]) {
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+    if constexpr (C::F32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pf[kb][r] = x[kb][r];
+    } else {
+#pragma unroll
+      for (int hk = 0; hk < 2; ++hk) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16(x[kb][8 * hk + 2 * e], x[kb][8 * hk + 2 * e + 1]);
+        pf[kb][hk] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  }
+}
+
+// grid (T), C::NT threads: unit t of the forward decomposition.
+template <typename T, class C, bool CAUSAL>
+__global__ void __launch_bounds__(C::NT) bwd_dq_kernel(BwdArgs ba) {
+  const PrefillArgs& a = ba.f;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+  T* const KsA = reinterpret_cast<T*>(smem);  // K row-major (V transposed, unused)
+  T* const VsA = KsA + C::K_ELEMS;
+  T* const KsB = reinterpret_cast<T*>(smem + C::STAGE_BYTES);  // V row-major
+  T* const VsB = KsB + C::K_ELEMS;                             // K transposed
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int j = lane & 31;
+  const int h2 = lane >> 5;
+
+  const int t = blockIdx.x;
+  const int qb = t % a.NQB;
+  const int rest = t / a.NQB;
+  const int hb = rest % a.HB;
+  const int kvg = rest / a.HB;
+  const int hkv = kvg % a.Hkv;
+  const int b = kvg / a.Hkv;
+  const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
+
+  typename C::Frag qf[C::QF], dof[C::QF], of[C::QF];
+  load_q_frag<T, C>(qf, reinterpret_cast<const T*>(a.q) + col.row_off, col.valid, false, h2);
+  load_q_frag<T, C>(dof, reinterpret_cast<const T*>(ba.dout) + col.row_off, col.valid, false,
+                    h2);
+  load_q_frag<T, C>(of, reinterpret_cast<const T*>(ba.o) + col.row_off, col.valid, false, h2);
+  const float Dv = halves_sum(frag_dot<C>(dof, of));
+
+  const T* kbase;
+  const T* vbase;
+  kv_bases<T, C>(a, b, hkv, kbase, vbase);
+  const int ntiles = unit_tiles<C, CAUSAL>(a, qb);
+  const int full_lim = CAUSAL ? min(a.Nk, a.q_offset + qb * a.R + 1) : a.Nk;
+  const int lim = (CAUSAL && col.valid) ? min(a.q_offset + col.i, a.Nk - 1) : a.Nk - 1;
+  const float c = a.c;
+
+  // ---- pass 1: row maxima and sums over the visible keys.  Key 0 is
+  // visible to every row, so the first tile makes m finite in every lane.
+  TileRegs<C> ra, rb;
+  float m = kNegInf, l = 0.f;
+  load_tile<T, C>(ra, kbase, vbase, 0, a.Nk, tid, a.kv_rowb);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    __syncthreads();
+    store_tile<T, C>(ra, KsA, VsA, tid);
+    __syncthreads();
+    if (kt + 1 < ntiles) load_tile<T, C>(ra, kbase, vbase, (kt + 1) * C::BC, a.Nk, tid, a.kv_rowb);
+    f32x16 s[C::KB];
+    qk_tile<T, C>(s, qf, KsA, j, h2);
+    const int key0 = kt * C::BC;
+    if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
+    const float mn = fmaxf(m, tile_rowmax<C>(s));
+    float lt = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lt += fast_exp2(__builtin_fmaf(s[kb][r], c, -mn * c));
+    l = l * fast_exp2((m - mn) * c) + lt;
+    m = mn;
+  }
+  const float lse = m * c + log2f(halves_sum(l));
+
+  // ---- pass 2: dQ^T += K^T dS^T over the same tiles
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  load_tile<T, C>(ra, kbase, vbase, 0, a.Nk, tid, a.kv_rowb);
+  load_tile<T, C>(rb, vbase, kbase, 0, a.Nk, tid, a.kv_rowb);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    __syncthreads();
+    store_tile<T, C>(ra, KsA, VsA, tid);
+    store_tile<T, C>(rb, KsB, VsB, tid);
+    __syncthreads();
+    if (kt + 1 < ntiles) {
+      load_tile<T, C>(ra, kbase, vbase, (kt + 1) * C::BC, a.Nk, tid, a.kv_rowb);
+      load_tile<T, C>(rb, vbase, kbase, (kt + 1) * C::BC, a.Nk, tid, a.kv_rowb);
+    }
+    f32x16 s[C::KB], dp[C::KB];
+    qk_tile<T, C>(s, qf, KsA, j, h2);    // S^T = K Q^T
+    qk_tile<T, C>(dp, dof, KsB, j, h2);  // dP^T = V dO^T
+    const int key0 = kt * C::BC;
+    if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse));  // masked: 0
+        s[kb][r] = p * (dp[kb][r] - Dv);
+      }
+    typename C::Frag dsf[C::KB][C::PF];
+    to_frag<C>(s, dsf);
+    pv_tile<T, C>(acc, dsf, VsB, j, h2);  // dQ^T += K^T dS^T
+  }
+
+  if (col.valid) {
+    store_out_row<T, C>(reinterpret_cast<T*>(ba.dq) + col.row_off, acc, ba.scale, h2);
+    if (h2 == 0) {
+      const size_t row = col.row_off / C::D;  // contiguous rows
+      ba.lse[row] = lse;
+      ba.dd[row] = Dv;
+    }
+  }
+}
+
+// grid (ceil(Nk / (32 NW)), Hkv, B), C::NT threads: wave w owns keys
+// k0 + 32 w .. k0 + 32 w + 31 of K/V head (b, hkv).
+template <typename T, class C, bool CAUSAL>
+__global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
+  const PrefillArgs& a = ba.f;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+  T* const KsA = reinterpret_cast<T*>(smem);  // Q row-major
+  T* const VsA = KsA + C::K_ELEMS;            // dO transposed
+  T* const KsB = reinterpret_cast<T*>(smem + C::STAGE_BYTES);  // dO row-major
+  T* const VsB = KsB + C::K_ELEMS;                             // Q transposed
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int j = lane & 31;
+  const int h2 = lane >> 5;
+
+  const int k0 = blockIdx.x * 32 * C::NW;
+  const int hkv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int key = k0 + 32 * w + j;
+  const bool kvalid = key < a.Nk;
+  const size_t key_row = ((size_t)(b * a.Hkv + hkv) * a.Nk + (kvalid ? key : 0)) * C::D;
+  typename C::Frag kf[C::QF], vf[C::QF];
+  load_q_frag<T, C>(kf, reinterpret_cast<const T*>(a.k) + key_row, kvalid, false, h2);
+  load_q_frag<T, C>(vf, reinterpret_cast<const T*>(a.v) + key_row, kvalid, false, h2);
+
+  // query tiles: every head of the group, positions from the first tile
+  // whose rows can see a key of this workgroup
+  const int first = CAUSAL ? max(0, k0 - a.q_offset) / C::BC : 0;
+  const int nqt = (a.Nq + C::BC - 1) / C::BC - first;  // >= 1 for launched blocks
+  const int nsteps = a.g * nqt;
+  const float c = a.c;
+  const int rowb = C::D * C::ESZ;
+
+  f32x16 acc_dk[C::DB], acc_dv[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    acc_dk[db] = f32x16{};
+    acc_dv[db] = f32x16{};
+  }
+  TileRegs<C> ra, rb;
+  auto tile_head = [&](int st) { return hkv * a.g + st / nqt; };
+  auto tile_i0 = [&](int st) { return (first + st % nqt) * C::BC; };
+  auto issue = [&](int st) {
+    const size_t hoff = (size_t)(b * a.Hq + tile_head(st)) * a.Nq * C::D;
+    const T* qbase = uniform_ptr(reinterpret_cast<const T*>(a.q) + hoff);
+    const T* dobase = uniform_ptr(reinterpret_cast<const T*>(ba.dout) + hoff);
+    load_tile<T, C>(ra, qbase, dobase, tile_i0(st), a.Nq, tid, rowb);
+    load_tile<T, C>(rb, dobase, qbase, tile_i0(st), a.Nq, tid, rowb);
+  };
+  if (nqt > 0) issue(0);
+  for (int st = 0; st < nsteps; ++st) {
+    __syncthreads();
+    store_tile<T, C>(ra, KsA, VsA, tid);
+    store_tile<T, C>(rb, KsB, VsB, tid);
+    __syncthreads();
+    const int i0 = tile_i0(st);
+    const size_t srow = (size_t)(b * a.Hq + tile_head(st)) * a.Nq;  // row statistics base
+    if (st + 1 < nsteps) issue(st + 1);
+    f32x16 s[C::KB], dp[C::KB];
+    qk_tile<T, C>(s, kf, KsA, j, h2);   // S = Q K^T
+    qk_tile<T, C>(dp, vf, KsB, j, h2);  // dP = dO V^T
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // query row of accumulator register r; rows past Nq hold zero Q and
+        // dO, so whatever statistics they read, they add nothing
+        const int qi = i0 + 32 * kb + key_of_reg(r, h2);
+        const int qc = min(qi, a.Nq - 1);
+        const float lse = ba.lse[srow + qc];
+        const float Dr = ba.dd[srow + qc];
+        const bool vis = !CAUSAL || key <= a.q_offset + qi;
+        const float p = vis ? fast_exp2(__builtin_fmaf(s[kb][r], c, -lse)) : 0.f;
+        s[kb][r] = p;
+        dp[kb][r] = p * (dp[kb][r] - Dr);
+      }
+    typename C::Frag pf[C::KB][C::PF], dsf[C::KB][C::PF];
+    to_frag<C>(s, pf);
+    to_frag<C>(dp, dsf);
+    pv_tile<T, C>(acc_dv, pf, VsA, j, h2);   // dV^T += dO^T P
+    pv_tile<T, C>(acc_dk, dsf, VsB, j, h2);  // dK^T += Q^T dS
+  }
+
+  if (kvalid) {
+    store_out_row<T, C>(reinterpret_cast<T*>(ba.dk) + key_row, acc_dk, ba.scale, h2);
+    store_out_row<T, C>(reinterpret_cast<T*>(ba.dv) + key_row, acc_dv, 1.0f, h2);
+  }
+}
+
+}  // namespace gqa

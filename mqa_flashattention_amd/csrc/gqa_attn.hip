@@ -3,7 +3,8 @@
 // Host side only: argument validation (pure CPU, before any HIP call), the
 // gfx950 device check, the per-(device, stream) scheduler counters, choice
 // of the unit decomposition and split size, and the kernel launches.  All
-// arithmetic runs in the kernels of prefill_kernel.hpp / decode_kernel.hpp.
+// arithmetic runs in the kernels of prefill_kernel.hpp / decode_kernel.hpp /
+// backward_kernel.hpp.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -17,6 +18,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "backward_kernel.hpp"
 #include "decode_kernel.hpp"
 #include "gqa_attn.h"
 #include "prefill_kernel.hpp"
@@ -563,6 +565,112 @@ int decode_entry(const void* q, const void* kcache, const void* vcache, const in
   return dispatch_decode<float, DecCfgF32, false>(a, d, hs);
 }
 
+// ------------------------------------------------------------------ backward
+
+template <typename T, class C, bool CAUSAL>
+int launch_bwd(gqa::BwdArgs& ba, hipStream_t stream) {
+  (void)hipGetLastError();  // a stale error belongs to an earlier call
+  hipLaunchKernelGGL((gqa::bwd_dq_kernel<T, C, CAUSAL>), dim3((unsigned)ba.f.T), dim3(C::NT), 0,
+                     stream, ba);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "backward dQ kernel launch");
+  const unsigned kblocks = (unsigned)((ba.f.Nk + 32 * C::NW - 1) / (32 * C::NW));
+  hipLaunchKernelGGL((gqa::bwd_dkdv_kernel<T, C, CAUSAL>),
+                     dim3(kblocks, (unsigned)ba.f.Hkv, (unsigned)ba.f.B), dim3(C::NT), 0, stream,
+                     ba);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "backward dK/dV kernel launch");
+  return GQA_OK;
+}
+
+template <typename T, template <int> class Cfg>
+int dispatch_bwd(gqa::BwdArgs& ba, int d, int causal, hipStream_t s) {
+  switch (d) {
+    case 32: return causal ? launch_bwd<T, Cfg<32>, true>(ba, s) : launch_bwd<T, Cfg<32>, false>(ba, s);
+    case 64: return causal ? launch_bwd<T, Cfg<64>, true>(ba, s) : launch_bwd<T, Cfg<64>, false>(ba, s);
+    default:
+      return causal ? launch_bwd<T, Cfg<128>, true>(ba, s) : launch_bwd<T, Cfg<128>, false>(ba, s);
+  }
+}
+
+size_t bwd_ws_bytes(int B, int Hq, int Nq) { return 2 * (size_t)B * Hq * Nq * sizeof(float); }
+
+int bwd_entry(const void* q, const void* k, const void* v, const void* o, const void* dout,
+              void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+              int causal, int q_offset, float scale, int dtype, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1)
+    return fail(GQA_ERR_BAD_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d)", B,
+                Hq, Hkv, Nq, Nk, d);
+  if (causal && q_offset < 0) return fail(GQA_ERR_BAD_SHAPE, "q_offset=%d < 0", q_offset);
+  if (Hq % Hkv != 0)
+    return fail(GQA_ERR_HEAD_GROUPING, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(GQA_ERR_UNSUPPORTED, "the backward needs a finite scale > 0");
+  if ((long long)Nq * d > kIntMax || (long long)Nk * d > kIntMax ||
+      (causal && (long long)q_offset + Nq > kIntMax))
+    return fail(GQA_ERR_BAD_SHAPE, "sequence too long for 32-bit in-head indexing");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(GQA_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+  const size_t need = bwd_ws_bytes(B, Hq, Nq);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(GQA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  const int M = 32 * kPrefillWaves;
+  const int g = Hq / Hkv;
+  const int Gu = g < M ? g : M;
+  const int R = M / Gu;
+  const long long NQB = ((long long)Nq + R - 1) / R;
+  const long long T = (long long)B * Hkv * ((g + Gu - 1) / Gu) * NQB;
+  if (T > kIntMax || B > 65535 || Hkv > 65535)
+    return fail(GQA_ERR_BAD_SHAPE, "too many work units (%lld)", T);
+
+  int dev = 0;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != GQA_OK) return st;
+
+  const int esz = dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  gqa::BwdArgs ba;
+  gqa::PrefillArgs& a = ba.f;
+  a = gqa::PrefillArgs{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = nullptr;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.q_sb = (long long)Hq * Nq * d;
+  a.q_sh = (long long)Nq * d;
+  a.q_sn = d;
+  a.kv_sb = (long long)Hkv * Nk * d;
+  a.kv_sh = (long long)Nk * d;
+  a.kv_rowb = d * esz;
+  a.g = g;
+  decompose(a, M);
+  a.q_offset = causal ? q_offset : 0;
+  a.c = scale * gqa::kLog2e;
+  a.thr = gqa::kRescaleSlack / a.c;
+  ba.o = o;
+  ba.dout = dout;
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.lse = reinterpret_cast<float*>(workspace);
+  ba.dd = ba.lse + (size_t)B * Hq * Nq;
+  ba.scale = scale;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == GQA_DTYPE_BF16) return dispatch_bwd<uint16_t, CfgBf16>(ba, d, causal, hs);
+  return dispatch_bwd<float, CfgF32>(ba, d, causal, hs);
+}
+
 }  // namespace
 
 extern "C" {
@@ -662,6 +770,22 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new, 
                 "q, k_new, v_new, kcache, vcache, positions and o must be non-NULL");
   return decode_entry(q, kcache, vcache, positions, k_new, v_new, kcache, vcache, o, B, Hq, Hkv,
                       Smax, d, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
+  if (B < 1 || Hq < 1 || Nq < 1) return 0;
+  return bwd_ws_bytes(B, Hq, Nq);
+}
+
+int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 int causal, int q_offset, float scale, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !dout || !dq || !dk || !dv)
+    return fail(GQA_ERR_NULL_POINTER, "q, k, v, o, dout, dq, dk and dv must be non-NULL");
+  return bwd_entry(q, k, v, o, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal, q_offset, scale,
+                   dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -189,3 +189,46 @@ def test_binding_checks_tensors_before_the_library():
         binding.attn_fwd(q.float(), q[:, :2], q[:, :2])
     with pytest.raises(ValueError):
         binding.attn_decode(q[:, :, 0], q, q, torch.zeros(1, dtype=torch.int32))
+
+
+# ---------------------------------------------------------------- backward
+PB = [ctypes.c_void_p(0x10000 * (n + 1)) for n in range(9)]
+
+
+def bwd(q=PB[0], k=PB[1], v=PB[2], o=PB[3], do=PB[4], dq=PB[5], dk=PB[6], dv=PB[7], B=1, Hq=4,
+        Hkv=2, Nq=64, Nk=64, d=32, causal=0, q_offset=0, scale=0.17, dtype=BF16, ws=PB[8],
+        ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = binding.bwd_workspace_bytes(B, Hq, Nq)
+    return binding.lib.gqa_attn_bwd(q, k, v, o, do, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal,
+                                    q_offset, ctypes.c_float(scale), dtype, ws, ws_bytes, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(o=None), NULLP), (dict(do=None), NULLP), (dict(dq=None), NULLP),
+    (dict(dk=None), NULLP), (dict(dv=None), NULLP),
+    (dict(B=0), SHAPE), (dict(Nq=0), SHAPE), (dict(Nk=-3), SHAPE),
+    (dict(causal=1, q_offset=-1), SHAPE), (dict(Nk=2 ** 30, d=32), SHAPE),
+    (dict(Hq=6, Hkv=4), GROUP),
+    (dict(dtype=7), UNSUP), (dict(d=48), UNSUP), (dict(scale=0.0), UNSUP),
+    (dict(scale=-0.1), UNSUP), (dict(scale=float("inf")), UNSUP),
+    (dict(dq=ctypes.c_void_p(0x10008)), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=64), WS), (dict(ws=ctypes.c_void_p(0x10004)), WS),
+])
+def test_bwd_rejects_invalid_arguments(kw, code):
+    assert bwd(**kw) == code
+    assert binding.lib.gqa_last_error_string()
+
+
+def test_bwd_workspace_bytes():
+    ws = binding.bwd_workspace_bytes
+    # two fp32 row statistics (log-sum-exp and D) per query row
+    assert ws(1, 32, 2048) == 2 * 32 * 2048 * 4
+    assert ws(3, 5, 7) == 2 * 3 * 5 * 7 * 4
+    assert ws(0, 1, 1) == 0 and ws(1, 1, 0) == 0
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="valid arguments would launch on a GPU")
+def test_valid_bwd_call_without_gpu_reports_no_device():
+    assert bwd() == NODEV
+    assert bwd(causal=1, q_offset=5, dtype=F32, d=128) == NODEV
