@@ -243,6 +243,50 @@ def time_append_workload(s, steps, warmup):
     return float(np.mean([a.elapsed_time(b) for a, b in ev])), pos_h.tolist()
 
 
+def bwd_flops(s) -> float:
+    """Algorithmic backward FLOPs: five contractions over the visible pairs
+    (S recomputed, dP, dV, dK, dQ), 2 FLOPs per MAC -- 2.5x the forward."""
+    return 10.0 * s.B * s.Hq * s.d * s.visible_pairs_per_head()
+
+
+def time_bwd_workload(s, steps, warmup):
+    """Event-timed average duration (ms) of one gqa_attn_bwd call (both of its
+    kernels), after a parity check of dQ, dK, dV against the oracle."""
+    import numpy as np
+    import torch
+
+    import oracle  # test infrastructure: parity gate only
+    from mqa_flashattention_amd import attn_bwd, attn_fwd, bwd_workspace_bytes
+    from mqa_flashattention_amd.workloads import fwd_inputs, random_tensor
+    q_h, k_h, v_h = fwd_inputs(s, 0)
+    do_h = random_tensor(q_h.shape, 11, s.dtype)
+    q, k, v, do = (t.cuda() for t in (q_h, k_h, v_h, do_h))
+    o = attn_fwd(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale)
+    ws = torch.empty(bwd_workspace_bytes(s.B, s.Hq, s.Nq), dtype=torch.uint8, device=q.device)
+    grads = attn_bwd(q, k, v, o, do, causal=s.causal, q_offset=s.q_offset, scale=s.scale,
+                     workspace=ws)
+    torch.cuda.synchronize()
+    want = oracle.attn_bwd(q_h, k_h, v_h, do_h, causal=s.causal, q_offset=s.q_offset,
+                           scale=s.scale)
+    for name, g, w in zip(("dq", "dk", "dv"), grads, want):
+        got = g.detach().cpu().double().numpy()
+        if not np.all(np.abs(got - w) <= 2e-2 + 2.0 ** -7 * np.abs(w)):
+            raise SystemExit(f"backward {name}: parity check failed")
+    for _ in range(warmup):
+        attn_bwd(q, k, v, o, do, causal=s.causal, q_offset=s.q_offset, scale=s.scale,
+                 workspace=ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        attn_bwd(q, k, v, o, do, causal=s.causal, q_offset=s.q_offset, scale=s.scale,
+                 workspace=ws)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
 # Supplementary decode sweep: the batch-8 shape (Hq 12, Hkv 2, d 128) at more
 # rows and longer contexts, lengths uniform in [Smax/4, Smax] as for the
 # batch-8 workload's [512, 2048].  It shows how close the decode kernels come
@@ -321,7 +365,9 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--all", action="store_true",
-                    help="also time the MHA/GQA/MQA sweep and the chunked prefill")
+                    help="also time the MHA/GQA/MQA sweep, the chunked prefill, the "
+                         "token-major prefill, decode with append, the backward and the "
+                         "decode sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after timing, stream 256 MiB through a plain elementwise kernel "
@@ -500,6 +546,14 @@ def main(argv=None):
             "frac_hbm_peak": round(gb / PEAK_HBM_GBPS, 4),
             "algorithmic_mb": round(append_bytes(sa, positions) / 1e6, 4),
             "note": "store of the new K/V rows + split + combine, one call, HBM-cold caches"}
+        ms = time_bwd_workload(ps, max(10, K // 2), 3)
+        tf = bwd_flops(ps) / (ms * 1e-3) / 1e12
+        extra["llama3_8b_backward"] = {
+            "ms": round(ms, 5), "tflops": round(tf, 2),
+            "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_gflop": round(bwd_flops(ps) / 1e9, 4),
+            "note": "gqa_attn_bwd: dQ kernel (row statistics + dQ) and dK/dV kernel; "
+                    "5 contractions counted (the kernels execute 7: S three times)"}
         extra.update(time_decode_sweep(20, 3))
         result["other_workloads"] = extra
 

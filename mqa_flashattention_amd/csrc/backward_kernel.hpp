@@ -231,6 +231,15 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
     acc_dv[db] = f32x16{};
   }
   TileRegs<C> ra, rb;
+  // row statistics of a tile, per accumulator register: register r of
+  // block kb is query row 32 kb + key_of_reg(r, h2), i.e. runs of 8
+  // consecutive rows -- two 16-byte loads per run, through a resource over
+  // the whole statistics area (reads past its end return 0; rows past Nq
+  // are excluded below whatever they read)
+  const auto stats = buffer_rsrc(
+      ba.lse, __builtin_amdgcn_readfirstlane((uint32_t)(2ull * a.B * a.Hq * a.Nq * 4)));
+  const uint32_t dd_off = (uint32_t)((size_t)a.B * a.Hq * a.Nq * 4);
+  float4 lse4[C::KB][4], dd4[C::KB][4];
   auto tile_head = [&](int st) { return hkv * a.g + st / nqt; };
   auto tile_i0 = [&](int st) { return (first + st % nqt) * C::BC; };
   auto issue = [&](int st) {
@@ -239,6 +248,19 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
     const T* dobase = uniform_ptr(reinterpret_cast<const T*>(ba.dout) + hoff);
     load_tile<T, C>(ra, qbase, dobase, tile_i0(st), a.Nq, tid, rowb);
     load_tile<T, C>(rb, dobase, qbase, tile_i0(st), a.Nq, tid, rowb);
+    const uint32_t srow = (uint32_t)((size_t)(b * a.Hq + tile_head(st)) * a.Nq + tile_i0(st));
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // registers 4 q4 .. 4 q4 + 3: rows 16 (q4 / 2) + 8 h2 + 4 (q4 % 2) + 0..3
+        const uint32_t off =
+            4u * (srow + 32 * kb + 16 * (q4 / 2) + 8 * h2 + 4 * (q4 % 2));
+        lse4[kb][q4] = __builtin_bit_cast(
+            float4, __builtin_amdgcn_raw_buffer_load_b128(stats, (int)off, 0, 0));
+        dd4[kb][q4] = __builtin_bit_cast(
+            float4, __builtin_amdgcn_raw_buffer_load_b128(stats, (int)(off + dd_off), 0, 0));
+      }
   };
   if (nqt > 0) issue(0);
   for (int st = 0; st < nsteps; ++st) {
@@ -247,7 +269,20 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
     store_tile<T, C>(rb, KsB, VsB, tid);
     __syncthreads();
     const int i0 = tile_i0(st);
-    const size_t srow = (size_t)(b * a.Hq + tile_head(st)) * a.Nq;  // row statistics base
+    float lse_r[C::KB][16], dd_r[C::KB][16];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        lse_r[kb][4 * q4] = lse4[kb][q4].x;
+        lse_r[kb][4 * q4 + 1] = lse4[kb][q4].y;
+        lse_r[kb][4 * q4 + 2] = lse4[kb][q4].z;
+        lse_r[kb][4 * q4 + 3] = lse4[kb][q4].w;
+        dd_r[kb][4 * q4] = dd4[kb][q4].x;
+        dd_r[kb][4 * q4 + 1] = dd4[kb][q4].y;
+        dd_r[kb][4 * q4 + 2] = dd4[kb][q4].z;
+        dd_r[kb][4 * q4 + 3] = dd4[kb][q4].w;
+      }
     if (st + 1 < nsteps) issue(st + 1);
     f32x16 s[C::KB], dp[C::KB];
     qk_tile<T, C>(s, kf, KsA, j, h2);   // S = Q K^T
@@ -256,16 +291,13 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        // query row of accumulator register r; rows past Nq hold zero Q and
-        // dO, so whatever statistics they read, they add nothing
+        // query row of accumulator register r; rows past Nq (zero Q and dO)
+        // and, when causal, rows that cannot see this key weigh exactly 0
         const int qi = i0 + 32 * kb + key_of_reg(r, h2);
-        const int qc = min(qi, a.Nq - 1);
-        const float lse = ba.lse[srow + qc];
-        const float Dr = ba.dd[srow + qc];
-        const bool vis = !CAUSAL || key <= a.q_offset + qi;
-        const float p = vis ? fast_exp2(__builtin_fmaf(s[kb][r], c, -lse)) : 0.f;
+        const bool vis = qi < a.Nq && (!CAUSAL || key <= a.q_offset + qi);
+        const float p = vis ? fast_exp2(__builtin_fmaf(s[kb][r], c, -lse_r[kb][r])) : 0.f;
         s[kb][r] = p;
-        dp[kb][r] = p * (dp[kb][r] - Dr);
+        dp[kb][r] = p * (dp[kb][r] - dd_r[kb][r]);
       }
     typename C::Frag pf[C::KB][C::PF], dsf[C::KB][C::PF];
     to_frag<C>(s, pf);

@@ -574,9 +574,12 @@ int launch_bwd(gqa::BwdArgs& ba, hipStream_t stream) {
                      stream, ba);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "backward dQ kernel launch");
-  const unsigned kblocks = (unsigned)((ba.f.Nk + 32 * C::NW - 1) / (32 * C::NW));
-  hipLaunchKernelGGL((gqa::bwd_dkdv_kernel<T, C, CAUSAL>),
-                     dim3(kblocks, (unsigned)ba.f.Hkv, (unsigned)ba.f.B), dim3(C::NT), 0, stream,
+  // dK/dV: 64 keys (two waves) per workgroup, so that the LLaMA-sized
+  // launches spread over every CU (its registers allow one wave per SIMD)
+  using CK = gqa::TileCfg<T, C::D, C::BC, 2>;
+  const unsigned kblocks = (unsigned)((ba.f.Nk + 32 * CK::NW - 1) / (32 * CK::NW));
+  hipLaunchKernelGGL((gqa::bwd_dkdv_kernel<T, CK, CAUSAL>),
+                     dim3(kblocks, (unsigned)ba.f.Hkv, (unsigned)ba.f.B), dim3(CK::NT), 0, stream,
                      ba);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "backward dK/dV kernel launch");
@@ -628,6 +631,9 @@ int bwd_entry(const void* q, const void* k, const void* v, const void* o, const 
   const long long T = (long long)B * Hkv * ((g + Gu - 1) / Gu) * NQB;
   if (T > kIntMax || B > 65535 || Hkv > 65535)
     return fail(GQA_ERR_BAD_SHAPE, "too many work units (%lld)", T);
+  // the row statistics are addressed with 32-bit byte offsets
+  if (8LL * B * Hq * Nq > 4294967295LL)
+    return fail(GQA_ERR_BAD_SHAPE, "too many query rows (%lld)", (long long)B * Hq * Nq);
 
   int dev = 0;
   DeviceInfo info;
