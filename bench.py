@@ -387,7 +387,7 @@ def main(argv=None):
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention "
-              "path is not sharded across GPUs in this build.", file=sys.stderr)
+              "path is not sharded across GPUs by this library.", file=sys.stderr)
         return 2
 
     import numpy as np
