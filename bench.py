@@ -243,6 +243,51 @@ def time_append_workload(s, steps, warmup):
     return float(np.mean([a.elapsed_time(b) for a, b in ev])), pos_h.tolist()
 
 
+def time_decode_graph(steps):
+    """Decode of the batch-8 workload replayed from a HIP graph: one graph of
+    DECODE_SETS calls (one per HBM-cold cache set, caller-provided
+    workspace), replayed `steps` times; returns ms per call.  Before timing,
+    the graph's last call is checked bit for bit against the same call made
+    eagerly, after a first replay and again after the timed ones."""
+    import numpy as np
+    import torch
+    from mqa_flashattention_amd import attn_decode, decode_workspace_bytes
+    from mqa_flashattention_amd.workloads import WORKLOADS, decode_inputs
+    s = WORKLOADS["kv_decode_b8"].decode
+    dev = torch.device("cuda:0")
+    q_h, k_h, v_h, l_h = decode_inputs(s, 0)
+    q, lens = q_h.to(dev), l_h.to(dev)
+    kcs, vcs = [k_h.to(dev)], [v_h.to(dev)]
+    gen = torch.Generator(device=dev).manual_seed(3)
+    for _ in range(DECODE_SETS - 1):
+        kcs.append(torch.randn(k_h.shape, generator=gen, device=dev).to(s.dtype))
+        vcs.append(torch.randn(v_h.shape, generator=gen, device=dev).to(s.dtype))
+    ws = torch.empty(decode_workspace_bytes(s.B, s.Hq, s.Hkv, s.Smax, s.d), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty_like(q)
+    want = attn_decode(q, kcs[-1], vcs[-1], lens, scale=s.scale, workspace=ws).clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(DECODE_SETS):
+            attn_decode(q, kcs[i], vcs[i], lens, scale=s.scale, out=o, workspace=ws)
+    graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(o, want):
+        raise SystemExit("decode graph replay differs from the eager call")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        graph.replay()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    if not torch.equal(o, want):
+        raise SystemExit("decode graph replay differs from the eager call")
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev])) / DECODE_SETS
+    return ms, decode_bytes(s, l_h.tolist())
+
+
 def bwd_flops(s) -> float:
     """Algorithmic backward FLOPs: five contractions over the visible pairs
     (S recomputed, dP, dV, dK, dQ), 2 FLOPs per MAC -- 2.5x the forward."""
@@ -546,6 +591,13 @@ def main(argv=None):
             "frac_hbm_peak": round(gb / PEAK_HBM_GBPS, 4),
             "algorithmic_mb": round(append_bytes(sa, positions) / 1e6, 4),
             "note": "store of the new K/V rows + split + combine, one call, HBM-cold caches"}
+        ms, nbytes = time_decode_graph(20)
+        gb = nbytes / (ms * 1e-3) / 1e9
+        extra["kv_decode_b8[graph]"] = {
+            "ms": round(ms, 5), "value": round(gb, 2), "unit": "GB/s",
+            "frac_hbm_peak": round(gb / PEAK_HBM_GBPS, 4),
+            "note": "the same decode calls replayed from a HIP graph (48 per replay, one per "
+                    "HBM-cold cache set): no host dispatch between calls"}
         ms = time_bwd_workload(ps, max(10, K // 2), 3)
         tf = bwd_flops(ps) / (ms * 1e-3) / 1e12
         extra["llama3_8b_backward"] = {

@@ -436,3 +436,34 @@ RANDOM_SHAPES = _random_shapes()
 def test_random_shapes(idx):
     s, rows = RANDOM_SHAPES[idx]
     _check_fwd(s, 300 + idx, rows=rows)
+
+
+# ---------------------------------------------------------------- HIP graph capture
+def test_decode_graph_replay_matches_eager():
+    """Decode calls captured in a HIP graph (caller-provided workspace: the
+    decode path allocates nothing and issues no memset) replay to the eager
+    results, bit for bit, on every replay, with eager work and
+    synchronisations between the replays."""
+    s = WORKLOADS["kv_decode_b8"].decode
+    cases = []
+    for seed in (0, 1, 2):
+        q, kc, vc, lens = (t.to(DEV) for t in decode_inputs(s, seed))
+        cases.append((q, kc, vc, lens))
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device=DEV)
+    eager = [attn_decode(*c, workspace=ws).clone() for c in cases]
+    outs = [torch.empty_like(c[0]) for c in cases]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for c, o in zip(cases, outs):
+            attn_decode(*c, out=o, workspace=ws)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep} differs from the eager call"
+        # eager work between replays, on the same workspace
+        assert torch.equal(attn_decode(*cases[rep % 3], workspace=ws), eager[rep % 3])
+        torch.cuda.synchronize()
