@@ -84,7 +84,10 @@ __device__ __forceinline__ void to_frag(const f32x16 (&x)[C::KB],
   }
 }
 
-// grid (T), C::NT threads: unit t of the forward decomposition.
+// grid (T), C::NT threads: one unit of the forward decomposition per
+// workgroup.  Causal units are taken heaviest first (position blocks in
+// descending order, all heads of a block together), so that the light
+// units fill in behind the heavy ones instead of ending the launch.
 template <typename T, class C, bool CAUSAL>
 __global__ void __launch_bounds__(C::NT) bwd_dq_kernel(BwdArgs ba) {
   const PrefillArgs& a = ba.f;
@@ -99,9 +102,10 @@ __global__ void __launch_bounds__(C::NT) bwd_dq_kernel(BwdArgs ba) {
   const int j = lane & 31;
   const int h2 = lane >> 5;
 
+  const int per_qb = a.T / a.NQB;  // units of one position block
   const int t = blockIdx.x;
-  const int qb = t % a.NQB;
-  const int rest = t / a.NQB;
+  const int qb = CAUSAL ? a.NQB - 1 - t / per_qb : t % a.NQB;
+  const int rest = CAUSAL ? t % per_qb : t / a.NQB;
   const int hb = rest % a.HB;
   const int kvg = rest / a.HB;
   const int hkv = kvg % a.Hkv;
