@@ -307,7 +307,8 @@ def time_bwd_workload(s, steps, warmup):
     do_h = random_tensor(q_h.shape, 11, s.dtype)
     q, k, v, do = (t.cuda() for t in (q_h, k_h, v_h, do_h))
     o = attn_fwd(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale)
-    ws = torch.empty(bwd_workspace_bytes(s.B, s.Hq, s.Nq), dtype=torch.uint8, device=q.device)
+    ws = torch.empty(bwd_workspace_bytes(s.B, s.Hq, s.Hkv, s.Nq, s.Nk, s.d), dtype=torch.uint8,
+                     device=q.device)
     grads = attn_bwd(q, k, v, o, do, causal=s.causal, q_offset=s.q_offset, scale=s.scale,
                      workspace=ws)
     torch.cuda.synchronize()
@@ -604,8 +605,9 @@ def main(argv=None):
             "ms": round(ms, 5), "tflops": round(tf, 2),
             "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "algorithmic_gflop": round(bwd_flops(ps) / 1e9, 4),
-            "note": "gqa_attn_bwd: dQ kernel (row statistics + dQ) and dK/dV kernel; "
-                    "5 contractions counted (the kernels execute 7: S three times)"}
+            "note": "gqa_attn_bwd: dQ kernel (row statistics + dQ), dK/dV kernel (two query "
+                    "parts per key block) and their merge; 5 contractions counted (the "
+                    "kernels execute 7: S three times)"}
         extra.update(time_decode_sweep(20, 3))
         result["other_workloads"] = extra
 

@@ -178,10 +178,12 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new,
                            int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of device workspace gqa_attn_bwd needs: two fp32 values per query
- * row (B * Hq * Nq rows).  Returns 0 for invalid sizes.
+ * Bytes of device workspace gqa_attn_bwd needs for these sizes: two fp32
+ * row statistics per query row (B * Hq * Nq rows, rounded up to 16 bytes),
+ * then two fp32 partial copies of dk and dv (2 * 2 * B * Hkv * Nk * d
+ * floats).  Returns 0 for invalid sizes.
  */
-size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Nq);
+size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
 /*
  * Backward of gqa_attn_fwd: the gradients dq, dk, dv of a loss L given
@@ -203,11 +205,13 @@ size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Nq);
  * result is run-to-run reproducible).
  *
  * workspace: device memory of at least gqa_attn_bwd_workspace_bytes(B, Hq,
- * Nq) bytes, owned by the caller, contents on entry irrelevant; it receives
- * each row's log-sum-exp and D.  scale must be finite and > 0
+ * Hkv, Nq, Nk, d) bytes, owned by the caller, contents on entry irrelevant;
+ * it receives each row's log-sum-exp and D, and the fp32 dk, dv of the two
+ * halves of each key block's query range, added in a fixed order at the end.  scale must be finite and > 0
  * (GQA_ERR_UNSUPPORTED otherwise).  Outputs must not alias inputs.  Other
  * status codes and error behaviour as gqa_attn_fwd (plus GQA_ERR_WORKSPACE).
- * Two launches on the stream: dq (with the row statistics), then dk and dv.
+ * Three launches on the stream: dq (with the row statistics), the dk/dv
+ * parts, and their merge.
  */
 int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  void* dq, void* dk, void* dv,

@@ -57,7 +57,7 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp,
                                            sz, vp]
     lib.gqa_attn_decode_append.restype = i
-    lib.gqa_attn_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.gqa_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.gqa_attn_bwd_workspace_bytes.restype = sz
     lib.gqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp,
                                  sz, vp]
@@ -177,8 +177,8 @@ def attn_fwd_strided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
     return out
 
 
-def bwd_workspace_bytes(B: int, Hq: int, Nq: int) -> int:
-    return int(lib.gqa_attn_bwd_workspace_bytes(B, Hq, Nq))
+def bwd_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    return int(lib.gqa_attn_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d))
 
 
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
@@ -201,7 +201,7 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
         raise ValueError("o and dout must have the shape of q")
-    need = bwd_workspace_bytes(B, Hq, Nq)
+    need = bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or not workspace.is_contiguous():

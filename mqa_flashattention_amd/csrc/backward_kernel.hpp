@@ -21,7 +21,9 @@
 //  * bwd_dkdv_kernel: 32 keys per wave of one K/V head.  The wave walks
 //    the query tiles of every query head of the group (this is the GQA
 //    reduction, done in registers), with S = Q K^T and dP = dO V^T, and
-//    accumulates dV^T += dO^T P and dK^T += Q^T dS.
+//    accumulates dV^T += dO^T P and dK^T += Q^T dS.  The query steps of a
+//    key block are cut into kBwdQuerySplit parts, one workgroup each, whose
+//    fp32 results bwd_merge_kernel adds in part order.
 // In both, a staged tile occupies two LDS stages: one holds the first
 // operand row-major (the A operand of S or S^T) with the second transposed,
 // the other the second operand row-major with the first transposed.
@@ -40,8 +42,15 @@ struct BwdArgs {
   void* dv;
   float* lse;  // [B][Hq][Nq]: m c + log2 l of each query row
   float* dd;   // [B][Hq][Nq]: D = sum_c dO O
+  float* part;  // [kBwdQuerySplit][2][B][Hkv][Nk][D] fp32: dK, dV of each query part
   float scale;
 };
+
+// Each K/V key block's query range is cut into this many parts, one
+// workgroup each, so that the first key blocks of a causal launch (which
+// every query sees) do not serialise the kernel; bwd_merge_kernel adds the
+// parts' dK, dV in part order.
+constexpr int kBwdQuerySplit = 2;
 
 // Sum over this lane's elements of x * y (two B-operand fragments of one
 // column); the other half-wave holds the rest of the row.
@@ -194,8 +203,10 @@ __global__ void __launch_bounds__(C::NT) bwd_dq_kernel(BwdArgs ba) {
   }
 }
 
-// grid (ceil(Nk / (32 NW)), Hkv, B), C::NT threads: wave w owns keys
-// k0 + 32 w .. k0 + 32 w + 31 of K/V head (b, hkv).
+// grid (ceil(Nk / (32 NW)) * kBwdQuerySplit, Hkv, B), C::NT threads: wave
+// w owns keys k0 + 32 w .. k0 + 32 w + 31 of K/V head (b, hkv), over part
+// `part` of the block's query steps; it writes fp32 partial dK (scaled) and
+// dV to the part's records.
 template <typename T, class C, bool CAUSAL>
 __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
   const PrefillArgs& a = ba.f;
@@ -210,7 +221,8 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
   const int j = lane & 31;
   const int h2 = lane >> 5;
 
-  const int k0 = blockIdx.x * 32 * C::NW;
+  const int part = blockIdx.x % kBwdQuerySplit;
+  const int k0 = (blockIdx.x / kBwdQuerySplit) * 32 * C::NW;
   const int hkv = blockIdx.y;
   const int b = blockIdx.z;
   const int key = k0 + 32 * w + j;
@@ -224,7 +236,10 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
   // whose rows can see a key of this workgroup
   const int first = CAUSAL ? max(0, k0 - a.q_offset) / C::BC : 0;
   const int nqt = (a.Nq + C::BC - 1) / C::BC - first;  // >= 1 for launched blocks
-  const int nsteps = a.g * nqt;
+  const int nall = a.g * nqt;  // query steps of the key block
+  const int per_part = (nall + kBwdQuerySplit - 1) / kBwdQuerySplit;
+  const int st0 = min(nall, part * per_part);
+  const int nsteps = max(0, min(nall, st0 + per_part) - st0);  // this part's steps
   const float c = a.c;
   const int rowb = C::D * C::ESZ;
 
@@ -244,8 +259,9 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
       ba.lse, __builtin_amdgcn_readfirstlane((uint32_t)(2ull * a.B * a.Hq * a.Nq * 4)));
   const uint32_t dd_off = (uint32_t)((size_t)a.B * a.Hq * a.Nq * 4);
   float4 lse4[C::KB][4], dd4[C::KB][4];
-  auto tile_head = [&](int st) { return hkv * a.g + st / nqt; };
-  auto tile_i0 = [&](int st) { return (first + st % nqt) * C::BC; };
+  // step st of this part is step st0 + st of the key block
+  auto tile_head = [&](int st) { return hkv * a.g + (st0 + st) / nqt; };
+  auto tile_i0 = [&](int st) { return (first + (st0 + st) % nqt) * C::BC; };
   auto issue = [&](int st) {
     const size_t hoff = (size_t)(b * a.Hq + tile_head(st)) * a.Nq * C::D;
     const T* qbase = uniform_ptr(reinterpret_cast<const T*>(a.q) + hoff);
@@ -266,7 +282,7 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
             float4, __builtin_amdgcn_raw_buffer_load_b128(stats, (int)(off + dd_off), 0, 0));
       }
   };
-  if (nqt > 0) issue(0);
+  if (nsteps > 0) issue(0);
   for (int st = 0; st < nsteps; ++st) {
     __syncthreads();
     store_tile<T, C>(ra, KsA, VsA, tid);
@@ -311,8 +327,52 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
   }
 
   if (kvalid) {
-    store_out_row<T, C>(reinterpret_cast<T*>(ba.dk) + key_row, acc_dk, ba.scale, h2);
-    store_out_row<T, C>(reinterpret_cast<T*>(ba.dv) + key_row, acc_dv, 1.0f, h2);
+    // records [part][dK, dV][b][hkv][key][D], fp32; this lane holds
+    // d = 32 db + 8 q4 + 4 h2 + 0..3
+    const size_t rows = (size_t)a.B * a.Hkv * a.Nk;
+    const size_t krow = (size_t)(b * a.Hkv + hkv) * a.Nk + key;
+    float* pk = ba.part + ((size_t)(2 * part) * rows + krow) * C::D;
+    float* pv = ba.part + ((size_t)(2 * part + 1) * rows + krow) * C::D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * h2;
+        *reinterpret_cast<float4*>(pk + d0) =
+            float4{acc_dk[db][4 * q4] * ba.scale, acc_dk[db][4 * q4 + 1] * ba.scale,
+                   acc_dk[db][4 * q4 + 2] * ba.scale, acc_dk[db][4 * q4 + 3] * ba.scale};
+        *reinterpret_cast<float4*>(pv + d0) = float4{acc_dv[db][4 * q4], acc_dv[db][4 * q4 + 1],
+                                                     acc_dv[db][4 * q4 + 2], acc_dv[db][4 * q4 + 3]};
+      }
+  }
+}
+
+// dK, dV = the sum of the query parts' records, in part order, rounded
+// once to the output type.  One thread per 4 consecutive elements of
+// dK or dV; n4 = 2 * B * Hkv * Nk * D / 4.
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_merge_kernel(BwdArgs ba, long long n4) {
+  const long long half4 = n4 / 2;  // float4s of dK (then as many of dV)
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x) {
+    const bool is_v = i >= half4;
+    const long long e4 = is_v ? i - half4 : i;
+    const float4* src = reinterpret_cast<const float4*>(ba.part) + (is_v ? half4 : 0) + e4;
+    float4 acc = src[0];
+#pragma unroll
+    for (int p = 1; p < kBwdQuerySplit; ++p) {
+      const float4 x = src[(long long)p * n4];
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    T* dst = reinterpret_cast<T*>(is_v ? ba.dv : ba.dk) + 4 * e4;
+    if constexpr (std::is_same<T, float>::value) {
+      *reinterpret_cast<float4*>(dst) = acc;
+    } else {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(acc.x, acc.y), pack_bf16(acc.z, acc.w)};
+    }
   }
 }
 

@@ -579,10 +579,17 @@ int launch_bwd(gqa::BwdArgs& ba, hipStream_t stream) {
   using CK = gqa::TileCfg<T, C::D, C::BC, 2>;
   const unsigned kblocks = (unsigned)((ba.f.Nk + 32 * CK::NW - 1) / (32 * CK::NW));
   hipLaunchKernelGGL((gqa::bwd_dkdv_kernel<T, CK, CAUSAL>),
-                     dim3(kblocks, (unsigned)ba.f.Hkv, (unsigned)ba.f.B), dim3(CK::NT), 0, stream,
-                     ba);
+                     dim3(kblocks * gqa::kBwdQuerySplit, (unsigned)ba.f.Hkv, (unsigned)ba.f.B),
+                     dim3(CK::NT), 0, stream, ba);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "backward dK/dV kernel launch");
+  const long long n4 = 2LL * ba.f.B * ba.f.Hkv * ba.f.Nk * C::D / 4;
+  long long mblocks = (n4 + 255) / 256;
+  if (mblocks > 4096) mblocks = 4096;
+  hipLaunchKernelGGL((gqa::bwd_merge_kernel<T>), dim3((unsigned)mblocks), dim3(256), 0, stream,
+                     ba, n4);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "backward dK/dV merge kernel launch");
   return GQA_OK;
 }
 
@@ -596,7 +603,15 @@ int dispatch_bwd(gqa::BwdArgs& ba, int d, int causal, hipStream_t s) {
   }
 }
 
-size_t bwd_ws_bytes(int B, int Hq, int Nq) { return 2 * (size_t)B * Hq * Nq * sizeof(float); }
+// Backward workspace: the row statistics (log-sum-exp, D: 2 fp32 per query
+// row, rounded up to 16 bytes), then the query parts' fp32 dK, dV records.
+size_t bwd_stats_bytes(int B, int Hq, int Nq) {
+  return (2 * (size_t)B * Hq * Nq * sizeof(float) + 15) / 16 * 16;
+}
+size_t bwd_ws_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  return bwd_stats_bytes(B, Hq, Nq) +
+         (size_t)gqa::kBwdQuerySplit * 2 * B * Hkv * Nk * d * sizeof(float);
+}
 
 int bwd_entry(const void* q, const void* k, const void* v, const void* o, const void* dout,
               void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,
@@ -619,7 +634,7 @@ int bwd_entry(const void* q, const void* k, const void* v, const void* o, const 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return fail(GQA_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
-  const size_t need = bwd_ws_bytes(B, Hq, Nq);
+  const size_t need = bwd_ws_bytes(B, Hq, Hkv, Nq, Nk, d);
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(GQA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -671,6 +686,8 @@ int bwd_entry(const void* q, const void* k, const void* v, const void* o, const 
   ba.dv = dv;
   ba.lse = reinterpret_cast<float*>(workspace);
   ba.dd = ba.lse + (size_t)B * Hq * Nq;
+  ba.part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                     bwd_stats_bytes(B, Hq, Nq));
   ba.scale = scale;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (dtype == GQA_DTYPE_BF16) return dispatch_bwd<uint16_t, CfgBf16>(ba, d, causal, hs);
@@ -778,9 +795,10 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new, 
                       Smax, d, scale, dtype, workspace, workspace_bytes, stream);
 }
 
-size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Nq) {
-  if (B < 1 || Hq < 1 || Nq < 1) return 0;
-  return bwd_ws_bytes(B, Hq, Nq);
+size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || !head_dim_ok(d) || Hq % Hkv != 0)
+    return 0;
+  return bwd_ws_bytes(B, Hq, Hkv, Nq, Nk, d);
 }
 
 int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

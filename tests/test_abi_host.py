@@ -199,7 +199,7 @@ def bwd(q=PB[0], k=PB[1], v=PB[2], o=PB[3], do=PB[4], dq=PB[5], dk=PB[6], dv=PB[
         Hkv=2, Nq=64, Nk=64, d=32, causal=0, q_offset=0, scale=0.17, dtype=BF16, ws=PB[8],
         ws_bytes=None, stream=None):
     if ws_bytes is None:
-        ws_bytes = binding.bwd_workspace_bytes(B, Hq, Nq)
+        ws_bytes = binding.bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
     return binding.lib.gqa_attn_bwd(q, k, v, o, do, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal,
                                     q_offset, ctypes.c_float(scale), dtype, ws, ws_bytes, stream)
 
@@ -222,10 +222,13 @@ def test_bwd_rejects_invalid_arguments(kw, code):
 
 def test_bwd_workspace_bytes():
     ws = binding.bwd_workspace_bytes
-    # two fp32 row statistics (log-sum-exp and D) per query row
-    assert ws(1, 32, 2048) == 2 * 32 * 2048 * 4
-    assert ws(3, 5, 7) == 2 * 3 * 5 * 7 * 4
-    assert ws(0, 1, 1) == 0 and ws(1, 1, 0) == 0
+    # two fp32 row statistics (log-sum-exp and D) per query row, rounded up to
+    # 16 bytes, then two query parts' fp32 dK and dV
+    assert ws(1, 32, 8, 2048, 2048, 128) == 2 * 32 * 2048 * 4 + 2 * 2 * 8 * 2048 * 128 * 4
+    assert ws(3, 5, 5, 7, 9, 32) == 848 + 2 * 2 * 3 * 5 * 9 * 32 * 4  # 840 bytes -> 848
+    for bad in [(0, 1, 1, 1, 1, 32), (1, 3, 2, 1, 1, 32), (1, 1, 1, 0, 1, 32),
+                (1, 1, 1, 1, 0, 32), (1, 1, 1, 1, 1, 48)]:
+        assert ws(*bad) == 0
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="valid arguments would launch on a GPU")
