@@ -22,8 +22,8 @@
 //    the query tiles of every query head of the group (this is the GQA
 //    reduction, done in registers), with S = Q K^T and dP = dO V^T, and
 //    accumulates dV^T += dO^T P and dK^T += Q^T dS.  The query steps of a
-//    key block are cut into kBwdQuerySplit parts, one workgroup each, whose
-//    fp32 results bwd_merge_kernel adds in part order.
+//    key block are cut into up to kBwdQuerySplitMax parts, one workgroup
+//    each, whose fp32 results bwd_merge_kernel adds in part order.
 // In both, a staged tile occupies two LDS stages: one holds the first
 // operand row-major (the A operand of S or S^T) with the second transposed,
 // the other the second operand row-major with the first transposed.
@@ -42,15 +42,16 @@ struct BwdArgs {
   void* dv;
   float* lse;  // [B][Hq][Nq]: m c + log2 l of each query row
   float* dd;   // [B][Hq][Nq]: D = sum_c dO O
-  float* part;  // [kBwdQuerySplit][2][B][Hkv][Nk][D] fp32: dK, dV of each query part
+  float* part;  // [qsplit][2][B][Hkv][Nk][D] fp32: dK, dV of each query part
+  int qsplit;   // query parts per key block, 1 .. kBwdQuerySplitMax
   float scale;
 };
 
-// Each K/V key block's query range is cut into this many parts, one
+// Each K/V key block's query range is cut into up to this many parts, one
 // workgroup each, so that the first key blocks of a causal launch (which
-// every query sees) do not serialise the kernel; bwd_merge_kernel adds the
-// parts' dK, dV in part order.
-constexpr int kBwdQuerySplit = 2;
+// every query sees) do not serialise the kernel and small launches still
+// fill the CUs; bwd_merge_kernel adds the parts' dK, dV in part order.
+constexpr int kBwdQuerySplitMax = 4;
 
 // Sum over this lane's elements of x * y (two B-operand fragments of one
 // column); the other half-wave holds the rest of the row.
@@ -203,7 +204,7 @@ __global__ void __launch_bounds__(C::NT) bwd_dq_kernel(BwdArgs ba) {
   }
 }
 
-// grid (ceil(Nk / (32 NW)) * kBwdQuerySplit, Hkv, B), C::NT threads: wave
+// grid (ceil(Nk / (32 NW)) * qsplit, Hkv, B), C::NT threads: wave
 // w owns keys k0 + 32 w .. k0 + 32 w + 31 of K/V head (b, hkv), over part
 // `part` of the block's query steps; it writes fp32 partial dK (scaled) and
 // dV to the part's records.
@@ -221,8 +222,8 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
   const int j = lane & 31;
   const int h2 = lane >> 5;
 
-  const int part = blockIdx.x % kBwdQuerySplit;
-  const int k0 = (blockIdx.x / kBwdQuerySplit) * 32 * C::NW;
+  const int part = blockIdx.x % ba.qsplit;
+  const int k0 = (blockIdx.x / ba.qsplit) * 32 * C::NW;
   const int hkv = blockIdx.y;
   const int b = blockIdx.z;
   const int key = k0 + 32 * w + j;
@@ -237,7 +238,7 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
   const int first = CAUSAL ? max(0, k0 - a.q_offset) / C::BC : 0;
   const int nqt = (a.Nq + C::BC - 1) / C::BC - first;  // >= 1 for launched blocks
   const int nall = a.g * nqt;  // query steps of the key block
-  const int per_part = (nall + kBwdQuerySplit - 1) / kBwdQuerySplit;
+  const int per_part = (nall + ba.qsplit - 1) / ba.qsplit;
   const int st0 = min(nall, part * per_part);
   const int nsteps = max(0, min(nall, st0 + per_part) - st0);  // this part's steps
   const float c = a.c;
@@ -359,8 +360,7 @@ __global__ void __launch_bounds__(256) bwd_merge_kernel(BwdArgs ba, long long n4
     const long long e4 = is_v ? i - half4 : i;
     const float4* src = reinterpret_cast<const float4*>(ba.part) + (is_v ? half4 : 0) + e4;
     float4 acc = src[0];
-#pragma unroll
-    for (int p = 1; p < kBwdQuerySplit; ++p) {
+    for (int p = 1; p < ba.qsplit; ++p) {
       const float4 x = src[(long long)p * n4];
       acc.x += x.x;
       acc.y += x.y;

@@ -568,7 +568,7 @@ int decode_entry(const void* q, const void* kcache, const void* vcache, const in
 // ------------------------------------------------------------------ backward
 
 template <typename T, class C, bool CAUSAL>
-int launch_bwd(gqa::BwdArgs& ba, hipStream_t stream) {
+int launch_bwd(gqa::BwdArgs& ba, int cus, hipStream_t stream) {
   (void)hipGetLastError();  // a stale error belongs to an earlier call
   hipLaunchKernelGGL((gqa::bwd_dq_kernel<T, C, CAUSAL>), dim3((unsigned)ba.f.T), dim3(C::NT), 0,
                      stream, ba);
@@ -578,8 +578,13 @@ int launch_bwd(gqa::BwdArgs& ba, hipStream_t stream) {
   // launches spread over every CU (its registers allow one wave per SIMD)
   using CK = gqa::TileCfg<T, C::D, C::BC, 2>;
   const unsigned kblocks = (unsigned)((ba.f.Nk + 32 * CK::NW - 1) / (32 * CK::NW));
+  // query parts: about 8 dK/dV waves per CU (two rounds at one resident
+  // wave per SIMD, so causal launches balance), at most kBwdQuerySplitMax
+  const long long waves = (long long)kblocks * ba.f.Hkv * ba.f.B * CK::NW;
+  long long qs = (8LL * cus + waves - 1) / waves;
+  ba.qsplit = (int)std::max(1LL, std::min<long long>(qs, gqa::kBwdQuerySplitMax));
   hipLaunchKernelGGL((gqa::bwd_dkdv_kernel<T, CK, CAUSAL>),
-                     dim3(kblocks * gqa::kBwdQuerySplit, (unsigned)ba.f.Hkv, (unsigned)ba.f.B),
+                     dim3(kblocks * (unsigned)ba.qsplit, (unsigned)ba.f.Hkv, (unsigned)ba.f.B),
                      dim3(CK::NT), 0, stream, ba);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "backward dK/dV kernel launch");
@@ -594,12 +599,17 @@ int launch_bwd(gqa::BwdArgs& ba, hipStream_t stream) {
 }
 
 template <typename T, template <int> class Cfg>
-int dispatch_bwd(gqa::BwdArgs& ba, int d, int causal, hipStream_t s) {
+int dispatch_bwd(gqa::BwdArgs& ba, int d, int causal, int cus, hipStream_t s) {
   switch (d) {
-    case 32: return causal ? launch_bwd<T, Cfg<32>, true>(ba, s) : launch_bwd<T, Cfg<32>, false>(ba, s);
-    case 64: return causal ? launch_bwd<T, Cfg<64>, true>(ba, s) : launch_bwd<T, Cfg<64>, false>(ba, s);
+    case 32:
+      return causal ? launch_bwd<T, Cfg<32>, true>(ba, cus, s)
+                    : launch_bwd<T, Cfg<32>, false>(ba, cus, s);
+    case 64:
+      return causal ? launch_bwd<T, Cfg<64>, true>(ba, cus, s)
+                    : launch_bwd<T, Cfg<64>, false>(ba, cus, s);
     default:
-      return causal ? launch_bwd<T, Cfg<128>, true>(ba, s) : launch_bwd<T, Cfg<128>, false>(ba, s);
+      return causal ? launch_bwd<T, Cfg<128>, true>(ba, cus, s)
+                    : launch_bwd<T, Cfg<128>, false>(ba, cus, s);
   }
 }
 
@@ -610,7 +620,7 @@ size_t bwd_stats_bytes(int B, int Hq, int Nq) {
 }
 size_t bwd_ws_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   return bwd_stats_bytes(B, Hq, Nq) +
-         (size_t)gqa::kBwdQuerySplit * 2 * B * Hkv * Nk * d * sizeof(float);
+         (size_t)gqa::kBwdQuerySplitMax * 2 * B * Hkv * Nk * d * sizeof(float);
 }
 
 int bwd_entry(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -690,8 +700,8 @@ int bwd_entry(const void* q, const void* k, const void* v, const void* o, const 
                                      bwd_stats_bytes(B, Hq, Nq));
   ba.scale = scale;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == GQA_DTYPE_BF16) return dispatch_bwd<uint16_t, CfgBf16>(ba, d, causal, hs);
-  return dispatch_bwd<float, CfgF32>(ba, d, causal, hs);
+  if (dtype == GQA_DTYPE_BF16) return dispatch_bwd<uint16_t, CfgBf16>(ba, d, causal, info.cus, hs);
+  return dispatch_bwd<float, CfgF32>(ba, d, causal, info.cus, hs);
 }
 
 }  // namespace

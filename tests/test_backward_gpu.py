@@ -77,6 +77,16 @@ def test_bwd_llama3_8b_shape_full():
     _check(WORKLOADS["llama3_8b_prefill"].fwd[0], seed=0)
 
 
+@pytest.mark.parametrize("s", [
+    FwdShape(1, 16, 16, 2048, 2048, 64, True, 0),  # two query parts per key block
+    FwdShape(2, 16, 16, 2048, 2048, 64, True, 0),  # enough key blocks: one part
+], ids=["two_parts", "one_part"])
+def test_bwd_query_split_counts(s):
+    """Launches large enough that each key block's query range is cut into
+    two parts, or not cut at all (the small shapes above use four)."""
+    _check(s, seed=5)
+
+
 def test_bwd_offset_past_end_is_noncausal():
     """q_offset >= Nk - 1 sees every key: the causal call equals the full one."""
     s = FwdShape(1, 4, 2, 40, 64, 64, True, 80)
