@@ -308,18 +308,32 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
     f32x16 s[C::KB], dp[C::KB];
     qk_tile<T, C>(s, kf, KsA, j, h2);   // S = Q K^T
     qk_tile<T, C>(dp, vf, KsB, j, h2);  // dP = dO V^T
+    // every row of the tile exists and sees every key of this wave: no
+    // per-element test (wave-uniform)
+    const bool whole = i0 + C::BC <= a.Nq && (!CAUSAL || k0 + 32 * w + 31 <= a.q_offset + i0);
+    if (whole) {
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // query row of accumulator register r; rows past Nq (zero Q and dO)
-        // and, when causal, rows that cannot see this key weigh exactly 0
-        const int qi = i0 + 32 * kb + key_of_reg(r, h2);
-        const bool vis = qi < a.Nq && (!CAUSAL || key <= a.q_offset + qi);
-        const float p = vis ? fast_exp2(__builtin_fmaf(s[kb][r], c, -lse_r[kb][r])) : 0.f;
-        s[kb][r] = p;
-        dp[kb][r] = p * (dp[kb][r] - dd_r[kb][r]);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse_r[kb][r]));
+          s[kb][r] = p;
+          dp[kb][r] = p * (dp[kb][r] - dd_r[kb][r]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          // query row of accumulator register r; rows past Nq (zero Q and
+          // dO) and, when causal, rows that cannot see this key weigh 0
+          const int qi = i0 + 32 * kb + key_of_reg(r, h2);
+          const bool vis = qi < a.Nq && (!CAUSAL || key <= a.q_offset + qi);
+          const float p = vis ? fast_exp2(__builtin_fmaf(s[kb][r], c, -lse_r[kb][r])) : 0.f;
+          s[kb][r] = p;
+          dp[kb][r] = p * (dp[kb][r] - dd_r[kb][r]);
+        }
+    }
     typename C::Frag pf[C::KB][C::PF], dsf[C::KB][C::PF];
     to_frag<C>(s, pf);
     to_frag<C>(dp, dsf);
