@@ -14,10 +14,11 @@
 // Two kernels, both on the forward's MFMA tile code with the operands
 // swapped around, no atomics, fixed summation order:
 //  * bwd_dq_kernel: one 128-column unit of query rows (the forward's units:
-//    the group's heads stacked over positions).  Pass 1 over the unit's key
-//    tiles gives each row's lse; pass 2 forms dS^T = P^T (dP^T - D) from
-//    S^T = K Q^T and dP^T = V dO^T and accumulates dQ^T += K^T dS^T.  It
-//    writes lse and D of its rows for the second kernel.
+//    the group's heads stacked over positions).  One pass over the unit's
+//    key tiles forms S^T = K Q^T and dP^T = V dO^T and accumulates
+//    dQ^T += K^T (E^T (dP^T - D)) with unnormalised weights E under the
+//    forward's online softmax, normalised by l at the end.  It writes lse
+//    and D of its rows for the second kernel.
 //  * bwd_dkdv_kernel: 32 keys per wave of one K/V head.  The wave walks
 //    the query tiles of every query head of the group (this is the GQA
 //    reduction, done in registers), with S = Q K^T and dP = dO V^T, and
@@ -137,35 +138,16 @@ __global__ void __launch_bounds__(C::NT) bwd_dq_kernel(BwdArgs ba) {
   const int lim = (CAUSAL && col.valid) ? min(a.q_offset + col.i, a.Nk - 1) : a.Nk - 1;
   const float c = a.c;
 
-  // ---- pass 1: row maxima and sums over the visible keys.  Key 0 is
-  // visible to every row, so the first tile makes m finite in every lane.
+  // ---- one pass over the unit's key tiles.  dQ_i = (1 / l_i) sum_j e_ij
+  // (dP_ij - D_i) K_j is linear in the unnormalised weights e_ij, so it is
+  // accumulated with the forward's online softmax: weights against a running
+  // reference m, raised lazily (acc and l rescaled), divided by l at the end,
+  // where lse = m c + log2 l also falls out for the dK/dV kernel.
   TileRegs<C> ra, rb;
-  float m = kNegInf, l = 0.f;
-  load_tile<T, C>(ra, kbase, vbase, 0, a.Nk, tid, a.kv_rowb);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();
-    store_tile<T, C>(ra, KsA, VsA, tid);
-    __syncthreads();
-    if (kt + 1 < ntiles) load_tile<T, C>(ra, kbase, vbase, (kt + 1) * C::BC, a.Nk, tid, a.kv_rowb);
-    f32x16 s[C::KB];
-    qk_tile<T, C>(s, qf, KsA, j, h2);
-    const int key0 = kt * C::BC;
-    if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
-    const float mn = fmaxf(m, tile_rowmax<C>(s));
-    float lt = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) lt += fast_exp2(__builtin_fmaf(s[kb][r], c, -mn * c));
-    l = l * fast_exp2((m - mn) * c) + lt;
-    m = mn;
-  }
-  const float lse = m * c + log2f(halves_sum(l));
-
-  // ---- pass 2: dQ^T += K^T dS^T over the same tiles
   f32x16 acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  float m = kNegInf, l = 0.f;
   load_tile<T, C>(ra, kbase, vbase, 0, a.Nk, tid, a.kv_rowb);
   load_tile<T, C>(rb, vbase, kbase, 0, a.Nk, tid, a.kv_rowb);
   for (int kt = 0; kt < ntiles; ++kt) {
@@ -182,20 +164,27 @@ __global__ void __launch_bounds__(C::NT) bwd_dq_kernel(BwdArgs ba) {
     qk_tile<T, C>(dp, dof, KsB, j, h2);  // dP^T = V dO^T
     const int key0 = kt * C::BC;
     if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
+    // key 0 is visible to every row, so the first tile raises m in every lane
+    const float mt = tile_rowmax<C>(s);
+    if (__any(mt > m + a.thr)) raise_reference<C>(m, l, acc, mt, c);
+    const float mc = m * c;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse));  // masked: 0
-        s[kb][r] = p * (dp[kb][r] - Dv);
+        const float e = fast_exp2(__builtin_fmaf(s[kb][r], c, -mc));  // masked: 0
+        l += e;
+        s[kb][r] = e * (dp[kb][r] - Dv);
       }
     typename C::Frag dsf[C::KB][C::PF];
     to_frag<C>(s, dsf);
-    pv_tile<T, C>(acc, dsf, VsB, j, h2);  // dQ^T += K^T dS^T
+    pv_tile<T, C>(acc, dsf, VsB, j, h2);  // dQ^T += K^T dS^T (unnormalised)
   }
+  const float lsum = halves_sum(l);
+  const float lse = m * c + log2f(lsum);
 
   if (col.valid) {
-    store_out_row<T, C>(reinterpret_cast<T*>(ba.dq) + col.row_off, acc, ba.scale, h2);
+    store_out_row<T, C>(reinterpret_cast<T*>(ba.dq) + col.row_off, acc, ba.scale / lsum, h2);
     if (h2 == 0) {
       const size_t row = col.row_off / C::D;  // contiguous rows
       ba.lse[row] = lse;
