@@ -606,7 +606,7 @@ def main(argv=None):
             "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "algorithmic_gflop": round(bwd_flops(ps) / 1e9, 4),
             "note": "gqa_attn_bwd: dQ kernel (one pass, online softmax, row statistics), "
-                    "dK/dV kernel (query range of each key block in up to 4 parts) and their "
+                    "dK/dV kernel (query range of each key block in up to 8 parts) and their "
                     "merge; 5 contractions counted (the kernels execute 6: S twice)"}
         extra.update(time_decode_sweep(20, 3))
         result["other_workloads"] = extra

@@ -180,8 +180,10 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new,
 /*
  * Bytes of device workspace gqa_attn_bwd needs for these sizes: two fp32
  * row statistics per query row (B * Hq * Nq rows, rounded up to 16 bytes),
- * then up to four fp32 partial copies of dk and dv (4 * 2 * B * Hkv * Nk * d
- * floats).  Returns 0 for invalid sizes.
+ * then, when the K/V side is small (fewer than 256 * 16 waves of 32 keys),
+ * P = min(8, ceil(4096 / (ceil(Nk / 64) * Hkv * B * 2))) fp32 partial copies
+ * of dk and dv (P * 2 * B * Hkv * Nk * d floats).  Returns 0 for invalid
+ * sizes.
  */
 size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
@@ -207,12 +209,12 @@ size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int 
  * workspace: device memory of at least gqa_attn_bwd_workspace_bytes(B, Hq,
  * Hkv, Nq, Nk, d) bytes, owned by the caller, contents on entry irrelevant;
  * it receives each row's log-sum-exp and D, and the fp32 dk, dv of the
- * parts (up to four) each key block's query range is cut into, added in a
+ * parts (up to eight) each key block's query range is cut into, added in a
  * fixed order at the end.  scale must be finite and > 0
  * (GQA_ERR_UNSUPPORTED otherwise).  Outputs must not alias inputs.  Other
  * status codes and error behaviour as gqa_attn_fwd (plus GQA_ERR_WORKSPACE).
- * Three launches on the stream: dq (with the row statistics), the dk/dv
- * parts, and their merge.
+ * Launches on the stream: dq (with the row statistics), dk/dv, and, with
+ * more than one query part, the merge of the parts.
  */
 int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  void* dq, void* dk, void* dv,

@@ -52,7 +52,8 @@ struct BwdArgs {
 // workgroup each, so that the first key blocks of a causal launch (which
 // every query sees) do not serialise the kernel and small launches still
 // fill the CUs; bwd_merge_kernel adds the parts' dK, dV in part order.
-constexpr int kBwdQuerySplitMax = 4;
+// With one part the kernel writes dK, dV itself.
+constexpr int kBwdQuerySplitMax = 8;
 
 // Sum over this lane's elements of x * y (two B-operand fragments of one
 // column); the other half-wave holds the rest of the row.
@@ -330,7 +331,10 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
     pv_tile<T, C>(acc_dk, dsf, VsB, j, h2);  // dK^T += Q^T dS
   }
 
-  if (kvalid) {
+  if (kvalid && ba.qsplit == 1) {  // one part: the result itself
+    store_out_row<T, C>(reinterpret_cast<T*>(ba.dk) + key_row, acc_dk, ba.scale, h2);
+    store_out_row<T, C>(reinterpret_cast<T*>(ba.dv) + key_row, acc_dv, 1.0f, h2);
+  } else if (kvalid) {
     // records [part][dK, dV][b][hkv][key][D], fp32; this lane holds
     // d = 32 db + 8 q4 + 4 h2 + 0..3
     const size_t rows = (size_t)a.B * a.Hkv * a.Nk;

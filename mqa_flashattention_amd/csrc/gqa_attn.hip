@@ -567,8 +567,31 @@ int decode_entry(const void* q, const void* kcache, const void* vcache, const in
 
 // ------------------------------------------------------------------ backward
 
+// Query parts per dK/dV key block (64 keys, two waves): about 16 dK/dV waves
+// per CU of a 256-CU gfx950 part (four rounds at one resident wave per
+// SIMD, so causal launches balance), at most kBwdQuerySplitMax.  A function
+// of the shape alone, so that the workspace query and the launch agree.
+constexpr long long kBwdSplitWaves = 16LL * 256;
+int bwd_query_parts(int B, int Hkv, int Nk) {
+  const long long waves = (long long)((Nk + 63) / 64) * Hkv * B * 2;
+  const long long qs = (kBwdSplitWaves + waves - 1) / waves;
+  return (int)std::max(1LL, std::min<long long>(qs, gqa::kBwdQuerySplitMax));
+}
+
+// Backward workspace: the row statistics (log-sum-exp, D: 2 fp32 per query
+// row, rounded up to 16 bytes), then, with more than one query part, the
+// parts' fp32 dK, dV records.
+size_t bwd_stats_bytes(int B, int Hq, int Nq) {
+  return (2 * (size_t)B * Hq * Nq * sizeof(float) + 15) / 16 * 16;
+}
+size_t bwd_ws_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  const int qs = bwd_query_parts(B, Hkv, Nk);
+  return bwd_stats_bytes(B, Hq, Nq) +
+         (qs > 1 ? (size_t)qs * 2 * B * Hkv * Nk * d * sizeof(float) : 0);
+}
+
 template <typename T, class C, bool CAUSAL>
-int launch_bwd(gqa::BwdArgs& ba, int cus, hipStream_t stream) {
+int launch_bwd(gqa::BwdArgs& ba, hipStream_t stream) {
   (void)hipGetLastError();  // a stale error belongs to an earlier call
   hipLaunchKernelGGL((gqa::bwd_dq_kernel<T, C, CAUSAL>), dim3((unsigned)ba.f.T), dim3(C::NT), 0,
                      stream, ba);
@@ -578,16 +601,13 @@ int launch_bwd(gqa::BwdArgs& ba, int cus, hipStream_t stream) {
   // launches spread over every CU (its registers allow one wave per SIMD)
   using CK = gqa::TileCfg<T, C::D, C::BC, 2>;
   const unsigned kblocks = (unsigned)((ba.f.Nk + 32 * CK::NW - 1) / (32 * CK::NW));
-  // query parts: about 8 dK/dV waves per CU (two rounds at one resident
-  // wave per SIMD, so causal launches balance), at most kBwdQuerySplitMax
-  const long long waves = (long long)kblocks * ba.f.Hkv * ba.f.B * CK::NW;
-  long long qs = (8LL * cus + waves - 1) / waves;
-  ba.qsplit = (int)std::max(1LL, std::min<long long>(qs, gqa::kBwdQuerySplitMax));
+  ba.qsplit = bwd_query_parts(ba.f.B, ba.f.Hkv, ba.f.Nk);
   hipLaunchKernelGGL((gqa::bwd_dkdv_kernel<T, CK, CAUSAL>),
                      dim3(kblocks * (unsigned)ba.qsplit, (unsigned)ba.f.Hkv, (unsigned)ba.f.B),
                      dim3(CK::NT), 0, stream, ba);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "backward dK/dV kernel launch");
+  if (ba.qsplit == 1) return GQA_OK;
   const long long n4 = 2LL * ba.f.B * ba.f.Hkv * ba.f.Nk * C::D / 4;
   long long mblocks = (n4 + 255) / 256;
   if (mblocks > 4096) mblocks = 4096;
@@ -599,28 +619,13 @@ int launch_bwd(gqa::BwdArgs& ba, int cus, hipStream_t stream) {
 }
 
 template <typename T, template <int> class Cfg>
-int dispatch_bwd(gqa::BwdArgs& ba, int d, int causal, int cus, hipStream_t s) {
+int dispatch_bwd(gqa::BwdArgs& ba, int d, int causal, hipStream_t s) {
   switch (d) {
-    case 32:
-      return causal ? launch_bwd<T, Cfg<32>, true>(ba, cus, s)
-                    : launch_bwd<T, Cfg<32>, false>(ba, cus, s);
-    case 64:
-      return causal ? launch_bwd<T, Cfg<64>, true>(ba, cus, s)
-                    : launch_bwd<T, Cfg<64>, false>(ba, cus, s);
+    case 32: return causal ? launch_bwd<T, Cfg<32>, true>(ba, s) : launch_bwd<T, Cfg<32>, false>(ba, s);
+    case 64: return causal ? launch_bwd<T, Cfg<64>, true>(ba, s) : launch_bwd<T, Cfg<64>, false>(ba, s);
     default:
-      return causal ? launch_bwd<T, Cfg<128>, true>(ba, cus, s)
-                    : launch_bwd<T, Cfg<128>, false>(ba, cus, s);
+      return causal ? launch_bwd<T, Cfg<128>, true>(ba, s) : launch_bwd<T, Cfg<128>, false>(ba, s);
   }
-}
-
-// Backward workspace: the row statistics (log-sum-exp, D: 2 fp32 per query
-// row, rounded up to 16 bytes), then the query parts' fp32 dK, dV records.
-size_t bwd_stats_bytes(int B, int Hq, int Nq) {
-  return (2 * (size_t)B * Hq * Nq * sizeof(float) + 15) / 16 * 16;
-}
-size_t bwd_ws_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
-  return bwd_stats_bytes(B, Hq, Nq) +
-         (size_t)gqa::kBwdQuerySplitMax * 2 * B * Hkv * Nk * d * sizeof(float);
 }
 
 int bwd_entry(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -700,8 +705,8 @@ int bwd_entry(const void* q, const void* k, const void* v, const void* o, const 
                                      bwd_stats_bytes(B, Hq, Nq));
   ba.scale = scale;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == GQA_DTYPE_BF16) return dispatch_bwd<uint16_t, CfgBf16>(ba, d, causal, info.cus, hs);
-  return dispatch_bwd<float, CfgF32>(ba, d, causal, info.cus, hs);
+  if (dtype == GQA_DTYPE_BF16) return dispatch_bwd<uint16_t, CfgBf16>(ba, d, causal, hs);
+  return dispatch_bwd<float, CfgF32>(ba, d, causal, hs);
 }
 
 }  // namespace

@@ -78,12 +78,13 @@ def test_bwd_llama3_8b_shape_full():
 
 
 @pytest.mark.parametrize("s", [
-    FwdShape(1, 16, 16, 2048, 2048, 64, True, 0),  # two query parts per key block
-    FwdShape(2, 16, 16, 2048, 2048, 64, True, 0),  # enough key blocks: one part
-], ids=["two_parts", "one_part"])
+    FwdShape(1, 16, 16, 2048, 2048, 64, True, 0),  # four query parts per key block
+    FwdShape(2, 16, 16, 2048, 2048, 64, True, 0),  # two
+    FwdShape(4, 16, 16, 2048, 2048, 64, True, 0),  # one: dK, dV written directly
+], ids=["four_parts", "two_parts", "one_part"])
 def test_bwd_query_split_counts(s):
     """Launches large enough that each key block's query range is cut into
-    two parts, or not cut at all (the small shapes above use four)."""
+    four or two parts, or not cut at all (the small shapes above use eight)."""
     _check(s, seed=5)
 
 
