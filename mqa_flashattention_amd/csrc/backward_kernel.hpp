@@ -101,7 +101,8 @@ __device__ __forceinline__ void to_frag(const f32x16 (&x)[C::KB],
 // descending order, all heads of a block together), so that the light
 // units fill in behind the heavy ones instead of ending the launch.
 template <typename T, class C, bool CAUSAL>
-__global__ void __launch_bounds__(C::NT) bwd_dq_kernel(BwdArgs ba) {
+__global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+bwd_dq_kernel(BwdArgs ba) {
   const PrefillArgs& a = ba.f;
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
   T* const KsA = reinterpret_cast<T*>(smem);  // K row-major (V transposed, unused)
