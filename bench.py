@@ -47,8 +47,8 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "prefill_llama3_8b_counters.json")
-KERNEL_SOURCES = ["attn_tile.hpp", "prefill_kernel.hpp", "decode_kernel.hpp", "backward_kernel.hpp",
-                  "gqa_attn.hip"]
+KERNEL_SOURCES = ["attn_tile.hpp", "prefill_kernel.hpp", "decode_kernel.hpp", "mixed_kernel.hpp",
+                  "backward_kernel.hpp", "gqa_attn.hip"]
 DECODE_SETS = 48  # 48 x 16 MiB of caches > 256 MB Infinity Cache
 COPY_BYTES = 256 * 1024 * 1024  # calibration copy: reads and writes this many bytes
 
@@ -333,6 +333,62 @@ def time_bwd_workload(s, steps, warmup):
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
+def time_mixed_workload(w, steps, warmup, sets=3):
+    """Event-timed average duration (ms) of one gqa_attn_mixed call (the
+    persistent launch and the decode combine), and of the same work as two
+    calls (gqa_attn_fwd on the chunk, then gqa_attn_decode), after a parity
+    check of both outputs against the oracle.  The decode caches cycle over
+    `sets` copies (more bytes than the Infinity Cache holds), so each call
+    reads them from HBM as a serving step would."""
+    import numpy as np
+    import torch
+
+    import oracle  # test infrastructure: parity gate only
+    from mqa_flashattention_amd import (attn_decode, attn_fwd, attn_mixed,
+                                        decode_workspace_bytes)
+    from mqa_flashattention_amd.workloads import mixed_inputs
+    c, r = w.fwd[0], w.decode
+    host = mixed_inputs(c, r, 0)
+    q, k, v = (t.cuda() for t in host[:3])
+    qd, sl = host[3].cuda(), host[6].cuda()
+    caches = [(host[4].cuda(), host[5].cuda())]
+    caches += [(torch.roll(caches[0][0], i, 2).contiguous(), torch.roll(caches[0][1], i, 2).contiguous())
+               for i in range(1, sets)]
+    ws = torch.empty(decode_workspace_bytes(r.B, r.Hq, r.Hkv, r.Smax, r.d), dtype=torch.uint8,
+                     device=q.device)
+    o, od = attn_mixed(q, k, v, c.q_offset, qd, *caches[0], sl, scale=c.scale, workspace=ws)
+    torch.cuda.synchronize()
+    ids = np.unique(np.random.default_rng(5).integers(0, c.B * c.Hq * c.Nq, 64))
+    ref = oracle.attn_fwd_rows(host[0], host[1], host[2], ids, causal=True, q_offset=c.q_offset,
+                               scale=c.scale)
+    check(o.reshape(-1, c.d)[torch.from_numpy(ids).cuda()], ref, 2e-2, "mixed batch chunk")
+    check(od, oracle.attn_decode(host[3], host[4], host[5], host[6], scale=c.scale), 2e-2,
+          "mixed batch decode rows")
+
+    def mixed(i):
+        attn_mixed(q, k, v, c.q_offset, qd, *caches[i % sets], sl, scale=c.scale, out=o,
+                   out_decode=od, workspace=ws)
+
+    def separate(i):
+        attn_fwd(q, k, v, causal=True, q_offset=c.q_offset, scale=c.scale, out=o)
+        attn_decode(qd, *caches[i % sets], sl, scale=c.scale, out=od, workspace=ws)
+
+    res = []
+    for fn in (mixed, separate):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        res.append(float(np.mean([a.elapsed_time(b) for a, b in ev])))
+    return res[0], res[1], sl
+
+
 # Supplementary decode sweep: the batch-8 shape (Hq 12, Hkv 2, d 128) at more
 # rows and longer contexts, lengths uniform in [Smax/4, Smax] as for the
 # batch-8 workload's [512, 2048].  It shows how close the decode kernels come
@@ -608,6 +664,16 @@ def main(argv=None):
             "note": "gqa_attn_bwd: dQ kernel (one pass, online softmax, row statistics), "
                     "dK/dV kernel (query range of each key block in up to 8 parts) and their "
                     "merge; 5 contractions counted (the kernels execute 6: S twice)"}
+        wm = WORKLOADS["llama3_8b_mixed"]
+        ms, ms_sep, lens_m = time_mixed_workload(wm, max(20, K), 5)
+        extra["llama3_8b_mixed"] = {
+            "ms": round(ms, 5), "ms_as_two_calls": round(ms_sep, 5),
+            "speedup_vs_two_calls": round(ms_sep / ms, 4),
+            "chunk_gflop": round(prefill_flops(wm.fwd[0]) / 1e9, 4),
+            "decode_mb": round(decode_bytes(wm.decode, lens_m) / 1e6, 4),
+            "note": "gqa_attn_mixed: the 512-query chunk and 8 decode rows in one persistent "
+                    "launch + the decode combine, against gqa_attn_fwd then gqa_attn_decode; "
+                    "decode caches HBM-cold"}
         extra.update(time_decode_sweep(20, 3))
         result["other_workloads"] = extra
 

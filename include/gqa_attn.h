@@ -178,6 +178,54 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new,
                            int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Mixed batch of one layer in one persistent launch: the causal query chunk
+ * of a chunked prefill and single-token decode rows.
+ *
+ *   chunk (B >= 0 sequences; B == 0: none, and q, k, v, o may be NULL):
+ *     q, o            : [B, Hq, Nq, d]
+ *     k, v            : [B, Hkv, Nk, d]
+ *     query row i sits at position q_offset + i and sees keys
+ *     j <= min(q_offset + i, Nk - 1) -- gqa_attn_fwd with causal = 1.
+ *   decode rows (Bd >= 0; Bd == 0: none, and qd, kcache, vcache, seqlens,
+ *   od, workspace may be NULL):
+ *     qd, od          : [Bd, Hq, d]
+ *     kcache, vcache  : [Bd, Hkv, Smax, d]
+ *     seqlens         : int32[Bd], device memory
+ *     row b attends cache slots [0, clamp(seqlens[b], 0, Smax)) --
+ *     gqa_attn_decode.
+ *   Hq, Hkv, d, scale and dtype are shared by both parts (one layer).
+ *
+ * The kaispace.site note "Chunked Prefill" describes the batch: prefill
+ * chunks (compute-bound) beside decode tokens (memory-bound).  Both come
+ * from one persistent launch whose workgroups take the chunk's units (the
+ * GQA head mapping and heaviest-first unit queues of the persistent prefill
+ * schedule) and then the decode splits from the same counters -- the
+ * "Kernel 10" of the BootstrapAI evolution log, persistent scheduling with
+ * the GQA head mapping -- so decode work fills the CUs the chunk leaves
+ * idle.  A second launch merges the decode rows' split states.  The decode
+ * rows' outputs equal gqa_attn_decode's bit for bit; the chunk's are those
+ * of gqa_attn_fwd's persistent schedule (the same to within rounding order
+ * when gqa_attn_fwd chooses another schedule).
+ *
+ * workspace: at least gqa_attn_decode_workspace_bytes(Bd, Hq, Hkv, Smax, d)
+ * bytes when Bd > 0, as for gqa_attn_decode.  Calls that may run
+ * concurrently must use different streams (each stream has its own
+ * scheduler counters) and different workspaces.
+ *
+ * Errors: B < 0 or Bd < 0 -> GQA_ERR_BAD_SHAPE; a NULL pointer of a part
+ * that is present -> GQA_ERR_NULL_POINTER; otherwise each present part is
+ * checked as gqa_attn_fwd / gqa_attn_decode check it, with the same codes.
+ * B == Bd == 0 returns GQA_OK with nothing launched.  On any error nothing
+ * is launched.
+ */
+int gqa_attn_mixed(const void* q, const void* k, const void* v, void* o,
+                   int B, int Nq, int Nk, int q_offset,
+                   const void* qd, const void* kcache, const void* vcache,
+                   const int32_t* seqlens, void* od, int Bd, int Smax,
+                   int Hq, int Hkv, int d, float scale, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace gqa_attn_bwd needs for these sizes: two fp32
  * row statistics per query row (B * Hq * Nq rows, rounded up to 16 bytes),
  * then, when the K/V side is small (fewer than 256 * 16 waves of 32 keys),

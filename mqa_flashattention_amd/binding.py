@@ -28,7 +28,8 @@ STATUS_NAMES = {
 }
 EXPORTED = ("gqa_attn_fwd", "gqa_attn_fwd_strided", "gqa_attn_decode",
             "gqa_attn_decode_append", "gqa_attn_decode_workspace_bytes", "gqa_attn_bwd",
-            "gqa_attn_bwd_workspace_bytes", "gqa_status_string", "gqa_last_error_string")
+            "gqa_attn_bwd_workspace_bytes", "gqa_attn_mixed", "gqa_status_string",
+            "gqa_last_error_string")
 
 
 class GqaError(RuntimeError):
@@ -62,6 +63,9 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp,
                                  sz, vp]
     lib.gqa_attn_bwd.restype = i
+    lib.gqa_attn_mixed.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, vp, vp, vp, vp, i, i, i, i, i,
+                                   f, i, vp, sz, vp]
+    lib.gqa_attn_mixed.restype = i
     lib.gqa_status_string.argtypes = [i]
     lib.gqa_status_string.restype = ctypes.c_char_p
     lib.gqa_last_error_string.argtypes = []
@@ -320,3 +324,83 @@ def attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor
                                         _stream_handle(dev))
     _raise(st)
     return out
+
+
+def attn_mixed(q: torch.Tensor | None, k: torch.Tensor | None, v: torch.Tensor | None,
+               q_offset: int, qd: torch.Tensor | None, kcache: torch.Tensor | None,
+               vcache: torch.Tensor | None, seqlens: torch.Tensor | None, *,
+               scale: float | None = None, out: torch.Tensor | None = None,
+               out_decode: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None):
+    """A chunked-prefill chunk and decode rows in one launch via gqa_attn_mixed.
+
+    Chunk: q [B, Hq, Nq, d], k, v [B, Hkv, Nk, d], causal, query row i at
+    position q_offset + i (q is None: no chunk).  Decode rows: qd [Bd, Hq, d],
+    kcache, vcache [Bd, Hkv, Smax, d], seqlens int32 [Bd] (qd is None: no
+    decode rows).  Returns (o, od); the missing part's entry is None."""
+    ref = q if q is not None else qd
+    if ref is None:
+        return None, None
+    if ref.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {ref.dtype}")
+    dev = ref.device
+    B = Nq = Nk = 0
+    Bd = Smax = 0
+    Hq, d = ref.shape[1], ref.shape[-1]
+    Hkv = (k if q is not None else kcache).shape[1]
+    nul = ctypes.c_void_p(0)
+    ptrs = [nul] * 4
+    if q is not None:
+        _check_tensor("q", q, 4, ref.dtype, dev)
+        _check_tensor("k", k, 4, ref.dtype, dev)
+        _check_tensor("v", v, 4, ref.dtype, dev)
+        B, _, Nq, _ = q.shape
+        Nk = k.shape[2]
+        if (tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != tuple(k.shape)
+                or q.shape[1] != Hq or q.shape[3] != d):
+            raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+        if out is None:
+            out = torch.empty_like(q)
+        else:
+            _check_tensor("out", out, 4, ref.dtype, dev)
+            if tuple(out.shape) != tuple(q.shape):
+                raise ValueError("out must have the shape of q")
+        ptrs = [q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr()]
+    else:
+        out = None
+    dptrs = [nul] * 5
+    ws_ptr, ws_bytes = nul, 0
+    if qd is not None:
+        _check_tensor("qd", qd, 3, ref.dtype, dev)
+        _check_tensor("kcache", kcache, 4, ref.dtype, dev)
+        _check_tensor("vcache", vcache, 4, ref.dtype, dev)
+        _check_tensor("seqlens", seqlens, 1, torch.int32, dev)
+        Bd = qd.shape[0]
+        Smax = kcache.shape[2]
+        if (tuple(qd.shape) != (Bd, Hq, d) or tuple(kcache.shape) != (Bd, Hkv, Smax, d)
+                or tuple(vcache.shape) != tuple(kcache.shape) or seqlens.shape[0] != Bd):
+            raise ValueError(f"shape mismatch qd{tuple(qd.shape)} kcache{tuple(kcache.shape)}")
+        if out_decode is None:
+            out_decode = torch.empty_like(qd)
+        else:
+            _check_tensor("out_decode", out_decode, 3, ref.dtype, dev)
+            if tuple(out_decode.shape) != tuple(qd.shape):
+                raise ValueError("out_decode must have the shape of qd")
+        need = decode_workspace_bytes(Bd, Hq, Hkv, Smax, d)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        elif workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the GPU of the inputs")
+        dptrs = [qd.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), seqlens.data_ptr(),
+                 out_decode.data_ptr()]
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    else:
+        out_decode = None
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(dev):
+        st = lib.gqa_attn_mixed(*ptrs, B, Nq, Nk, int(q_offset), *dptrs, Bd, Smax, Hq, Hkv, d,
+                                float(scale), _DTYPES[ref.dtype], ws_ptr, ws_bytes,
+                                _stream_handle(dev))
+    _raise(st)
+    return out, out_decode

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = [os.path.join(CSRC, "gqa_attn.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("attn_tile.hpp", "prefill_kernel.hpp",
-                                           "decode_kernel.hpp", "backward_kernel.hpp")] + [
+                                           "decode_kernel.hpp", "mixed_kernel.hpp",
+                                           "backward_kernel.hpp")] + [
     os.path.join(INCLUDE, "gqa_attn.h")]
 LIBRARY = os.path.join(PKG, "libgqa_attn.so")
 ARCH = "gfx950"

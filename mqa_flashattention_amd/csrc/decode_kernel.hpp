@@ -82,25 +82,39 @@ __device__ __forceinline__ void patch_row(T* __restrict__ Ks, T* __restrict__ Vs
   }
 }
 
-// grid (NS, Hkv * NCB, B), one wavefront per block.
-template <typename T, class C, bool APPEND>
-__global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
+// Orders one wave's LDS writes before its later LDS reads (and the reads
+// before later writes).  WAVE: the wave runs alone in its LDS area while
+// other waves of its workgroup do other work, so only the wave itself is
+// ordered -- a wave's LDS operations complete in issue order, so keeping
+// the compiler from moving them across this point is enough.  Otherwise a
+// workgroup barrier (the workgroup is the one wave).
+template <bool WAVE>
+__device__ __forceinline__ void split_sync() {
+  if constexpr (WAVE) {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  } else {
+    __syncthreads();
+  }
+}
+
+// Split s_idx of row b for column block y = hkv * NCB + cb, run by one
+// wavefront (lane 0..63) in the LDS area smem (C::STAGE_BYTES): reads the
+// split's cache tiles, and writes its partial state for the combine pass.
+template <typename T, class C, bool APPEND, bool WAVE>
+__device__ __forceinline__ void decode_split(const DecodeArgs& a, char* smem, int s_idx, int y,
+                                             int b, int lane) {
   static_assert(C::NW == 1 && C::BC == 32, "decode works in single-wave 32-token tiles");
-  __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
   T* const Ks = reinterpret_cast<T*>(smem);
   T* const Vs = Ks + C::K_ELEMS;
 
-  const int s_idx = blockIdx.x;
-  const int hkv = blockIdx.y / a.NCB;
-  const int cb = blockIdx.y % a.NCB;
-  const int b = blockIdx.z;
+  const int hkv = y / a.NCB;
+  const int cb = y % a.NCB;
   const int n = row_len<APPEND>(a, b);
   const int start = s_idx * a.S_TOK;
   if (start >= n) return;
   const int end = min(n, start + a.S_TOK);
   const int ntok = end - start;
-
-  const int lane = threadIdx.x;
 
   // append: the split holding the new token's slot (the row's last) loads
   // the new rows, stores them into the caches (first column block only) and
@@ -145,33 +159,41 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
-  // Two register stages: the loads of tiles t+1 and t+2 are in flight while
-  // tile t is computed, so a split of up to two tiles costs one memory
-  // round trip.  The loop is unrolled by two so each stage is a named
-  // register set (an indexed pair would be placed in scratch memory).
+  // Register stages: the loads of the next NSTG tiles are in flight while
+  // tile t is computed.  Two in the decode kernel (one resident wave per
+  // SIMD), so a split of up to two tiles costs one memory round trip; one
+  // in a workgroup of the mixed kernel, whose register budget (two waves
+  // per SIMD) holds one stage -- the same bytes in flight per SIMD.  With
+  // two, the loop is unrolled by two so each stage is a named register set
+  // (an indexed pair would be placed in scratch memory).
+  constexpr int NSTG = WAVE ? 1 : 2;
   const int ntiles = (ntok + 31) / 32;
   TileRegs<C> ra, rb;
   load_tile<T, C>(ra, kbase, vbase, 0, ntok, lane, C::D * C::ESZ);
-  if (ntiles > 1) load_tile<T, C>(rb, kbase, vbase, 32, ntok, lane, C::D * C::ESZ);
+  if (NSTG > 1 && ntiles > 1) load_tile<T, C>(rb, kbase, vbase, 32, ntok, lane, C::D * C::ESZ);
 
   auto step = [&](TileRegs<C>& regs, int kt) {
     store_tile<T, C>(regs, Ks, Vs, lane);
     if constexpr (APPEND) {
       if (kt == new_tile && lane < CH) patch_row<T, C>(Ks, Vs, new_row, lane, nk, nv);
     }
-    __syncthreads();
-    if (kt + 2 < ntiles)
-      load_tile<T, C>(regs, kbase, vbase, (kt + 2) * 32, ntok, lane, C::D * C::ESZ);
+    split_sync<WAVE>();
+    if (kt + NSTG < ntiles)
+      load_tile<T, C>(regs, kbase, vbase, (kt + NSTG) * 32, ntok, lane, C::D * C::ESZ);
     f32x16 s[C::KB];
     qk_tile<T, C>(s, qf, Ks, j, h2);
     const int key0 = kt * 32;
     if (key0 + 32 > ntok) mask_tile<C>(s, key0, ntok - 1, h2);
     softmax_pv_step<T, C>(s, mrun, lrun, acc, Vs, j, h2, a.c, a.thr);
-    __syncthreads();
+    split_sync<WAVE>();
   };
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    step(ra, kt);
-    if (kt + 1 < ntiles) step(rb, kt + 1);
+  if constexpr (NSTG == 1) {
+    for (int kt = 0; kt < ntiles; ++kt) step(ra, kt);
+  } else {
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      step(ra, kt);
+      if (kt + 1 < ntiles) step(rb, kt + 1);
+    }
   }
 
   const float lsum = halves_sum(lrun);
@@ -191,6 +213,13 @@ __global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
       part[C::D + 1] = lsum;
     }
   }
+}
+
+// grid (NS, Hkv * NCB, B), one wavefront per block.
+template <typename T, class C, bool APPEND>
+__global__ void __launch_bounds__(64) decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
+  decode_split<T, C, APPEND, false>(a, smem, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x);
 }
 
 // grid (Hq, B), 256 threads.  Thread t takes 16-byte chunk t % (D/4) of

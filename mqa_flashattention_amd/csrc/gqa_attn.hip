@@ -4,7 +4,7 @@
 // gfx950 device check, the per-(device, stream) scheduler counters, choice
 // of the unit decomposition and split size, and the kernel launches.  All
 // arithmetic runs in the kernels of prefill_kernel.hpp / decode_kernel.hpp /
-// backward_kernel.hpp.
+// mixed_kernel.hpp / backward_kernel.hpp.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -21,6 +21,7 @@
 #include "backward_kernel.hpp"
 #include "decode_kernel.hpp"
 #include "gqa_attn.h"
+#include "mixed_kernel.hpp"
 #include "prefill_kernel.hpp"
 
 namespace {
@@ -112,13 +113,13 @@ hipError_t zero_ints(int* p, long long n, hipStream_t stream) {
 }
 
 // Device memory the library keeps per (device, stream):
-//  * ctr: one counter per work queue plus a finished-workgroup count, zeroed
-//    in stream order when allocated; each persistent launch leaves them at
-//    zero when it ends;
+//  * ctr: one counter per work queue, a finished-workgroup count and the
+//    mixed launch's decode-split counter, zeroed in stream order when
+//    allocated; each persistent launch leaves them at zero when it ends;
 //  * ws: partial records of the prefill units that the balanced schedule
 //    cuts, grown on demand (after
 //    the stream drains, so no queued launch still uses the old buffer).
-constexpr int kCounterInts = (gqa::kNumQueues + 1) * gqa::kCounterStride;
+constexpr int kCounterInts = (gqa::kMixedDecodeCounter + 1) * gqa::kCounterStride;
 struct StreamState {
   int* ctr = nullptr;
   float* ws = nullptr;
@@ -421,12 +422,13 @@ size_t decode_ws_bytes(int B, int Hq, int smax, int d, int split) {
   return (size_t)B * Hq * ns * (size_t)(d + 4) * sizeof(float);
 }
 
-// Shared body of the two forward entry points: qs / kvs are element strides
-// {batch, head, token} of Q and O / of K and V (the head dimension is
-// contiguous); pointers and strides are already checked for NULL.
-int fwd_entry(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+// Validation and launch arguments of a forward call (everything but the
+// schedule): qs / kvs are element strides {batch, head, token} of Q and O /
+// of K and V (the head dimension is contiguous); pointers and strides are
+// already checked for NULL.  Pure host code: no HIP call.
+int fwd_setup(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
               int Nq, int Nk, int d, const int64_t* qs, const int64_t* kvs, int causal,
-              int q_offset, float scale, int dtype, void* stream) {
+              int q_offset, float scale, int dtype, gqa::PrefillArgs* out) {
   // ---- validation: host only, before any HIP call
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1)
     return fail(GQA_ERR_BAD_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d)", B,
@@ -453,15 +455,8 @@ int fwd_entry(const void* q, const void* k, const void* v, void* o, int B, int H
   const long long T = (long long)B * Hkv * HB * NQB;
   if (T > kIntMax) return fail(GQA_ERR_BAD_SHAPE, "too many work units (%lld)", T);
 
-  // ---- device
-  int dev = 0;
-  DeviceInfo info;
-  int st = current_device(&dev, &info);
-  if (st != GQA_OK) return st;
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-
   const int esz = dtype == GQA_DTYPE_BF16 ? 2 : 4;
-  gqa::PrefillArgs a;
+  gqa::PrefillArgs& a = *out;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -487,6 +482,21 @@ int fwd_entry(const void* q, const void* k, const void* v, void* o, int B, int H
   a.c = softmax_coef(scale);
   a.thr = gqa::kRescaleSlack / a.c;
   a.negate_q = scale < 0.f ? 1 : 0;
+  return GQA_OK;
+}
+
+int fwd_entry(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+              int Nq, int Nk, int d, const int64_t* qs, const int64_t* kvs, int causal,
+              int q_offset, float scale, int dtype, void* stream) {
+  gqa::PrefillArgs a;
+  int st = fwd_setup(q, k, v, o, B, Hq, Hkv, Nq, Nk, d, qs, kvs, causal, q_offset, scale, dtype,
+                     &a);
+  if (st != GQA_OK) return st;
+  int dev = 0;
+  DeviceInfo info;
+  st = current_device(&dev, &info);
+  if (st != GQA_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   // K/V rows D elements apart: the compile-time stride
   if (kvs[2] == d) {
     if (dtype == GQA_DTYPE_BF16)
@@ -501,10 +511,12 @@ int fwd_entry(const void* q, const void* k, const void* v, void* o, int B, int H
 // Shared body of the two decode entry points.  knew == NULL: plain decode
 // over the cached lengths in lens; otherwise append (lens are positions, the
 // caches are written at them).
-int decode_entry(const void* q, const void* kcache, const void* vcache, const int32_t* lens,
+// Validation and launch arguments of a decode call, all but the split size
+// (decode_splits).  Pure host code: no HIP call.
+int decode_setup(const void* q, const void* kcache, const void* vcache, const int32_t* lens,
                  const void* knew, const void* vnew, void* kc_out, void* vc_out, void* o, int B,
                  int Hq, int Hkv, int Smax, int d, float scale, int dtype, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 size_t workspace_bytes, gqa::DecodeArgs* out) {
   const bool append = knew != nullptr;
   if (B < 1 || Hq < 1 || Hkv < 1 || Smax < 1 || d < 1)
     return fail(GQA_ERR_BAD_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Smax=%d d=%d)", B, Hq,
@@ -524,14 +536,13 @@ int decode_entry(const void* q, const void* kcache, const void* vcache, const in
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(GQA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
-
-  int dev = 0;
-  DeviceInfo info;
-  int st = current_device(&dev, &info);
-  if (st != GQA_OK) return st;
-
   const int g = Hq / Hkv;
-  gqa::DecodeArgs a;
+  const int ncb = (g + 31) / 32;
+  if ((long long)Hkv * ncb > 65535 || B > 65535)
+    return fail(GQA_ERR_BAD_SHAPE, "grid too large (B=%d, Hkv*blocks=%lld)", B,
+                (long long)Hkv * ncb);
+
+  gqa::DecodeArgs& a = *out;
   a.q = q;
   a.kc = kcache;
   a.vc = vcache;
@@ -547,14 +558,32 @@ int decode_entry(const void* q, const void* kcache, const void* vcache, const in
   a.Hkv = Hkv;
   a.Smax = Smax;
   a.g = g;
-  a.NCB = (g + 31) / 32;
-  a.S_TOK = decode_split_tokens(B, Hkv, a.NCB, Smax, info.cus);
-  a.NS = (Smax + a.S_TOK - 1) / a.S_TOK;
+  a.NCB = ncb;
   a.c = softmax_coef(scale);
   a.thr = gqa::kRescaleSlack / a.c;
   a.negate_q = scale < 0.f ? 1 : 0;
-  if ((long long)a.Hkv * a.NCB > 65535 || B > 65535)
-    return fail(GQA_ERR_BAD_SHAPE, "grid too large (B=%d, Hkv*blocks=%d)", B, a.Hkv * a.NCB);
+  return GQA_OK;
+}
+
+void decode_splits(gqa::DecodeArgs& a, int cus) {
+  a.S_TOK = decode_split_tokens(a.B, a.Hkv, a.NCB, a.Smax, cus);
+  a.NS = (a.Smax + a.S_TOK - 1) / a.S_TOK;
+}
+
+int decode_entry(const void* q, const void* kcache, const void* vcache, const int32_t* lens,
+                 const void* knew, const void* vnew, void* kc_out, void* vc_out, void* o, int B,
+                 int Hq, int Hkv, int Smax, int d, float scale, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  const bool append = knew != nullptr;
+  gqa::DecodeArgs a;
+  int st = decode_setup(q, kcache, vcache, lens, knew, vnew, kc_out, vc_out, o, B, Hq, Hkv, Smax,
+                        d, scale, dtype, workspace, workspace_bytes, &a);
+  if (st != GQA_OK) return st;
+  int dev = 0;
+  DeviceInfo info;
+  st = current_device(&dev, &info);
+  if (st != GQA_OK) return st;
+  decode_splits(a, info.cus);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (append) {
@@ -563,6 +592,99 @@ int decode_entry(const void* q, const void* kcache, const void* vcache, const in
   }
   if (dtype == GQA_DTYPE_BF16) return dispatch_decode<uint16_t, DecCfgBf16, false>(a, d, hs);
   return dispatch_decode<float, DecCfgF32, false>(a, d, hs);
+}
+
+// ------------------------------------------------------------------ mixed batch
+
+// Persistent launch over the chunk's units and the decode splits, one
+// workgroup per resident slot (fewer if there is less work), then the
+// decode rows' combine pass.
+template <typename T, class C, class CD>
+int launch_mixed(gqa::MixedArgs& m, int dev_id, const DeviceInfo& dev, hipStream_t stream) {
+  const void* kern = reinterpret_cast<const void*>(&gqa::mixed_kernel<T, C, CD>);
+  const int per_cu = occupancy(kern, C::NT);
+  const long long slots = (long long)dev.cus * per_cu;
+  constexpr int DW = gqa::mixed_decode_waves<C, CD>();
+  const long long work = (long long)m.p.T + ((long long)m.nd + DW - 1) / DW;
+  const long long grid = std::max<long long>(1, std::min<long long>(work, slots));
+  StreamState ss;
+  int st = stream_state(dev_id, stream, 0, &ss);
+  if (st != GQA_OK) return st;
+  m.p.ctr = ss.ctr;
+  m.p.zero = 0;
+  (void)hipGetLastError();  // a stale error belongs to an earlier call
+  hipLaunchKernelGGL((gqa::mixed_kernel<T, C, CD>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
+                     m);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "mixed kernel launch");
+  if (m.nd > 0) {
+    hipLaunchKernelGGL((gqa::decode_combine_kernel<T, C::D, false>),
+                       dim3((unsigned)m.d.Hq, (unsigned)m.d.B), dim3(256), 0, stream, m.d);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "decode combine kernel launch");
+  }
+  return GQA_OK;
+}
+
+template <typename T, template <int> class Cfg, template <int> class DCfg>
+int dispatch_mixed(gqa::MixedArgs& m, int d, int dev_id, const DeviceInfo& dev,
+                   hipStream_t s) {
+  switch (d) {
+    case 32: return launch_mixed<T, Cfg<32>, DCfg<32>>(m, dev_id, dev, s);
+    case 64: return launch_mixed<T, Cfg<64>, DCfg<64>>(m, dev_id, dev, s);
+    default: return launch_mixed<T, Cfg<128>, DCfg<128>>(m, dev_id, dev, s);
+  }
+}
+
+int mixed_entry(const void* q, const void* k, const void* v, void* o, int B, int Nq, int Nk,
+                int q_offset, const void* qd, const void* kcache, const void* vcache,
+                const int32_t* seqlens, void* od, int Bd, int Smax, int Hq, int Hkv, int d,
+                float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  // ---- validation: host only, before any HIP call
+  if (B < 0 || Bd < 0)
+    return fail(GQA_ERR_BAD_SHAPE, "part sizes must be >= 0 (B=%d Bd=%d)", B, Bd);
+  if (B > 0 && (!q || !k || !v || !o))
+    return fail(GQA_ERR_NULL_POINTER, "q, k, v and o must be non-NULL when B > 0");
+  if (Bd > 0 && (!qd || !kcache || !vcache || !seqlens || !od))
+    return fail(GQA_ERR_NULL_POINTER,
+                "qd, kcache, vcache, seqlens and od must be non-NULL when Bd > 0");
+  gqa::MixedArgs m;
+  std::memset(&m, 0, sizeof(m));
+  if (B > 0) {
+    const int64_t qs[3] = {(int64_t)Hq * Nq * d, (int64_t)Nq * d, d};
+    const int64_t kvs[3] = {(int64_t)Hkv * Nk * d, (int64_t)Nk * d, d};
+    if ((long long)Hq * Nq * d > (1LL << 62) / B || (long long)Hkv * Nk * d > (1LL << 62) / B)
+      return fail(GQA_ERR_BAD_SHAPE, "chunk tensors too large");
+    int st = fwd_setup(q, k, v, o, B, Hq, Hkv, Nq, Nk, d, qs, kvs, 1, q_offset, scale, dtype,
+                       &m.p);
+    if (st != GQA_OK) return st;
+  } else {
+    m.p.Hkv = 1;  // no units: every prefill queue is empty
+    m.p.HB = 1;
+    m.p.NQB = 1;
+  }
+  if (Bd > 0) {
+    int st = decode_setup(qd, kcache, vcache, seqlens, nullptr, nullptr, nullptr, nullptr, od, Bd,
+                          Hq, Hkv, Smax, d, scale, dtype, workspace, workspace_bytes, &m.d);
+    if (st != GQA_OK) return st;
+  }
+  if (B == 0 && Bd == 0) return GQA_OK;  // nothing to compute
+
+  // ---- device
+  int dev = 0;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != GQA_OK) return st;
+  if (Bd > 0) {
+    decode_splits(m.d, info.cus);
+    const long long nd = (long long)m.d.NS * m.d.Hkv * m.d.NCB * m.d.B;
+    if (nd > kIntMax / 2) return fail(GQA_ERR_BAD_SHAPE, "too many decode splits (%lld)", nd);
+    m.nd = (int)nd;
+  }
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == GQA_DTYPE_BF16)
+    return dispatch_mixed<uint16_t, CfgBf16, DecCfgBf16>(m, d, dev, info, hs);
+  return dispatch_mixed<float, CfgF32, DecCfgF32>(m, d, dev, info, hs);
 }
 
 // ------------------------------------------------------------------ backward
@@ -825,6 +947,16 @@ int gqa_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
     return fail(GQA_ERR_NULL_POINTER, "q, k, v, o, dout, dq, dk and dv must be non-NULL");
   return bwd_entry(q, k, v, o, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, causal, q_offset, scale,
                    dtype, workspace, workspace_bytes, stream);
+}
+
+int gqa_attn_mixed(const void* q, const void* k, const void* v, void* o, int B, int Nq, int Nk,
+                   int q_offset, const void* qd, const void* kcache, const void* vcache,
+                   const int32_t* seqlens, void* od, int Bd, int Smax, int Hq, int Hkv, int d,
+                   float scale, int dtype, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  g_last_error.clear();
+  return mixed_entry(q, k, v, o, B, Nq, Nk, q_offset, qd, kcache, vcache, seqlens, od, Bd, Smax,
+                     Hq, Hkv, d, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -388,6 +388,89 @@ __device__ __forceinline__ void write_record(float* rec, float mrun, float lrun,
   reinterpret_cast<float2*>(rec + C::DB * 16 * 64)[lane] = make_float2(mrun, lrun);
 }
 
+// Wave 0 of a persistent workgroup: the next item of the home queue; once
+// that is empty, every queue is looked at at once (lane l reads queue
+// home + l with an atomic add of zero) and an item is taken from the first
+// that still has one.  Every failed take means the queue is empty for good,
+// so this ends.  Returns t = -1 when every queue is empty; q is the queue
+// of t.
+__device__ __forceinline__ void take_unit(const PrefillArgs& a, int home, int nkv, int per_group,
+                                          bool& home_empty, int lane, int& t_out, int& q_out) {
+  int t = -1, q = home;
+  if (!home_empty) {
+    int cand = 0;
+    if (lane == 0) cand = atomicAdd(a.ctr + home * kCounterStride, 1);
+    cand = __shfl(cand, 0);
+    if (cand < queue_units(home, nkv, per_group)) t = cand;
+    else home_empty = true;
+  }
+  while (t < 0 && home_empty) {
+    const int ql = (home + lane) % kNumQueues;
+    int left = 0;
+    if (lane < kNumQueues)
+      left = atomicAdd(a.ctr + ql * kCounterStride, a.zero) < queue_units(ql, nkv, per_group);
+    const unsigned long long open = __ballot(left);
+    if (open == 0) break;
+    q = (home + __ffsll((long long)open) - 1) % kNumQueues;
+    int cand = 0;
+    if (lane == 0) cand = atomicAdd(a.ctr + q * kCounterStride, 1);
+    cand = __shfl(cand, 0);
+    if (cand < queue_units(q, nkv, per_group)) t = cand;
+  }
+  t_out = t;
+  q_out = q;
+}
+
+// Runs item t of queue q of the persistent schedule: maps it to its unit
+// (b, hkv, hb, qb), walks the unit's key tiles and stores its rows.  All
+// threads of the workgroup call it together.
+template <typename T, class C, bool CAUSAL>
+__device__ __forceinline__ void persistent_unit(const PrefillArgs& a, char* smem, int t, int q,
+                                                int w, int j) {
+  const int nkv = a.B * a.Hkv;
+  const int per_group = a.HB * a.NQB;
+  const int groups = queue_units(q, nkv, per_group) / per_group;
+  int qb, gi, hb;
+  if (CAUSAL) {
+    const int per_qb = groups * a.HB;
+    qb = a.NQB - 1 - t / per_qb;
+    const int rest = t % per_qb;
+    hb = rest % a.HB;
+    gi = rest / a.HB;
+  } else {
+    gi = t / per_group;
+    const int rest = t % per_group;
+    hb = rest / a.NQB;
+    qb = rest % a.NQB;
+  }
+  const int kvg = q + kNumQueues * gi;
+  const int hkv = kvg % a.Hkv;
+  const int b = kvg / a.Hkv;
+
+  const int ntiles = unit_tiles<C, CAUSAL>(a, qb);
+  const int rot = (int)((7u * (unsigned)t + 3u * (unsigned)q) % (unsigned)ntiles);
+  const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
+  float mrun, lrun;
+  f32x16 acc[C::DB];
+  run_segment<T, C, CAUSAL>(a, smem, b, hkv, qb, 0, ntiles, rot, col, mrun, lrun, acc);
+  // the ring is free (run_segment ends on a barrier); the next fetch
+  // starts with a barrier before any wave writes it again
+  finish_rows<T, C>(a, smem + w * stage_out_bytes<C>(), lrun, acc, b, hkv, hb, qb, w);
+}
+
+// The last workgroup to leave a persistent launch (all others have made
+// their final, failing fetches) sets counters 0 .. last back to zero for
+// the next launch; counter kNumQueues counts the workgroups that left.
+__device__ __forceinline__ void leave_persistent(const PrefillArgs& a, int last) {
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const int done = atomicAdd(a.ctr + kNumQueues * kCounterStride, 1);
+    if (done == (int)gridDim.x - 1) {
+      for (int i = 0; i <= last; ++i) atomicExch(a.ctr + i * kCounterStride, 0);
+    }
+  }
+}
+
 template <typename T, class C, bool CAUSAL>
 __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_kernel(PrefillArgs a) {
@@ -409,31 +492,8 @@ prefill_kernel(PrefillArgs a) {
   for (;;) {
     __syncthreads();  // every wave has read the previous item's shared words
     if (w == 0) {
-      // Take the next item of the home queue; once that is empty, look at
-      // every queue at once (lane l reads queue home + l with an atomic add
-      // of zero) and take an item from the first that still has one.  Every
-      // failed take means the queue is empty for good, so this ends.
-      int t = -1, q = home;
-      if (!home_empty) {
-        int cand = 0;
-        if (lane == 0) cand = atomicAdd(a.ctr + home * kCounterStride, 1);
-        cand = __shfl(cand, 0);
-        if (cand < queue_units(home, nkv, per_group)) t = cand;
-        else home_empty = true;
-      }
-      while (t < 0 && home_empty) {
-        const int ql = (home + lane) % kNumQueues;
-        int left = 0;
-        if (lane < kNumQueues)
-          left = atomicAdd(a.ctr + ql * kCounterStride, a.zero) < queue_units(ql, nkv, per_group);
-        const unsigned long long open = __ballot(left);
-        if (open == 0) break;
-        q = (home + __ffsll((long long)open) - 1) % kNumQueues;
-        int cand = 0;
-        if (lane == 0) cand = atomicAdd(a.ctr + q * kCounterStride, 1);
-        cand = __shfl(cand, 0);
-        if (cand < queue_units(q, nkv, per_group)) t = cand;
-      }
+      int t, q;
+      take_unit(a, home, nkv, per_group, home_empty, lane, t, q);
       if (lane == 0) {
         s_unit = t;
         s_queue = q;
@@ -444,46 +504,9 @@ prefill_kernel(PrefillArgs a) {
     const int t = __builtin_amdgcn_readfirstlane(s_unit);
     const int q = __builtin_amdgcn_readfirstlane(s_queue);
     if (t < 0) break;
-
-    // ---- (queue, index) -> (b, hkv, hb, qb)
-    const int groups = queue_units(q, nkv, per_group) / per_group;
-    int qb, gi, hb;
-    if (CAUSAL) {
-      const int per_qb = groups * a.HB;
-      qb = a.NQB - 1 - t / per_qb;
-      const int rest = t % per_qb;
-      hb = rest % a.HB;
-      gi = rest / a.HB;
-    } else {
-      gi = t / per_group;
-      const int rest = t % per_group;
-      hb = rest / a.NQB;
-      qb = rest % a.NQB;
-    }
-    const int kvg = q + kNumQueues * gi;
-    const int hkv = kvg % a.Hkv;
-    const int b = kvg / a.Hkv;
-
-    const int ntiles = unit_tiles<C, CAUSAL>(a, qb);
-    const int rot = (int)((7u * (unsigned)t + 3u * (unsigned)q) % (unsigned)ntiles);
-    const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
-    float mrun, lrun;
-    f32x16 acc[C::DB];
-    run_segment<T, C, CAUSAL>(a, smem, b, hkv, qb, 0, ntiles, rot, col, mrun, lrun, acc);
-    // the ring is free (run_segment ends on a barrier); the next fetch
-    // starts with a barrier before any wave writes it again
-    finish_rows<T, C>(a, smem + w * stage_out_bytes<C>(), lrun, acc, b, hkv, hb, qb, w);
+    persistent_unit<T, C, CAUSAL>(a, smem, t, q, w, j);
   }
-
-  // Leave the counters at zero for the next launch: the last workgroup out
-  // (all others have made their final, failing fetches) resets every word.
-  if (tid == 0) {
-    __threadfence();
-    const int done = atomicAdd(a.ctr + kNumQueues * kCounterStride, 1);
-    if (done == (int)gridDim.x - 1) {
-      for (int i = 0; i <= kNumQueues; ++i) atomicExch(a.ctr + i * kCounterStride, 0);
-    }
-  }
+  leave_persistent(a, kNumQueues);
 }
 
 // Workgroup g = c * nsl + s runs chunk c of slice s, so the workgroups of a

@@ -12,6 +12,8 @@ Recipe (one torch CPU generator per draw, ``manual_seed(seed)``):
   decode:  q, K cache, V cache in that order as above, then the per-sequence
            cache lengths ``torch.randint(lo, hi + 1, (B,))`` (inclusive
            uniform integers) from the same generator.
+  mixed:   the chunk as a forward draw with ``seed``, the decode rows as a
+           decode draw with ``seed + 1``.
 
 The shapes are the workloads the pages turn on:
   * LLaMA-3-8B attention shape (seq 2K, Hq 32, Hkv 8, d 128) from the
@@ -24,7 +26,8 @@ The shapes are the workloads the pages turn on:
     optimization log, experiments 060/085/294, which time steady decode at
     T2048 and B1..B8).
   * a 512-token chunk of a 4096-token prompt (kaispace.site note on Chunked
-    Prefill, which splits a 4096-token prompt into chunks).
+    Prefill, which splits a 4096-token prompt into chunks), alone and, as
+    that note's mixed batch, beside decode rows of the same layer.
 """
 from __future__ import annotations
 
@@ -110,6 +113,12 @@ WORKLOADS = {
         "chunked_prefill_4k",
         "Chunked prefill, bf16, causal: B=1 Hq=32 Hkv=8 d=128, Nq=512 at q_offset=3584, Nk=4096",
         fwd=(FwdShape(1, 32, 8, 512, 4096, 128, True, 3584),)),
+    "llama3_8b_mixed": Workload(
+        "llama3_8b_mixed",
+        "Mixed batch in one launch, bf16, Hq=32 Hkv=8 d=128: the 512-query chunk at q_offset=3584 "
+        "of a 4096-token prompt plus 8 decode rows, lengths U[512,4096], Smax=4096",
+        fwd=(FwdShape(1, 32, 8, 512, 4096, 128, True, 3584),),
+        decode=DecodeShape(8, 32, 8, 4096, 128, 512, 4096)),
 }
 
 
@@ -130,6 +139,12 @@ def decode_inputs(s: DecodeShape, seed: int = 0):
     vc = torch.randn((s.B, s.Hkv, s.Smax, s.d), generator=g, dtype=torch.float32)
     lens = torch.randint(s.len_lo, s.len_hi + 1, (s.B,), generator=g, dtype=torch.int64)
     return q.to(s.dtype), kc.to(s.dtype), vc.to(s.dtype), lens.to(torch.int32)
+
+
+def mixed_inputs(chunk: FwdShape, rows: DecodeShape, seed: int = 0):
+    """CPU tensors (q, k, v, qd, kcache, vcache, seqlens) of a mixed batch:
+    fwd_inputs(chunk, seed) then decode_inputs(rows, seed + 1)."""
+    return (*fwd_inputs(chunk, seed), *decode_inputs(rows, seed + 1))
 
 
 def append_inputs(s: DecodeShape, seed: int = 0):

@@ -18,7 +18,9 @@ GQA Flash Attention"), evaluated as max / exp-sum / weighted sum per row.  The d
 append first writes each active row's new K/V rows at its position (the
 single-launch K/V store and per-row position table of the microLLM-rocm
 optimization log, experiments 025, 083/084 and 098) and then attends slots
-[0, position].  The backward gives dQ, dK, dV of a loss with dL/dO given,
+[0, position].  A mixed batch (a chunked-prefill chunk beside decode rows,
+kaispace.site note "Chunked Prefill") is the two definitions side by side.
+The backward gives dQ, dK, dV of a loss with dL/dO given,
 the K/V gradients reduced over each K/V head's query heads (microLLM-rocm
 optimization log, experiments 044 and 051-054).
 
@@ -201,6 +203,28 @@ def attn_decode_append(q, k_new, v_new, kcache, vcache, positions, *,
                                          _ptr(o), B, Hq, Hkv, Smax, d, float(scale)),
            "attn_decode_append")
     return o, kc, vc
+
+
+def attn_mixed(q, k, v, q_offset: int, qd, kcache, vcache, seqlens, *,
+               scale: float | None = None, lib: ctypes.CDLL | None = None):
+    """(O_chunk, O_decode) as float64 for a mixed batch of one layer.
+
+    The batch holds a chunked-prefill chunk and single-token decode rows
+    (kaispace.site note "Chunked Prefill"); each part is defined on its own:
+    the chunk q[B,Hq,Nq,d] over k, v[B,Hkv,Nk,d] is the causal forward with
+    query row i at position q_offset + i, and each decode row is the decode
+    definition over its cache.  q is None: no chunk (None returned in its
+    place); qd is None: no decode rows.  The default scale is 1/sqrt(d) of
+    whichever part is present."""
+    ref = q if q is not None else qd
+    if ref is None:
+        return None, None
+    if scale is None:
+        scale = 1.0 / np.sqrt(ref.shape[-1])
+    o = None if q is None else attn_fwd(q, k, v, causal=True, q_offset=q_offset, scale=scale,
+                                        lib=lib)
+    od = None if qd is None else attn_decode(qd, kcache, vcache, seqlens, scale=scale, lib=lib)
+    return o, od
 
 
 def attn_bwd(q, k, v, dout, *, causal: bool = False, q_offset: int = 0,

@@ -309,6 +309,40 @@ def pin_decode_semantics(lib):
     assert np.all(z[0] == 0) and np.all(z[1] == 0)
 
 
+def pin_mixed_decode_rows_are_chunk_rows(lib):
+    """A chunked-prefill chunk and decode rows in one batch (kaispace.site note
+    "Chunked Prefill"): the chunk's query at position p sees keys 0..p, and a
+    decode row whose cache holds those keys (length p + 1) is that same query.
+    So decode rows built from the chunk's own queries and keys reproduce the
+    chunk's rows -- a causal diagonal, offset or length off by one, or a
+    non-causal chunk, breaks this.  Each part absent leaves the other as its
+    own definition."""
+    Hq, Hkv, Nk, Nq, d = 6, 2, 37, 11, 16
+    off = Nk - Nq
+    q = _rand((1, Hq, Nq, d), 171)
+    k = _rand((1, Hkv, Nk, d), 172)
+    v = _rand((1, Hkv, Nk, d), 173)
+    Smax = Nk + 5
+    qd = np.ascontiguousarray(q[0].transpose(1, 0, 2))          # [Nq, Hq, d]
+    kc = np.full((Nq, Hkv, Smax, d), np.nan)
+    vc = np.full((Nq, Hkv, Smax, d), np.nan)
+    kc[:, :, :Nk] = k[0]
+    vc[:, :, :Nk] = v[0]
+    lens = np.arange(off + 1, Nk + 1, dtype=np.int32)           # row i: position off + i
+    o, od = oracle.attn_mixed(q, k, v, off, qd, kc, vc, lens, lib=lib)
+    assert o.shape == q.shape and od.shape == qd.shape
+    assert _maxerr(od, o[0].transpose(1, 0, 2)) <= 1e-13
+    # the last row sees every key: the plain softmax over all Nk keys, by hand
+    s = (k[0][np.arange(Hq) // (Hq // Hkv)] @ q[0, :, -1, :, None])[..., 0] / math.sqrt(d)
+    w = np.exp(s - s.max(axis=1, keepdims=True))
+    last = (w[:, :, None] * v[0][np.arange(Hq) // (Hq // Hkv)]).sum(1) / w.sum(1, keepdims=True)
+    assert _maxerr(o[0, :, -1], last) <= TOL
+    o2, none_d = oracle.attn_mixed(q, k, v, off, None, None, None, None, lib=lib)
+    assert none_d is None and np.array_equal(o2, o)
+    none_c, od2 = oracle.attn_mixed(None, None, None, 0, qd, kc, vc, lens, lib=lib)
+    assert none_c is None and np.array_equal(od2, od)
+
+
 def _append_case(seed, B, Hkv, g, Smax, d):
     return (_rand((B, Hkv * g, d), seed), _rand((B, Hkv, d), seed + 1), _rand((B, Hkv, d), seed + 2),
             _rand((B, Hkv, Smax, d), seed + 3), _rand((B, Hkv, Smax, d), seed + 4))
@@ -512,6 +546,7 @@ PINS = [
     pin_hardmax_limit,
     pin_rows_match_full,
     pin_decode_semantics,
+    pin_mixed_decode_rows_are_chunk_rows,
     pin_append_library,
     pin_append_first_slot,
     pin_append_equal_keys_mean,

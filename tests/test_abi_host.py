@@ -238,3 +238,49 @@ def test_bwd_workspace_bytes():
 def test_valid_bwd_call_without_gpu_reports_no_device():
     assert bwd() == NODEV
     assert bwd(causal=1, q_offset=5, dtype=F32, d=128) == NODEV
+
+
+# ---------------------------------------------------------------- mixed batch
+PM = [ctypes.c_void_p(0x10000 * (n + 1)) for n in range(11)]
+NUL = ctypes.c_void_p(0)
+
+
+def mixed(q=PM[0], k=PM[1], v=PM[2], o=PM[3], B=1, Nq=64, Nk=128, q_offset=64, qd=PM[4],
+          kc=PM[5], vc=PM[6], lens=PM[7], od=PM[8], Bd=2, Smax=256, Hq=4, Hkv=2, d=64,
+          scale=0.125, dtype=BF16, ws=PM[9], ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = binding.lib.gqa_attn_decode_workspace_bytes(max(Bd, 1), Hq, Hkv, max(Smax, 1),
+                                                               d)
+    return binding.lib.gqa_attn_mixed(q, k, v, o, B, Nq, Nk, q_offset, qd, kc, vc, lens, od, Bd,
+                                      Smax, Hq, Hkv, d, scale, dtype, ws, ws_bytes, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), SHAPE), (dict(Bd=-1), SHAPE),
+    (dict(q=NUL), NULLP), (dict(o=NUL), NULLP), (dict(qd=NUL), NULLP),
+    (dict(lens=NUL), NULLP), (dict(od=NUL), NULLP),
+    (dict(Nq=0), SHAPE), (dict(q_offset=-1), SHAPE), (dict(Smax=0), SHAPE),
+    (dict(Hq=6, Hkv=4), GROUP), (dict(d=96), UNSUP), (dict(dtype=5), UNSUP),
+    (dict(scale=float("nan")), UNSUP), (dict(ws=NUL), WS), (dict(ws_bytes=16), WS),
+    (dict(kc=ctypes.c_void_p(0x10008)), UNSUP), (dict(q=ctypes.c_void_p(0x10004)), UNSUP),
+    (dict(Bd=70000, ws_bytes=1 << 40), SHAPE),
+], ids=lambda x: str(x))
+def test_mixed_rejects_invalid_arguments(kw, code):
+    assert mixed(**kw) == code
+    assert binding.lib.gqa_last_error_string() != b""
+
+
+def test_mixed_absent_parts_need_no_pointers():
+    # both parts empty: nothing to do, and no pointer is looked at
+    assert mixed(q=NUL, k=NUL, v=NUL, o=NUL, B=0, qd=NUL, kc=NUL, vc=NUL, lens=NUL, od=NUL, Bd=0,
+                 ws=NUL, ws_bytes=0) == OK
+    # an absent part's sizes and pointers are not checked
+    assert mixed(q=NUL, B=0, Nq=0, Nk=0, q_offset=-5, qd=NUL, Bd=0, Smax=0, ws=NUL,
+                 ws_bytes=0) == OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="valid arguments would launch on a GPU")
+def test_valid_mixed_call_without_gpu_reports_no_device():
+    assert mixed() == NODEV
+    assert mixed(q=NUL, k=NUL, v=NUL, o=NUL, B=0) == NODEV           # decode rows only
+    assert mixed(qd=NUL, kc=NUL, vc=NUL, lens=NUL, od=NUL, Bd=0, ws=NUL, ws_bytes=0) == NODEV

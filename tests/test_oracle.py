@@ -180,5 +180,36 @@ def test_planted_mistake_is_caught(tmp_path, name, old, new, occ):
     assert r.returncode != 0, f"mutant '{name}' passed every pin:\n{r.stdout}"
 
 
+# Planted mistakes in the mixed batch's composition (Python, not C): each
+# wrong attn_mixed must fail the mixed-batch pin.
+def _mixed_noncausal(q, k, v, off, qd, kc, vc, lens, *, scale=None, lib=None):
+    return (oracle.attn_fwd(q, k, v, causal=False, lib=lib),
+            oracle.attn_decode(qd, kc, vc, lens, lib=lib))
+
+
+def _mixed_offset_off_by_one(q, k, v, off, qd, kc, vc, lens, *, scale=None, lib=None):
+    return (oracle.attn_fwd(q, k, v, causal=True, q_offset=off - 1, lib=lib),
+            oracle.attn_decode(qd, kc, vc, lens, lib=lib))
+
+
+def _mixed_lengths_short(q, k, v, off, qd, kc, vc, lens, *, scale=None, lib=None):
+    return (oracle.attn_fwd(q, k, v, causal=True, q_offset=off, lib=lib),
+            oracle.attn_decode(qd, kc, vc, np.asarray(lens) - 1, lib=lib))
+
+
+def _mixed_decode_unscaled(q, k, v, off, qd, kc, vc, lens, *, scale=None, lib=None):
+    return (oracle.attn_fwd(q, k, v, causal=True, q_offset=off, lib=lib),
+            oracle.attn_decode(qd, kc, vc, lens, scale=1.0, lib=lib))
+
+
+@pytest.mark.parametrize("wrong", [_mixed_noncausal, _mixed_offset_off_by_one,
+                                   _mixed_lengths_short, _mixed_decode_unscaled],
+                         ids=lambda f: f.__name__[1:])
+def test_planted_mixed_mistake_is_caught(lib, monkeypatch, wrong):
+    monkeypatch.setattr(oracle, "attn_mixed", wrong)
+    with pytest.raises(Exception):
+        oracle_pins.pin_mixed_decode_rows_are_chunk_rows(lib)
+
+
 def test_pin_module_importable():
     assert len(oracle_pins.PINS) >= 15
