@@ -202,10 +202,13 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new,
  * schedule) and then the decode splits from the same counters -- the
  * "Kernel 10" of the BootstrapAI evolution log, persistent scheduling with
  * the GQA head mapping -- so decode work fills the CUs the chunk leaves
- * idle.  A second launch merges the decode rows' split states.  The decode
- * rows' outputs equal gqa_attn_decode's bit for bit; the chunk's are those
- * of gqa_attn_fwd's persistent schedule (the same to within rounding order
- * when gqa_attn_fwd chooses another schedule).
+ * idle.  A second launch merges the decode rows' split states.  A chunk of
+ * few, long units (at most two 64-column units per CU, >= 8 key tiles each)
+ * runs as the quad schedule's units, others as the persistent schedule's;
+ * the chunk's outputs equal gqa_attn_fwd's bit for bit when it picks the
+ * same schedule, and to within rounding order otherwise.  The decode rows
+ * are cut into about twice as many splits as gqa_attn_decode uses (eight
+ * decode waves per CU), so they equal its outputs to within rounding order.
  *
  * workspace: at least gqa_attn_decode_workspace_bytes(Bd, Hq, Hkv, Smax, d)
  * bytes when Bd > 0, as for gqa_attn_decode.  Calls that may run

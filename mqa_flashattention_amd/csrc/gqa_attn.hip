@@ -384,11 +384,12 @@ using DecCfgF32 = gqa::TileCfg<float, D, 32, 1>;
 // CU) when every row is full, in whole 32-token tiles.  The split kernel's
 // registers allow one resident wave per SIMD; more, shorter splits only run
 // in a second round (measured slower from batch 32 up, as were two waves
-// per CU).
-int decode_split_tokens(int B, int Hkv, int ncb, int smax, int cus) {
+// per CU).  The mixed launch runs its splits eight waves per CU (waves_per_cu
+// = 8), each with one register stage instead of two.
+int decode_split_tokens(int B, int Hkv, int ncb, int smax, int cus, int waves_per_cu = 4) {
   const long long tiles_per_row = (smax + 31) / 32;
   const long long heads = (long long)B * Hkv * ncb;
-  const long long target = 4LL * cus;
+  const long long target = (long long)waves_per_cu * cus;
   long long tiles_per_split = (heads * tiles_per_row + target - 1) / target;
   if (tiles_per_split < 1) tiles_per_split = 1;
   if (tiles_per_split > tiles_per_row) tiles_per_split = tiles_per_row;
@@ -565,8 +566,8 @@ int decode_setup(const void* q, const void* kcache, const void* vcache, const in
   return GQA_OK;
 }
 
-void decode_splits(gqa::DecodeArgs& a, int cus) {
-  a.S_TOK = decode_split_tokens(a.B, a.Hkv, a.NCB, a.Smax, cus);
+void decode_splits(gqa::DecodeArgs& a, int cus, int waves_per_cu = 4) {
+  a.S_TOK = decode_split_tokens(a.B, a.Hkv, a.NCB, a.Smax, cus, waves_per_cu);
   a.NS = (a.Smax + a.S_TOK - 1) / a.S_TOK;
 }
 
@@ -596,25 +597,45 @@ int decode_entry(const void* q, const void* kcache, const void* vcache, const in
 
 // ------------------------------------------------------------------ mixed batch
 
-// Persistent launch over the chunk's units and the decode splits, one
-// workgroup per resident slot (fewer if there is less work), then the
-// decode rows' combine pass.
+// One launch over the chunk's units and the decode splits, one workgroup
+// per resident slot (fewer if there is less work), then the decode rows'
+// combine pass.  A chunk of few, long units (at most two 64-column units
+// per CU, each of >= 8 key tiles) runs as quad units, whose four groups
+// split each unit's keys; any other chunk as the persistent schedule's
+// 128-column units.
 template <typename T, class C, class CD>
 int launch_mixed(gqa::MixedArgs& m, int dev_id, const DeviceInfo& dev, hipStream_t stream) {
-  const void* kern = reinterpret_cast<const void*>(&gqa::mixed_kernel<T, C, CD>);
-  const int per_cu = occupancy(kern, C::NT);
-  const long long slots = (long long)dev.cus * per_cu;
-  constexpr int DW = gqa::mixed_decode_waves<C, CD>();
-  const long long work = (long long)m.p.T + ((long long)m.nd + DW - 1) / DW;
-  const long long grid = std::max<long long>(1, std::min<long long>(work, slots));
   StreamState ss;
   int st = stream_state(dev_id, stream, 0, &ss);
   if (st != GQA_OK) return st;
   m.p.ctr = ss.ctr;
   m.p.zero = 0;
   (void)hipGetLastError();  // a stale error belongs to an earlier call
-  hipLaunchKernelGGL((gqa::mixed_kernel<T, C, CD>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
-                     m);
+  bool launched = false;
+  using CQ = gqa::TileCfg<T, C::D, C::BC, 2, C::KVS>;
+  if constexpr (8 * CQ::STAGE_BYTES <= kLdsBytes) {
+    gqa::MixedArgs mq = m;
+    if (m.p.T > 0) decompose(mq.p, 64);  // (no chunk: g = 0, nothing to decompose)
+    if (m.p.T > 0 && mq.p.T <= 2LL * dev.cus && unit_tiles<CQ>(mq.p, true, 0) >= 8) {
+      const void* kern = reinterpret_cast<const void*>(&gqa::mixed_quad_kernel<T, CQ, CD>);
+      const long long slots = (long long)dev.cus * occupancy(kern, 4 * CQ::NT);
+      constexpr int DW = gqa::mixed_quad_decode_waves<CQ, CD>();
+      const long long work = (long long)mq.p.T + ((long long)mq.nd + DW - 1) / DW;
+      const long long grid = std::max<long long>(1, std::min<long long>(work, slots));
+      hipLaunchKernelGGL((gqa::mixed_quad_kernel<T, CQ, CD>), dim3((unsigned)grid),
+                         dim3(4 * CQ::NT), 0, stream, mq);
+      launched = true;
+    }
+  }
+  if (!launched) {
+    const void* kern = reinterpret_cast<const void*>(&gqa::mixed_kernel<T, C, CD>);
+    const long long slots = (long long)dev.cus * occupancy(kern, C::NT);
+    constexpr int DW = gqa::mixed_decode_waves<C, CD>();
+    const long long work = (long long)m.p.T + ((long long)m.nd + DW - 1) / DW;
+    const long long grid = std::max<long long>(1, std::min<long long>(work, slots));
+    hipLaunchKernelGGL((gqa::mixed_kernel<T, C, CD>), dim3((unsigned)grid), dim3(C::NT), 0,
+                       stream, m);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "mixed kernel launch");
   if (m.nd > 0) {
@@ -676,7 +697,7 @@ int mixed_entry(const void* q, const void* k, const void* v, void* o, int B, int
   int st = current_device(&dev, &info);
   if (st != GQA_OK) return st;
   if (Bd > 0) {
-    decode_splits(m.d, info.cus);
+    decode_splits(m.d, info.cus, 8);
     const long long nd = (long long)m.d.NS * m.d.Hkv * m.d.NCB * m.d.B;
     if (nd > kIntMax / 2) return fail(GQA_ERR_BAD_SHAPE, "too many decode splits (%lld)", nd);
     m.nd = (int)nd;

@@ -6,14 +6,21 @@
 // decode tokens of other sequences.  Here both kinds of work come from one
 // persistent launch (the work-queue scheduler of the BootstrapAI evolution
 // log, "Kernel 8 -- persistent kernel", whose queue holds two kinds of
-// item): a workgroup first takes the chunk's prefill units from the XCD
-// queues, heaviest first, exactly as the persistent prefill schedule does;
-// once every prefill queue is empty it takes decode splits from one more
-// counter, DW at a time (one per wave, each wave in an LDS area of its own).
-// So the decode splits fill the CUs that the prefill units leave idle --
-// at the start when the chunk has fewer units than resident workgroups, and
-// in the tail.  The decode rows' partial states are merged by the decode
-// combine pass, launched after this kernel.
+// item): a workgroup first takes the chunk's prefill units, heaviest first,
+// and once they are gone takes decode splits from one more counter, DW at a
+// time (one per wave, each wave in an LDS area of its own).  So the decode
+// splits fill the CUs that the prefill units leave idle -- at the start when
+// the chunk has fewer units than resident workgroups, and in the tail.  The
+// decode rows' partial states are merged by the decode combine pass,
+// launched after this kernel.
+//
+// Two prefill unit shapes, as for a prefill launch:
+//  * mixed_kernel: 4-wave workgroups on 128-column units from the XCD
+//    queues of the persistent schedule, for chunks with many units;
+//  * mixed_quad_kernel: 8-wave workgroups on 64-column units whose keys
+//    four 2-wave groups split (the quad schedule), for chunks with few,
+//    long units -- a long chunk over a long prompt, where one wave walking
+//    all of a unit's keys would be the critical path.
 #pragma once
 
 #include "decode_kernel.hpp"
@@ -45,6 +52,32 @@ constexpr int mixed_lds_bytes() {
   constexpr int pre = 2 * C::STAGE_BYTES;
   constexpr int dec = mixed_decode_waves<C, CD>() * CD::STAGE_BYTES;
   return pre > dec ? pre : dec;
+}
+
+// Decode splits, after the prefill units: take i covers splits
+// DW*i .. DW*i + DW - 1 (wave w < DW runs the w-th in its own LDS area at
+// smem + w * CD::STAGE_BYTES); split x = (s, y, b) with s fastest, as the
+// decode grid orders them.  All threads of the workgroup call it.
+template <typename T, class CD, int DW>
+__device__ __forceinline__ void mixed_decode_phase(const MixedArgs& m, char* smem, int* s_take) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int ny = m.d.Hkv * m.d.NCB;
+  for (;;) {
+    __syncthreads();  // shared word read, LDS free of the previous item
+    if (tid == 0) *s_take = atomicAdd(m.p.ctr + kMixedDecodeCounter * kCounterStride, 1);
+    __syncthreads();
+    const int take = __builtin_amdgcn_readfirstlane(*s_take);
+    if ((long long)take * DW >= m.nd) break;
+    const int x = take * DW + w;
+    if (w < DW && x < m.nd) {
+      const int s_idx = x % m.d.NS;
+      const int rest = x / m.d.NS;
+      decode_split<T, CD, false, true>(m.d, smem + w * CD::STAGE_BYTES, s_idx, rest % ny,
+                                       rest / ny, lane);
+    }
+  }
 }
 
 // Causal prefill units (config C) then decode splits (config CD); grid =
@@ -87,23 +120,62 @@ mixed_kernel(MixedArgs m) {
     persistent_unit<T, C, true>(a, smem, t, q, w, j);
   }
 
-  // ---- decode splits: take i covers splits DW*i .. DW*i + DW - 1, split
-  // x = (s, y, b) with s fastest, as the decode grid orders them
-  const int ny = m.d.Hkv * m.d.NCB;
+  mixed_decode_phase<T, CD, DW>(m, smem, &s_unit);
+  leave_persistent(a, kMixedDecodeCounter);
+}
+
+// Decode waves of a mixed_quad_kernel workgroup (8 waves, the quad
+// schedule's LDS).
+template <class CQ, class CD>
+constexpr int mixed_quad_decode_waves() {
+  constexpr int fit = quad_lds_bytes<CQ>() / CD::STAGE_BYTES;
+  return fit < 1 ? 1 : (fit < 4 * CQ::NW ? fit : 4 * CQ::NW);
+}
+
+// Causal quad units (config CQ, 64 columns, m.p decomposed for them) from
+// the persistent schedule's XCD queues (the units of a K/V group stay on one
+// XCD, whose L2 then holds that group's K/V), heaviest position block first,
+// then decode splits.
+template <typename T, class CQ, class CD>
+__global__ void __launch_bounds__(4 * CQ::NT) __attribute__((amdgpu_waves_per_eu(2)))
+mixed_quad_kernel(MixedArgs m) {
+  constexpr int DW = mixed_quad_decode_waves<CQ, CD>();
+  constexpr int LDS = quad_lds_bytes<CQ>() > DW * CD::STAGE_BYTES ? quad_lds_bytes<CQ>()
+                                                                  : DW * CD::STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[LDS];
+  static_assert(CQ::D == CD::D, "one head dim for both parts");
+  __shared__ int s_unit;
+  __shared__ int s_queue;
+  const PrefillArgs& a = m.p;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int home = blockIdx.x % kNumQueues;
+  const int nkv = a.B * a.Hkv;
+  const int per_group = a.HB * a.NQB;
+  bool home_empty = false;  // wave 0: the home queue has run dry
   for (;;) {
-    __syncthreads();  // shared words read, LDS free of the previous item
-    if (tid == 0) s_unit = atomicAdd(a.ctr + kMixedDecodeCounter * kCounterStride, 1);
-    __syncthreads();
-    const int take = __builtin_amdgcn_readfirstlane(s_unit);
-    if ((long long)take * DW >= m.nd) break;
-    const int x = take * DW + w;
-    if (w < DW && x < m.nd) {
-      const int s_idx = x % m.d.NS;
-      const int rest = x / m.d.NS;
-      decode_split<T, CD, false, true>(m.d, smem + w * CD::STAGE_BYTES, s_idx, rest % ny,
-                                       rest / ny, lane);
+    __syncthreads();  // shared words read, LDS free of the previous unit
+    if (w == 0) {
+      int t, q;
+      take_unit(a, home, nkv, per_group, home_empty, lane, t, q);
+      if (lane == 0) {
+        s_unit = t;
+        s_queue = q;
+      }
     }
+    __syncthreads();
+    const int t = __builtin_amdgcn_readfirstlane(s_unit);
+    const int q = __builtin_amdgcn_readfirstlane(s_queue);
+    if (t < 0) break;
+    // (queue, index) -> unit, as the persistent schedule maps causal units
+    const int per_qb = (queue_units(q, nkv, per_group) / per_group) * a.HB;
+    const int qb = a.NQB - 1 - t / per_qb;
+    const int rest = t % per_qb;
+    const int hb = rest % a.HB;
+    const int kvg = q + kNumQueues * (rest / a.HB);
+    quad_unit<T, CQ, true>(a, smem, (kvg * a.HB + hb) * a.NQB + qb);
   }
+  mixed_decode_phase<T, CD, DW>(m, smem, &s_unit);
   leave_persistent(a, kMixedDecodeCounter);
 }
 

@@ -761,12 +761,19 @@ __global__ void __launch_bounds__(64 * C::DB) prefill_merge_kernel(PrefillArgs a
 // so there is no merge pass.  Unit i / 8-th of the list runs on the XCD
 // that takes block i mod 8 (when T is a multiple of 8), so the units of one
 // K/V head share one L2.
+template <class C>
+constexpr int quad_lds_bytes() {
+  return 4 * 2 * C::STAGE_BYTES;
+}
+
+// Unit t (qb = t % NQB, then head block, then K/V group) of the quad
+// schedule, run by the whole 8-wave workgroup in smem (quad_lds_bytes).
+// Ends with group 0 storing the rows; the caller puts a barrier between
+// this and any later use of smem.
 template <typename T, class C, bool CAUSAL>
-__global__ void __launch_bounds__(4 * C::NT) __attribute__((amdgpu_waves_per_eu(2)))
-prefill_quad_kernel(PrefillArgs a) {
+__device__ __forceinline__ void quad_unit(const PrefillArgs& a, char* smem, int t) {
   static_assert(C::NW == 2, "quad groups are two waves");
   constexpr int NG = 4;
-  __shared__ __attribute__((aligned(16))) char smem[NG * 2 * C::STAGE_BYTES];
   // hand-over block of one wave: DB*4 rows of 64 float4 (the accumulator),
   // then 64 float2 (m, l); consecutive lanes on consecutive 16-byte words
   constexpr int HAND_BYTES = (C::DB * 16 + 2) * 64 * 4;
@@ -781,8 +788,6 @@ prefill_quad_kernel(PrefillArgs a) {
   const int lane = tid & 63;
   const int j = lane & 31;
 
-  const int i = blockIdx.x;
-  const int t = (a.T % 8 == 0) ? (i % 8) * (a.T / 8) + i / 8 : i;
   const int qb = t % a.NQB;
   const int rest = t / a.NQB;
   const int hb = rest % a.HB;
@@ -853,6 +858,15 @@ prefill_quad_kernel(PrefillArgs a) {
     finish_rows<T, C>(a, smem + STAGE_OFF + w * stage_out_bytes<C>(), l, acc, b, hkv, hb, qb,
                       w);
   }
+}
+
+template <typename T, class C, bool CAUSAL>
+__global__ void __launch_bounds__(4 * C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+prefill_quad_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[quad_lds_bytes<C>()];
+  const int i = blockIdx.x;
+  const int t = (a.T % 8 == 0) ? (i % 8) * (a.T / 8) + i / 8 : i;
+  quad_unit<T, C, CAUSAL>(a, smem, t);
 }
 
 }  // namespace gqa

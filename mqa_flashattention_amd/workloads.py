@@ -119,6 +119,12 @@ WORKLOADS = {
         "of a 4096-token prompt plus 8 decode rows, lengths U[512,4096], Smax=4096",
         fwd=(FwdShape(1, 32, 8, 512, 4096, 128, True, 3584),),
         decode=DecodeShape(8, 32, 8, 4096, 128, 512, 4096)),
+    "llama3_8b_mixed_c128": Workload(
+        "llama3_8b_mixed_c128",
+        "The same mixed batch with a 128-query chunk (the prompt's last, q_offset=3968): fewer "
+        "prefill units than CUs",
+        fwd=(FwdShape(1, 32, 8, 128, 4096, 128, True, 3968),),
+        decode=DecodeShape(8, 32, 8, 4096, 128, 512, 4096)),
 }
 
 

@@ -5,10 +5,12 @@ q_offset + i) and decode rows of the same layer; both outputs are compared
 element by element with oracle.attn_mixed on the same inputs.  Bar: the
 forward's, max |O_gpu - O_oracle| <= 1e-4 for fp32 and <= 2e-2 for bf16.
 Cases span every head dim, MHA / GQA / MQA and groups wider than one column
-block, ragged chunk and cache lengths (empty, one slot, full capacity), a
-missing part, the LLaMA-3-8B mixed workload at full size, the decode rows'
-bitwise identity with gqa_attn_decode, determinism, and back-to-back calls
-of different sizes sharing one stream's scheduler counters.
+block, both prefill unit shapes (128-column persistent units; quad units
+for chunks of few long units), ragged chunk and cache lengths (empty, one
+slot, full capacity), a missing part, the LLaMA-3-8B mixed workload at full
+size, the decode rows' agreement with gqa_attn_decode and the quad chunk's
+bitwise identity with gqa_attn_fwd, determinism, and back-to-back calls of different
+sizes sharing one stream's scheduler counters.
 """
 from __future__ import annotations
 
@@ -62,7 +64,10 @@ SMALL = [
     _pair(1, 8, 1, 33, 33, 0, 6, 257, 200, 257, 128, torch.bfloat16),       # MQA, prompt start
     _pair(2, 4, 4, 64, 96, 32, 2, 96, 90, 96, 128, torch.float32),          # MHA
     _pair(1, 40, 1, 20, 90, 70, 3, 300, 1, 300, 32, torch.bfloat16),        # g = 40: 2 blocks
+    # chunks of few long units: quad units (keys split four ways)
     _pair(3, 16, 4, 127, 1000, 873, 9, 1000, 1, 1000, 64, torch.float32),
+    _pair(1, 16, 2, 128, 1024, 896, 4, 1024, 1, 1024, 64, torch.bfloat16),  # group of 8
+    _pair(2, 4, 1, 64, 800, 736, 3, 800, 1, 800, 32, torch.bfloat16),
 ]
 
 
@@ -97,15 +102,34 @@ def test_llama3_8b_mixed_full():
     _run(w.fwd[0], w.decode, seed=0)
 
 
-def test_mixed_decode_rows_equal_decode_bitwise():
-    """The decode rows run the decode kernel's split code on the same splits
-    and are merged by the same combine pass: identical bits."""
+def test_mixed_decode_rows_match_decode():
+    """The decode rows run the decode kernel's split code (on shorter splits)
+    and its combine pass: they agree with gqa_attn_decode to within the bar,
+    and exactly where a row fits one split of either."""
     w = WORKLOADS["llama3_8b_mixed"]
     q, k, v, qd, kc, vc, sl = _dev(mixed_inputs(w.fwd[0], w.decode, 3))
     _, od = attn_mixed(q, k, v, w.fwd[0].q_offset, qd, kc, vc, sl, scale=w.fwd[0].scale)
     ref = attn_decode(qd, kc, vc, sl, scale=w.fwd[0].scale)
     torch.cuda.synchronize()
-    assert torch.equal(od, ref)
+    assert float((od.double() - ref.double()).abs().max()) <= TOL[w.decode.dtype]
+    one = torch.tensor([1, 5, 31, 32, 7, 2, 9, 17], dtype=torch.int32, device=DEV)
+    _, od1 = attn_mixed(q, k, v, w.fwd[0].q_offset, qd, kc, vc, one, scale=w.fwd[0].scale)
+    ref1 = attn_decode(qd, kc, vc, one, scale=w.fwd[0].scale)
+    torch.cuda.synchronize()
+    assert torch.equal(od1, ref1)
+
+
+def test_mixed_chunk_equals_forward_bitwise():
+    """The LLaMA-3-8B chunk has few long units, so both gqa_attn_mixed and
+    gqa_attn_fwd run it as the same quad units over the same key ranges:
+    identical bits."""
+    w = WORKLOADS["llama3_8b_mixed"]
+    c = w.fwd[0]
+    q, k, v, qd, kc, vc, sl = _dev(mixed_inputs(c, w.decode, 7))
+    o, _ = attn_mixed(q, k, v, c.q_offset, qd, kc, vc, sl, scale=c.scale)
+    ref = attn_fwd(q, k, v, causal=True, q_offset=c.q_offset, scale=c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
 
 
 def test_mixed_bitwise_deterministic():
