@@ -5,14 +5,20 @@
 // into chunks so that each step's batch holds a prompt chunk beside the
 // decode tokens of other sequences.  Here both kinds of work come from one
 // persistent launch (the work-queue scheduler of the BootstrapAI evolution
-// log, "Kernel 8 -- persistent kernel", whose queue holds two kinds of
-// item): a workgroup first takes the chunk's prefill units, heaviest first,
-// and once they are gone takes decode splits from one more counter, DW at a
-// time (one per wave, each wave in an LDS area of its own).  So the decode
-// splits fill the CUs that the prefill units leave idle -- at the start when
-// the chunk has fewer units than resident workgroups, and in the tail.  The
+// log, "Kernel 8 -- persistent kernel", here with two kinds of item): a
+// workgroup first takes the chunk's prefill units, heaviest first, and once
+// they are gone takes decode splits from one more counter, DW at a time (one
+// per wave, each wave in an LDS area of its own).  So the decode splits go
+// to the CUs that the prefill units leave idle -- at the start when the
+// chunk has fewer units than resident workgroups, and in the tail.  The
 // decode rows' partial states are merged by the decode combine pass,
 // launched after this kernel.
+//
+// Prefill and decode waves never share a CU: the prefill units use the
+// whole register budget of two waves per SIMD, which leaves the decode
+// splits one register staging set per wave (two in the decode kernel).  On
+// the batches measured so far this launch is slower than a prefill call
+// followed by a decode call.
 //
 // Two prefill unit shapes, as for a prefill launch:
 //  * mixed_kernel: 4-wave workgroups on 128-column units from the XCD
