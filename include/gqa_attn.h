@@ -207,8 +207,10 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new,
  * runs as the quad schedule's units, others as the persistent schedule's;
  * the chunk's outputs equal gqa_attn_fwd's bit for bit when it picks the
  * same schedule, and to within rounding order otherwise.  The decode rows
- * are cut into about twice as many splits as gqa_attn_decode uses (eight
- * decode waves per CU), so they equal its outputs to within rounding order.
+ * use gqa_attn_decode's splits, and equal its outputs bit for bit, unless
+ * the chunk's units fill every resident workgroup; then they are cut into
+ * about twice as many splits (eight decode waves per CU, run in the chunk's
+ * tail) and equal its outputs to within rounding order.
  *
  * workspace: at least gqa_attn_decode_workspace_bytes(Bd, Hq, Hkv, Smax, d)
  * bytes when Bd > 0, as for gqa_attn_decode.  Calls that may run

@@ -384,8 +384,9 @@ using DecCfgF32 = gqa::TileCfg<float, D, 32, 1>;
 // CU) when every row is full, in whole 32-token tiles.  The split kernel's
 // registers allow one resident wave per SIMD; more, shorter splits only run
 // in a second round (measured slower from batch 32 up, as were two waves
-// per CU).  The mixed launch runs its splits eight waves per CU (waves_per_cu
-// = 8), each with one register stage instead of two.
+// per CU).  The mixed launch, whose decode waves hold one register stage,
+// sizes its splits for eight waves per CU (waves_per_cu = 8) when its
+// prefill units fill the device.
 int decode_split_tokens(int B, int Hkv, int ncb, int smax, int cus, int waves_per_cu = 4) {
   const long long tiles_per_row = (smax + 31) / 32;
   const long long heads = (long long)B * Hkv * ncb;
@@ -602,45 +603,60 @@ int decode_entry(const void* q, const void* kcache, const void* vcache, const in
 // combine pass.  A chunk of few, long units (at most two 64-column units
 // per CU, each of >= 8 key tiles) runs as quad units, whose four groups
 // split each unit's keys; any other chunk as the persistent schedule's
-// 128-column units.
+// 128-column units.  The decode splits are sized for eight decode waves per
+// CU when the chunk's units fill every resident workgroup (the splits then
+// run in the chunk's tail, where shorter ones end sooner), else for four,
+// as gqa_attn_decode sizes them (the splits run beside the units or alone,
+// where fewer, longer ones cost less: measured 31 against 47 us for the
+// LLaMA mixed batch's decode rows alone).
 template <typename T, class C, class CD>
 int launch_mixed(gqa::MixedArgs& m, int dev_id, const DeviceInfo& dev, hipStream_t stream) {
+  using CQ = gqa::TileCfg<T, C::D, C::BC, 2, C::KVS>;
+  bool quad = false;
+  gqa::MixedArgs mq = m;
+  if constexpr (8 * CQ::STAGE_BYTES <= kLdsBytes) {
+    if (m.p.T > 0) decompose(mq.p, 64);  // (no chunk: g = 0, nothing to decompose)
+    quad = m.p.T > 0 && mq.p.T <= 2LL * dev.cus && unit_tiles<CQ>(mq.p, true, 0) >= 8;
+  }
+  gqa::MixedArgs& a = quad ? mq : m;
+  const void* kern = nullptr;
+  int threads = C::NT, dw = gqa::mixed_decode_waves<C, CD>();
+  if constexpr (8 * CQ::STAGE_BYTES <= kLdsBytes) {
+    if (quad) {
+      kern = reinterpret_cast<const void*>(&gqa::mixed_quad_kernel<T, CQ, CD>);
+      threads = 4 * CQ::NT;
+      dw = gqa::mixed_quad_decode_waves<CQ, CD>();
+    }
+  }
+  if (!quad) kern = reinterpret_cast<const void*>(&gqa::mixed_kernel<T, C, CD>);
+  const long long slots = (long long)dev.cus * occupancy(kern, threads);
+  if (a.d.B > 0) {
+    decode_splits(a.d, dev.cus, a.p.T >= slots ? 8 : 4);
+    const long long nd = (long long)a.d.NS * a.d.Hkv * a.d.NCB * a.d.B;
+    if (nd > kIntMax / 2) return fail(GQA_ERR_BAD_SHAPE, "too many decode splits (%lld)", nd);
+    a.nd = (int)nd;
+  }
+  const long long work = (long long)a.p.T + ((long long)a.nd + dw - 1) / dw;
+  const long long grid = std::max<long long>(1, std::min<long long>(work, slots));
   StreamState ss;
   int st = stream_state(dev_id, stream, 0, &ss);
   if (st != GQA_OK) return st;
-  m.p.ctr = ss.ctr;
-  m.p.zero = 0;
+  a.p.ctr = ss.ctr;
+  a.p.zero = 0;
   (void)hipGetLastError();  // a stale error belongs to an earlier call
-  bool launched = false;
-  using CQ = gqa::TileCfg<T, C::D, C::BC, 2, C::KVS>;
   if constexpr (8 * CQ::STAGE_BYTES <= kLdsBytes) {
-    gqa::MixedArgs mq = m;
-    if (m.p.T > 0) decompose(mq.p, 64);  // (no chunk: g = 0, nothing to decompose)
-    if (m.p.T > 0 && mq.p.T <= 2LL * dev.cus && unit_tiles<CQ>(mq.p, true, 0) >= 8) {
-      const void* kern = reinterpret_cast<const void*>(&gqa::mixed_quad_kernel<T, CQ, CD>);
-      const long long slots = (long long)dev.cus * occupancy(kern, 4 * CQ::NT);
-      constexpr int DW = gqa::mixed_quad_decode_waves<CQ, CD>();
-      const long long work = (long long)mq.p.T + ((long long)mq.nd + DW - 1) / DW;
-      const long long grid = std::max<long long>(1, std::min<long long>(work, slots));
+    if (quad)
       hipLaunchKernelGGL((gqa::mixed_quad_kernel<T, CQ, CD>), dim3((unsigned)grid),
-                         dim3(4 * CQ::NT), 0, stream, mq);
-      launched = true;
-    }
+                         dim3(4 * CQ::NT), 0, stream, a);
   }
-  if (!launched) {
-    const void* kern = reinterpret_cast<const void*>(&gqa::mixed_kernel<T, C, CD>);
-    const long long slots = (long long)dev.cus * occupancy(kern, C::NT);
-    constexpr int DW = gqa::mixed_decode_waves<C, CD>();
-    const long long work = (long long)m.p.T + ((long long)m.nd + DW - 1) / DW;
-    const long long grid = std::max<long long>(1, std::min<long long>(work, slots));
+  if (!quad)
     hipLaunchKernelGGL((gqa::mixed_kernel<T, C, CD>), dim3((unsigned)grid), dim3(C::NT), 0,
-                       stream, m);
-  }
+                       stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "mixed kernel launch");
-  if (m.nd > 0) {
+  if (a.nd > 0) {
     hipLaunchKernelGGL((gqa::decode_combine_kernel<T, C::D, false>),
-                       dim3((unsigned)m.d.Hq, (unsigned)m.d.B), dim3(256), 0, stream, m.d);
+                       dim3((unsigned)a.d.Hq, (unsigned)a.d.B), dim3(256), 0, stream, a.d);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode combine kernel launch");
   }
@@ -696,12 +712,6 @@ int mixed_entry(const void* q, const void* k, const void* v, void* o, int B, int
   DeviceInfo info;
   int st = current_device(&dev, &info);
   if (st != GQA_OK) return st;
-  if (Bd > 0) {
-    decode_splits(m.d, info.cus, 8);
-    const long long nd = (long long)m.d.NS * m.d.Hkv * m.d.NCB * m.d.B;
-    if (nd > kIntMax / 2) return fail(GQA_ERR_BAD_SHAPE, "too many decode splits (%lld)", nd);
-    m.nd = (int)nd;
-  }
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (dtype == GQA_DTYPE_BF16)
     return dispatch_mixed<uint16_t, CfgBf16, DecCfgBf16>(m, d, dev, info, hs);

@@ -8,8 +8,8 @@ Cases span every head dim, MHA / GQA / MQA and groups wider than one column
 block, both prefill unit shapes (128-column persistent units; quad units
 for chunks of few long units), ragged chunk and cache lengths (empty, one
 slot, full capacity), a missing part, the LLaMA-3-8B mixed workload at full
-size, the decode rows' agreement with gqa_attn_decode and the quad chunk's
-bitwise identity with gqa_attn_fwd, determinism, and back-to-back calls of different
+size, the decode rows' agreement with gqa_attn_decode (bitwise where they
+use its splits) and the quad chunk's bitwise identity with gqa_attn_fwd, determinism, and back-to-back calls of different
 sizes sharing one stream's scheduler counters.
 """
 from __future__ import annotations
@@ -94,6 +94,23 @@ def test_mixed_one_part_missing():
     assert none_d is None and none_c is None
     ro, rod = oracle.attn_mixed(q, k, v, c.q_offset, qd, kc, vc, sl, scale=c.scale)
     assert _err(o, ro) <= TOL[c.dtype] and _err(od, rod) <= TOL[c.dtype]
+
+
+@pytest.mark.parametrize("chunk", [False, True], ids=["decode_only", "short_chunk"])
+def test_mixed_decode_rows_equal_decode_bitwise(chunk):
+    """Without a chunk, or with one whose units leave workgroups free, the
+    decode rows use gqa_attn_decode's splits, split code and combine pass:
+    identical bits."""
+    w = WORKLOADS["llama3_8b_mixed_c128"]
+    c = w.fwd[0]
+    q, k, v, qd, kc, vc, sl = _dev(mixed_inputs(c, w.decode, 12))
+    if not chunk:
+        q = k = v = None
+    o, od = attn_mixed(q, k, v, c.q_offset, qd, kc, vc, sl, scale=c.scale)
+    ref = attn_decode(qd, kc, vc, sl, scale=c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(od, ref)
+    assert (o is None) == (not chunk)
 
 
 def test_llama3_8b_mixed_full():
