@@ -688,9 +688,13 @@ int mixed_entry(const void* q, const void* k, const void* v, void* o, int B, int
   gqa::MixedArgs m;
   std::memset(&m, 0, sizeof(m));
   if (B > 0) {
-    const int64_t qs[3] = {(int64_t)Hq * Nq * d, (int64_t)Nq * d, d};
-    const int64_t kvs[3] = {(int64_t)Hkv * Nk * d, (int64_t)Nk * d, d};
-    if ((long long)Hq * Nq * d > (1LL << 62) / B || (long long)Hkv * Nk * d > (1LL << 62) / B)
+    // contiguous strides, computed only from sizes whose products fit; any
+    // other size is rejected by fwd_setup's own checks
+    const bool fits = Hq >= 1 && Hkv >= 1 && Nq >= 1 && Nk >= 1 && d >= 1 &&
+                      (long long)Nq * d <= kIntMax && (long long)Nk * d <= kIntMax;
+    const int64_t qs[3] = {fits ? (int64_t)Hq * Nq * d : 0, fits ? (int64_t)Nq * d : 0, d};
+    const int64_t kvs[3] = {fits ? (int64_t)Hkv * Nk * d : 0, fits ? (int64_t)Nk * d : 0, d};
+    if (fits && (qs[0] > (1LL << 62) / B || kvs[0] > (1LL << 62) / B))
       return fail(GQA_ERR_BAD_SHAPE, "chunk tensors too large");
     int st = fwd_setup(q, k, v, o, B, Hq, Hkv, Nq, Nk, d, qs, kvs, 1, q_offset, scale, dtype,
                        &m.p);

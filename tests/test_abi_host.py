@@ -264,6 +264,7 @@ def mixed(q=PM[0], k=PM[1], v=PM[2], o=PM[3], B=1, Nq=64, Nk=128, q_offset=64, q
     (dict(scale=float("nan")), UNSUP), (dict(ws=NUL), WS), (dict(ws_bytes=16), WS),
     (dict(kc=ctypes.c_void_p(0x10008)), UNSUP), (dict(q=ctypes.c_void_p(0x10004)), UNSUP),
     (dict(Bd=70000, ws_bytes=1 << 40), SHAPE),
+    (dict(Nq=1 << 28, d=128), SHAPE), (dict(Hq=1 << 30, Hkv=1 << 30, Nq=1 << 24), SHAPE),
 ], ids=lambda x: str(x))
 def test_mixed_rejects_invalid_arguments(kw, code):
     assert mixed(**kw) == code
