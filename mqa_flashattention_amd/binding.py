@@ -338,6 +338,10 @@ def attn_mixed(q: torch.Tensor | None, k: torch.Tensor | None, v: torch.Tensor |
     position q_offset + i (q is None: no chunk).  Decode rows: qd [Bd, Hq, d],
     kcache, vcache [Bd, Hkv, Smax, d], seqlens int32 [Bd] (qd is None: no
     decode rows).  Returns (o, od); the missing part's entry is None."""
+    if q is not None and (k is None or v is None):
+        raise ValueError("a chunk needs q, k and v")
+    if qd is not None and (kcache is None or vcache is None or seqlens is None):
+        raise ValueError("decode rows need qd, kcache, vcache and seqlens")
     ref = q if q is not None else qd
     if ref is None:
         return None, None

@@ -285,3 +285,14 @@ def test_valid_mixed_call_without_gpu_reports_no_device():
     assert mixed() == NODEV
     assert mixed(q=NUL, k=NUL, v=NUL, o=NUL, B=0) == NODEV           # decode rows only
     assert mixed(qd=NUL, kc=NUL, vc=NUL, lens=NUL, od=NUL, Bd=0, ws=NUL, ws_bytes=0) == NODEV
+
+
+def test_mixed_binding_checks_parts_before_the_library():
+    q = torch.zeros(1, 4, 8, 32, dtype=torch.bfloat16)
+    assert binding.attn_mixed(None, None, None, 0, None, None, None, None) == (None, None)
+    with pytest.raises(ValueError):
+        binding.attn_mixed(q, None, None, 0, None, None, None, None)
+    with pytest.raises(ValueError):
+        binding.attn_mixed(None, None, None, 0, q[:, :, 0], q, None, None)
+    with pytest.raises(ValueError):  # CPU tensors are refused
+        binding.attn_mixed(q, q[:, :2], q[:, :2], 0, None, None, None, None)
