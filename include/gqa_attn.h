@@ -215,7 +215,9 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new,
  * workspace: at least gqa_attn_decode_workspace_bytes(Bd, Hq, Hkv, Smax, d)
  * bytes when Bd > 0, as for gqa_attn_decode.  Calls that may run
  * concurrently must use different streams (each stream has its own
- * scheduler counters) and different workspaces.
+ * scheduler counters) and different workspaces.  The first call on a
+ * stream allocates and clears that stream's counters; later calls allocate
+ * nothing and record no memset, so they may be captured in a HIP graph.
  *
  * Errors: B < 0 or Bd < 0 -> GQA_ERR_BAD_SHAPE; a NULL pointer of a part
  * that is present -> GQA_ERR_NULL_POINTER; otherwise each present part is

@@ -19,7 +19,7 @@ import pytest
 import torch
 
 import oracle
-from mqa_flashattention_amd import attn_decode, attn_fwd, attn_mixed
+from mqa_flashattention_amd import attn_decode, attn_fwd, attn_mixed, decode_workspace_bytes
 from mqa_flashattention_amd.workloads import (WORKLOADS, DecodeShape, FwdShape, fwd_inputs,
                                               mixed_inputs)
 
@@ -181,3 +181,41 @@ def test_mixed_calls_of_different_sizes_share_counters():
         ids = np.array([0, 2047, 32 * 2048 + 5, 2 * 32 * 2048 - 1])
         rf = oracle.attn_fwd_rows(fq, fk, fv, ids, causal=True, scale=fwd_s.scale)
         assert _err(fo.reshape(-1, 128)[torch.from_numpy(ids).to(DEV)], rf) <= TOL[fwd_s.dtype]
+
+
+def test_mixed_graph_replay_matches_eager():
+    """A serving loop may capture the mixed call in a HIP graph.  One eager
+    call on the capture stream first sets up that stream's scheduler
+    counters (the only allocation); the captured launches then replay, each
+    leaving the counters at zero for the next.  Every replay, with outputs
+    poisoned before it and eager calls between replays, gives the eager bits."""
+    w = WORKLOADS["llama3_8b_mixed_c128"]
+    c, r = w.fwd[0], w.decode
+    q, k, v, qd, kc, vc, sl = _dev(mixed_inputs(c, r, 14))
+    ws = torch.empty(decode_workspace_bytes(r.B, r.Hq, r.Hkv, r.Smax, r.d), dtype=torch.uint8,
+                     device=DEV)
+    o, od = torch.empty_like(q), torch.empty_like(qd)
+    s = torch.cuda.Stream()
+
+    def call():
+        attn_mixed(q, k, v, c.q_offset, qd, kc, vc, sl, scale=c.scale, out=o, out_decode=od,
+                   workspace=ws)
+
+    with torch.cuda.stream(s):
+        call()
+    s.synchronize()
+    ref_o, ref_od = o.clone(), od.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for _ in range(4):
+        o.fill_(float("nan"))
+        od.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(od, ref_od)
+        with torch.cuda.stream(s):
+            call()
+        s.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(od, ref_od)
