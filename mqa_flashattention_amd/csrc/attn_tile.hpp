@@ -188,9 +188,15 @@ __device__ __forceinline__ void load_tile(TileRegs<C>& r, const T* __restrict__ 
   // unsigned 32 x 32 -> 64-bit byte offset: scalar multiplies (a signed
   // 64-bit product would be done on the vector unit)
   const uint64_t base = (uint64_t)(uint32_t)key0 * (uint32_t)ROWB;
-  // the range is uniform; readfirstlane keeps it (and so the resource) in
-  // scalar registers -- a vector value here makes every load a waterfall loop
-  const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)(rows * ROWB));
+  // The range ends with the last existing row's last byte: (rows - 1) rows
+  // apart, then one row of D elements.  For contiguous rows that is
+  // rows * ROWB; for a token stride below a row's width (overlapping or
+  // broadcast rows, stride 0 included) it still covers every row that
+  // exists.  The range is uniform; readfirstlane keeps it (and so the
+  // resource) in scalar registers -- a vector value here makes every load a
+  // waterfall loop.
+  const int span = rows > 0 ? (rows - 1) * ROWB + C::D * C::ESZ : 0;
+  const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)span);
   const auto krs = buffer_rsrc(reinterpret_cast<const char*>(kbase) + base, bytes);
   const auto vrs = buffer_rsrc(reinterpret_cast<const char*>(vbase) + base, bytes);
 #pragma unroll

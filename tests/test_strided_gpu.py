@@ -121,3 +121,44 @@ def test_broadcast_kv_over_batch():
     ref = oracle.attn_fwd(q, k1.expand(B, Hkv, N, d), v1.expand(B, Hkv, N, d), causal=True)
     err = float(np.max(np.abs(out.cpu().double().numpy() - ref)))
     assert err <= TOL[torch.bfloat16], f"max abs error {err}"
+
+
+def test_broadcast_kv_over_tokens():
+    """A zero K/V token stride: every key row is the same row (expand over
+    tokens), so each query's output is that V row exactly in exact arithmetic."""
+    B, Hq, Hkv, Nq, Nk, d = 2, 8, 2, 50, 90, 128
+    q = random_tensor((B, Hq, Nq, d), 41, torch.bfloat16)
+    k1 = random_tensor((B, Hkv, 1, d), 42, torch.bfloat16)
+    v1 = random_tensor((B, Hkv, 1, d), 43, torch.bfloat16)
+    kb = k1.to(DEV).expand(B, Hkv, Nk, d)
+    vb = v1.to(DEV).expand(B, Hkv, Nk, d)
+    assert kb.stride(2) == 0
+    for causal, off in ((False, 0), (True, 3)):
+        out = attn_fwd_strided(q.to(DEV), kb, vb, causal=causal, q_offset=off)
+        torch.cuda.synchronize()
+        ref = oracle.attn_fwd(q, k1.expand(B, Hkv, Nk, d), v1.expand(B, Hkv, Nk, d),
+                              causal=causal, q_offset=off)
+        err = float(np.max(np.abs(out.cpu().double().numpy() - ref)))
+        assert err <= TOL[torch.bfloat16], f"causal={causal}: max abs error {err}"
+
+
+@pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.float32)])
+def test_overlapping_kv_window(d, dtype):
+    """K/V rows that overlap: key row j is elements [j*d/2, j*d/2 + d) of one
+    flat buffer per head (a token stride of half a row)."""
+    B, Hq, Hkv, Nq, Nk = 1, 4, 2, 40, 77
+    esz = 2 if dtype == torch.bfloat16 else 4
+    step = d // 2
+    assert (step * esz) % 16 == 0
+    flat_n = (Nk - 1) * step + d
+    kf = random_tensor((B, Hkv, flat_n), 44, dtype).to(DEV)
+    vf = random_tensor((B, Hkv, flat_n), 45, dtype).to(DEV)
+    kw = kf.as_strided((B, Hkv, Nk, d), (Hkv * flat_n, flat_n, step, 1))
+    vw = vf.as_strided((B, Hkv, Nk, d), (Hkv * flat_n, flat_n, step, 1))
+    q = random_tensor((B, Hq, Nq, d), 46, dtype)
+    out = attn_fwd_strided(q.to(DEV), kw, vw, causal=True, q_offset=Nk - Nq)
+    torch.cuda.synchronize()
+    ref = oracle.attn_fwd(q, kw.cpu().contiguous(), vw.cpu().contiguous(), causal=True,
+                          q_offset=Nk - Nq)
+    err = float(np.max(np.abs(out.cpu().double().numpy() - ref)))
+    assert err <= TOL[dtype], f"max abs error {err}"
