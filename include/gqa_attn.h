@@ -147,6 +147,32 @@ int gqa_attn_decode(const void* q, const void* kcache, const void* vcache,
                     int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gqa_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP-graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing -- no hipMalloc, no
+ * allocating library call -- and takes its split records from a static
+ * device array of GQA_DECODE_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each GPU it runs on until the process ends.
+ *
+ * Arguments, layouts, semantics, status codes and outputs are those of
+ * gqa_attn_decode (the same kernels, the same splits: the results are
+ * bit-identical to a gqa_attn_decode call on the same inputs).  A call
+ * whose gqa_attn_decode_workspace_bytes(B, Hq, Hkv, Smax, d) exceeds
+ * GQA_DECODE_NOALLOC_SCRATCH_BYTES returns GQA_ERR_WORKSPACE, before any
+ * HIP call.
+ *
+ * Every call on one GPU shares that GPU's scratch array: calls that may
+ * overlap in time on one GPU (on different streams, or a captured graph
+ * replayed while another call runs) race on it and are not allowed.  Calls
+ * ordered on one stream are fine; nothing in the array has to start zeroed.
+ */
+#define GQA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int gqa_attn_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                            const int32_t* seqlens, void* o,
+                            int B, int Hq, int Hkv, int Smax, int d, float scale,
+                            int dtype, void* stream);
+
+/*
  * Decode step that also appends the new token's K/V to the caches, in the
  * same launch.
  *

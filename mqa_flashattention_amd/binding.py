@@ -27,7 +27,7 @@ STATUS_NAMES = {
     4: "GQA_ERR_UNSUPPORTED", 5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_NO_DEVICE", 7: "GQA_ERR_HIP",
 }
 EXPORTED = ("gqa_attn_fwd", "gqa_attn_fwd_strided", "gqa_attn_decode",
-            "gqa_attn_decode_append", "gqa_attn_decode_workspace_bytes", "gqa_attn_bwd",
+            "gqa_attn_decode_noalloc", "gqa_attn_decode_append", "gqa_attn_decode_workspace_bytes", "gqa_attn_bwd",
             "gqa_attn_bwd_workspace_bytes", "gqa_attn_mixed", "gqa_status_string",
             "gqa_last_error_string")
 
@@ -55,6 +55,8 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_decode_workspace_bytes.restype = sz
     lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.gqa_attn_decode.restype = i
+    lib.gqa_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.gqa_attn_decode_noalloc.restype = i
     lib.gqa_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp,
                                            sz, vp]
     lib.gqa_attn_decode_append.restype = i
@@ -269,6 +271,44 @@ def attn_decode(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
                                  float(scale), _DTYPES[q.dtype], workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(),
                                  _stream_handle(dev))
+    _raise(st)
+    return out
+
+
+# Bytes of the static scratch behind gqa_attn_decode_noalloc (the header's
+# GQA_DECODE_NOALLOC_SCRATCH_BYTES).
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def attn_decode_noalloc(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                        seqlens: torch.Tensor, out: torch.Tensor, *,
+                        scale: float | None = None) -> torch.Tensor:
+    """attn_decode via gqa_attn_decode_noalloc: no workspace, and nothing is
+    allocated -- out must be given (shape and dtype of q); the split records
+    live in the library's static scratch on the GPU.  Calls that may overlap
+    on one GPU must not use it."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _check_tensor("q", q, 3, q.dtype, dev)
+    _check_tensor("kcache", kcache, 4, q.dtype, dev)
+    _check_tensor("vcache", vcache, 4, q.dtype, dev)
+    _check_tensor("seqlens", seqlens, 1, torch.int32, dev)
+    _check_tensor("out", out, 3, q.dtype, dev)
+    B, Hq, d = q.shape
+    _, Hkv, Smax, _ = kcache.shape
+    if kcache.shape[0] != B or kcache.shape[3] != d or tuple(vcache.shape) != tuple(kcache.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} kcache{tuple(kcache.shape)}")
+    if seqlens.shape[0] != B:
+        raise ValueError("seqlens must have B entries")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have the shape of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(dev):
+        st = lib.gqa_attn_decode_noalloc(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(),
+                                         seqlens.data_ptr(), out.data_ptr(), B, Hq, Hkv, Smax,
+                                         d, float(scale), _DTYPES[q.dtype], _stream_handle(dev))
     _raise(st)
     return out
 

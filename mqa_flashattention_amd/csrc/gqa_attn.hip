@@ -371,6 +371,37 @@ int dispatch_prefill(gqa::PrefillArgs& a, int d, int causal, int dev_id,
   }
 }
 
+// ------------------------------------------------------------------ static scratch
+
+// Scratch of gqa_attn_decode_noalloc, for callers that cannot allocate: the
+// split records of one decode call, in a file-scope device array.  Each GPU
+// the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: host code
+// uses only the address hipGetSymbolAddress returns for the current device
+// (kept per device by scratch_address), never the array's name.
+constexpr size_t kNoAllocScratchBytes = GQA_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::map<int, void*> g_scratch;  // device -> address of its copy of `scratch`
+
+// The address of `scratch` on device dev, which must be the current device.
+int scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                      "hipGetSymbolAddress(static decode scratch)");
+    }
+    it = g_scratch.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return GQA_OK;
+}
+
 // ------------------------------------------------------------------ decode
 
 constexpr int kMinSplit = 32;
@@ -515,10 +546,12 @@ int fwd_entry(const void* q, const void* k, const void* v, void* o, int B, int H
 // caches are written at them).
 // Validation and launch arguments of a decode call, all but the split size
 // (decode_splits).  Pure host code: no HIP call.
+// check_ws == false: the caller supplies the workspace after validation (the
+// static scratch of gqa_attn_decode_noalloc, whose size it checks itself).
 int decode_setup(const void* q, const void* kcache, const void* vcache, const int32_t* lens,
                  const void* knew, const void* vnew, void* kc_out, void* vc_out, void* o, int B,
                  int Hq, int Hkv, int Smax, int d, float scale, int dtype, void* workspace,
-                 size_t workspace_bytes, gqa::DecodeArgs* out) {
+                 size_t workspace_bytes, gqa::DecodeArgs* out, bool check_ws = true) {
   const bool append = knew != nullptr;
   if (B < 1 || Hq < 1 || Hkv < 1 || Smax < 1 || d < 1)
     return fail(GQA_ERR_BAD_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Smax=%d d=%d)", B, Hq,
@@ -535,7 +568,7 @@ int decode_setup(const void* q, const void* kcache, const void* vcache, const in
       (append && (!aligned16(knew) || !aligned16(vnew))))
     return fail(GQA_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
   const size_t need = decode_ws_bytes(B, Hq, Smax, d, kMinSplit);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+  if (check_ws && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(GQA_ERR_WORKSPACE, "workspace needs %zu bytes, 16-byte aligned (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
   const int g = Hq / Hkv;
@@ -572,19 +605,35 @@ void decode_splits(gqa::DecodeArgs& a, int cus, int waves_per_cu = 4) {
   a.NS = (a.Smax + a.S_TOK - 1) / a.S_TOK;
 }
 
+// static_ws: the records go to this device's static scratch array instead of
+// a caller workspace (workspace / workspace_bytes are ignored).
 int decode_entry(const void* q, const void* kcache, const void* vcache, const int32_t* lens,
                  const void* knew, const void* vnew, void* kc_out, void* vc_out, void* o, int B,
                  int Hq, int Hkv, int Smax, int d, float scale, int dtype, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 size_t workspace_bytes, void* stream, bool static_ws = false) {
   const bool append = knew != nullptr;
   gqa::DecodeArgs a;
   int st = decode_setup(q, kcache, vcache, lens, knew, vnew, kc_out, vc_out, o, B, Hq, Hkv, Smax,
-                        d, scale, dtype, workspace, workspace_bytes, &a);
+                        d, scale, dtype, workspace, workspace_bytes, &a, !static_ws);
   if (st != GQA_OK) return st;
+  if (static_ws) {
+    const size_t need = decode_ws_bytes(B, Hq, Smax, d, kMinSplit);
+    if (need > kNoAllocScratchBytes)
+      return fail(GQA_ERR_WORKSPACE,
+                  "this decode needs %zu bytes of split records; the static scratch of "
+                  "gqa_attn_decode_noalloc holds %zu",
+                  need, kNoAllocScratchBytes);
+  }
   int dev = 0;
   DeviceInfo info;
   st = current_device(&dev, &info);
   if (st != GQA_OK) return st;
+  if (static_ws) {
+    void* p = nullptr;
+    st = scratch_address(dev, &p);
+    if (st != GQA_OK) return st;
+    a.ws = reinterpret_cast<float*>(p);
+  }
   decode_splits(a, info.cus);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
@@ -965,6 +1014,16 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new, 
                 "q, k_new, v_new, kcache, vcache, positions and o must be non-NULL");
   return decode_entry(q, kcache, vcache, positions, k_new, v_new, kcache, vcache, o, B, Hq, Hkv,
                       Smax, d, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+int gqa_attn_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                            const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int Smax,
+                            int d, float scale, int dtype, void* stream) {
+  g_last_error.clear();
+  if (!q || !kcache || !vcache || !seqlens || !o)
+    return fail(GQA_ERR_NULL_POINTER, "q, kcache, vcache, seqlens and o must be non-NULL");
+  return decode_entry(q, kcache, vcache, seqlens, nullptr, nullptr, nullptr, nullptr, o, B, Hq,
+                      Hkv, Smax, d, scale, dtype, nullptr, 0, stream, true);
 }
 
 size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {

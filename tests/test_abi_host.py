@@ -103,6 +103,36 @@ def test_decode_rejects_invalid_arguments(kw, code):
     assert binding.lib.gqa_last_error_string()
 
 
+def dec_na(q=P[0], kc=P[1], vc=P[2], sl=P[4], o=P[3], B=8, Hq=12, Hkv=2, Smax=2048, d=128,
+           scale=0.09, dtype=BF16, stream=None):
+    return binding.lib.gqa_attn_decode_noalloc(q, kc, vc, sl, o, B, Hq, Hkv, Smax, d,
+                                               ctypes.c_float(scale), dtype, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(kc=None), NULLP), (dict(vc=None), NULLP),
+    (dict(sl=None), NULLP), (dict(o=None), NULLP),
+    (dict(B=0), SHAPE), (dict(Smax=0), SHAPE), (dict(Smax=2 ** 25, d=128), SHAPE),
+    (dict(Hq=12, Hkv=5), GROUP), (dict(d=80), UNSUP), (dict(dtype=7), UNSUP),
+    (dict(kc=ctypes.c_void_p(0x20004)), UNSUP),
+    # split records beyond the static scratch
+    (dict(B=64, Hq=32, Hkv=8, Smax=32768), WS),
+])
+def test_decode_noalloc_rejects_invalid_arguments(kw, code):
+    assert dec_na(**kw) == code
+    assert binding.lib.gqa_last_error_string()
+
+
+def test_decode_noalloc_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define GQA_DECODE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m, "limit not found in the header"
+    assert int(m.group(1)) << int(m.group(2)) == binding.DECODE_NOALLOC_SCRATCH_BYTES
+    # the batch-8 decode workload fits
+    assert binding.decode_workspace_bytes(8, 12, 2, 2048, 128) <= \
+        binding.DECODE_NOALLOC_SCRATCH_BYTES
+
+
 def fwd_s(q=P[0], k=P[1], v=P[2], o=P[3], B=2, Hq=8, Hkv=2, Nq=64, Nk=96, d=64, qs=None,
           kvs=None, causal=1, q_offset=0, scale=0.17, dtype=BF16, stream=None):
     """Strided forward; default strides are BTHD (token-major)."""
@@ -175,6 +205,7 @@ def test_valid_call_without_gpu_reports_no_device():
     assert fwd() == NODEV
     assert b"device" in binding.lib.gqa_last_error_string()
     assert dec() == NODEV
+    assert dec_na() == NODEV
     assert app() == NODEV
     assert fwd_s() == NODEV
     # zero K/V batch stride (broadcast reads) is valid
