@@ -19,7 +19,9 @@ append first writes each active row's new K/V rows at its position (the
 single-launch K/V store and per-row position table of the microLLM-rocm
 optimization log, experiments 025, 083/084 and 098) and then attends slots
 [0, position].  A mixed batch (a chunked-prefill chunk beside decode rows,
-kaispace.site note "Chunked Prefill") is the two definitions side by side.
+kaispace.site note "Chunked Prefill") is the two definitions side by side,
+and a packed batch of sequences of different lengths (attn_fwd_varlen) is
+the forward definition applied to each sequence on its own.
 The backward gives dQ, dK, dV of a loss with dL/dO given,
 the K/V gradients reduced over each K/V head's query heads (microLLM-rocm
 optimization log, experiments 044 and 051-054).
@@ -139,6 +141,56 @@ def attn_fwd_rows(q, k, v, row_ids, *, causal: bool = False, q_offset: int = 0,
                                     ids.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                     ids.size, _ptr(out)), "attn_fwd_rows")
     return out
+
+
+def _varlen_offsets(cu) -> np.ndarray:
+    if hasattr(cu, "detach"):
+        cu = cu.detach().to("cpu").numpy()
+    return np.asarray(cu, dtype=np.int64)
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool = False,
+                    scale: float | None = None, lib: ctypes.CDLL | None = None) -> np.ndarray:
+    """O[total_q, Hq, d] (float64) for packed token-major q[total_q, Hq, d] and
+    k, v[total_k, Hkv, d] holding several sequences back to back.
+
+    Sequence s owns query rows [cu_q[s], cu_q[s+1]) and key rows
+    [cu_k[s], cu_k[s+1]) (nseq + 1 offsets each, first 0).  Its output is the
+    forward definition on its own tensors: query row i (0-based within the
+    sequence) sits at position Nk_s - Nq_s + i -- the queries are the
+    sequence's last Nq_s tokens, as a chunk of a prompt is (kaispace.site
+    note "Chunked Prefill"), and the whole prompt when Nq_s = Nk_s -- and,
+    causal, sees the keys j <= Nk_s - Nq_s + i.  A row that sees no key
+    (Nk_s = 0, or causal rows i < Nq_s - Nk_s) is zero, as an empty decode
+    row is.  Composed per sequence from attn_fwd; no arithmetic of its own."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cq, ck = _varlen_offsets(cu_seqlens_q), _varlen_offsets(cu_seqlens_k)
+    if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape or cq.shape != ck.shape:
+        raise ValueError("attn_fwd_varlen: q [Tq,Hq,d], k/v [Tk,Hkv,d], offsets [nseq+1]")
+    d = q.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.zeros_like(q)
+    for s in range(len(cq) - 1):
+        q0, q1, k0, k1 = int(cq[s]), int(cq[s + 1]), int(ck[s]), int(ck[s + 1])
+        nq, nk = q1 - q0, k1 - k0
+        if nq <= 0 or nk <= 0:
+            continue
+        qs = q[q0:q1].transpose(1, 0, 2)[None]          # [1, Hq, Nq, d]
+        ks = k[k0:k1].transpose(1, 0, 2)[None]          # [1, Hkv, Nk, d]
+        vs = v[k0:k1].transpose(1, 0, 2)[None]
+        if not causal:
+            os_ = attn_fwd(qs, ks, vs, causal=False, scale=scale, lib=lib)
+            o[q0:q1] = os_[0].transpose(1, 0, 2)
+            continue
+        off = nk - nq
+        first = max(0, -off)                          # rows before it see no key
+        if first >= nq:
+            continue
+        os_ = attn_fwd(qs[:, :, first:], ks, vs, causal=True, q_offset=off + first, scale=scale,
+                       lib=lib)
+        o[q0 + first:q1] = os_[0].transpose(1, 0, 2)
+    return o
 
 
 def attn_probs(q, k, v, b: int, h: int, i: int, *, causal: bool = False, q_offset: int = 0,

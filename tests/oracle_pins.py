@@ -527,6 +527,109 @@ def pin_bwd_gqa_equals_replicated_mha(lib):
     assert _maxerr(dv, dv2.reshape(B, Hkv, g, Nk, d).sum(axis=2)) <= TOL
 
 
+# ---------------------------------------------------------------- packed varlen
+
+def _varlen_case(seed, lens_q, lens_k, Hq, Hkv, d):
+    cq = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
+    ck = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int64)
+    q = _rand((int(cq[-1]), Hq, d), seed)
+    k = _rand((int(ck[-1]), Hkv, d), seed + 1)
+    v = _rand((int(ck[-1]), Hkv, d), seed + 2)
+    return q, k, v, cq, ck
+
+
+VARLEN_CASES = [
+    # (lens_q, lens_k, Hq, Hkv, d): ragged mixes, empty and one-token sequences,
+    # more queries than keys (causal rows that see no key), no keys at all
+    ([5, 0, 7, 1, 3], [9, 3, 3, 0, 3], 4, 2, 8),
+    ([1, 1, 1], [1, 6, 2], 3, 3, 4),
+    ([12], [12], 6, 2, 8),
+    ([4, 9, 2], [17, 9, 11], 2, 1, 32),
+]
+
+
+def pin_varlen_library(lib):
+    """Packed varlen vs the library attention routine on each sequence's own
+    tensors, with the mask written out: query i of a sequence with Nq queries
+    and Nk keys sees keys j <= Nk - Nq + i (its queries are its last Nq
+    tokens); a row that sees no key is zero by definition."""
+    import torch
+    import torch.nn.functional as F
+    for t, (lq, lk, Hq, Hkv, d) in enumerate(VARLEN_CASES):
+        q, k, v, cq, ck = _varlen_case(700 + 5 * t, lq, lk, Hq, Hkv, d)
+        scale = 1.0 / math.sqrt(d)
+        for causal in (False, True):
+            o = oracle.attn_fwd_varlen(q, k, v, cq, ck, causal=causal, scale=scale, lib=lib)
+            for s in range(len(lq)):
+                q0, q1, k0, k1 = cq[s], cq[s + 1], ck[s], ck[s + 1]
+                nq, nk = q1 - q0, k1 - k0
+                if nq == 0:
+                    continue
+                want = np.zeros((nq, Hq, d))
+                if nk > 0:
+                    qt = torch.from_numpy(q[q0:q1].transpose(1, 0, 2).copy())
+                    kt = torch.from_numpy(k[k0:k1].transpose(1, 0, 2).copy())
+                    vt = torch.from_numpy(v[k0:k1].transpose(1, 0, 2).copy())
+                    kt = kt.repeat_interleave(Hq // Hkv, dim=0)
+                    vt = vt.repeat_interleave(Hq // Hkv, dim=0)
+                    i = torch.arange(nq)[:, None]
+                    j = torch.arange(nk)[None, :]
+                    mask = (j <= nk - nq + i) if causal else torch.ones(nq, nk, dtype=torch.bool)
+                    seen = mask.any(dim=1)
+                    out = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+                    out = torch.where(seen[None, :, None], out, torch.zeros_like(out))
+                    want = out.numpy().transpose(1, 0, 2)
+                err = _maxerr(o[q0:q1], want)
+                assert err <= TOL, f"case {t} seq {s} causal={causal}: err {err}"
+
+
+def pin_varlen_sequence_independence(lib):
+    """A sequence's rows depend on its own tokens only: redrawing every other
+    sequence's queries, keys and values leaves them bit-identical."""
+    lq, lk, Hq, Hkv, d = VARLEN_CASES[3]
+    q, k, v, cq, ck = _varlen_case(900, lq, lk, Hq, Hkv, d)
+    o = oracle.attn_fwd_varlen(q, k, v, cq, ck, causal=True, lib=lib)
+    q2, k2, v2 = _rand(q.shape, 901), _rand(k.shape, 902), _rand(v.shape, 903)
+    s = 1
+    q2[cq[s]:cq[s + 1]] = q[cq[s]:cq[s + 1]]
+    k2[ck[s]:ck[s + 1]] = k[ck[s]:ck[s + 1]]
+    v2[ck[s]:ck[s + 1]] = v[ck[s]:ck[s + 1]]
+    o2 = oracle.attn_fwd_varlen(q2, k2, v2, cq, ck, causal=True, lib=lib)
+    assert np.array_equal(o[cq[s]:cq[s + 1]], o2[cq[s]:cq[s + 1]])
+    assert not np.array_equal(o, o2)
+
+
+def pin_varlen_reorder(lib):
+    """Packing the sequences in reverse order reverses the output blocks."""
+    lq, lk, Hq, Hkv, d = VARLEN_CASES[0]
+    q, k, v, cq, ck = _varlen_case(950, lq, lk, Hq, Hkv, d)
+    o = oracle.attn_fwd_varlen(q, k, v, cq, ck, causal=True, lib=lib)
+    n = len(lq)
+    rq = [q[cq[s]:cq[s + 1]] for s in reversed(range(n))]
+    rk = [k[ck[s]:ck[s + 1]] for s in reversed(range(n))]
+    rv = [v[ck[s]:ck[s + 1]] for s in reversed(range(n))]
+    rcq = np.concatenate([[0], np.cumsum(lq[::-1])])
+    rck = np.concatenate([[0], np.cumsum(lk[::-1])])
+    ro = oracle.attn_fwd_varlen(np.concatenate(rq), np.concatenate(rk), np.concatenate(rv),
+                                rcq, rck, causal=True, lib=lib)
+    want = np.concatenate([o[cq[s]:cq[s + 1]] for s in reversed(range(n))])
+    assert np.array_equal(ro, want)
+
+
+def pin_varlen_full_prompt_row0(lib):
+    """A sequence with as many queries as keys is a whole prompt: causal row 0
+    returns V[0] of its own keys exactly, and its last row equals the
+    non-causal pass over all its keys."""
+    lq, lk, Hq, Hkv, d = VARLEN_CASES[2]
+    q, k, v, cq, ck = _varlen_case(980, lq, lk, Hq, Hkv, d)
+    o = oracle.attn_fwd_varlen(q, k, v, cq, ck, causal=True, lib=lib)
+    g = Hq // Hkv
+    for h in range(Hq):
+        assert np.array_equal(o[0, h], v[0, h // g])
+    full = oracle.attn_fwd_varlen(q, k, v, cq, ck, causal=False, lib=lib)
+    assert _maxerr(o[-1], full[-1]) <= TOL
+
+
 PINS = [
     pin_library_attention,
     pin_decode_library,
@@ -555,6 +658,10 @@ PINS = [
     pin_bwd_closed_forms,
     pin_bwd_key_sum_zero,
     pin_bwd_gqa_equals_replicated_mha,
+    pin_varlen_library,
+    pin_varlen_sequence_independence,
+    pin_varlen_reorder,
+    pin_varlen_full_prompt_row0,
 ]
 
 

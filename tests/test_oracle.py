@@ -211,5 +211,64 @@ def test_planted_mixed_mistake_is_caught(lib, monkeypatch, wrong):
         oracle_pins.pin_mixed_decode_rows_are_chunk_rows(lib)
 
 
+# Planted mistakes in the packed varlen composition (Python): each wrong
+# attn_fwd_varlen must fail one of the varlen pins.
+def _varlen_mutant(kind):
+    def f(q, k, v, cu_q, cu_k, *, causal=False, scale=None, lib=None):
+        q, k, v = oracle._f64(q), oracle._f64(k), oracle._f64(v)
+        cq, ck = np.asarray(cu_q, dtype=np.int64), np.asarray(cu_k, dtype=np.int64)
+        if kind == "keys from query offsets":
+            ck = cq.copy()
+            ck[-1] = min(ck[-1], k.shape[0])
+            ck = np.minimum(ck, k.shape[0])
+        d = q.shape[2]
+        scale = 1.0 / np.sqrt(d) if scale is None else scale
+        o = np.zeros_like(q)
+        for s in range(len(cq) - 1):
+            q0, q1, k0, k1 = int(cq[s]), int(cq[s + 1]), int(ck[s]), int(ck[s + 1])
+            if kind == "rows shifted by one" and s > 0:
+                q0, q1 = q0 - 1, q1 - 1
+            nq, nk = q1 - q0, k1 - k0
+            if nq <= 0 or nk <= 0:
+                continue
+            qs = q[q0:q1].transpose(1, 0, 2)[None]
+            ks = k[k0:k1].transpose(1, 0, 2)[None]
+            vs = v[k0:k1].transpose(1, 0, 2)[None]
+            if not causal:
+                o[q0:q1] = oracle.attn_fwd(qs, ks, vs, scale=scale, lib=lib)[0].transpose(1, 0, 2)
+                continue
+            off = nk - nq
+            if kind == "top-left alignment":
+                off = 0
+            first = max(0, -off)
+            if kind == "keyless rows get the mean of V":
+                o[q0:q0 + first] = vs[0].mean(axis=1).repeat(q.shape[1] // k.shape[1], 0)
+            if first >= nq:
+                continue
+            os_ = oracle.attn_fwd(qs[:, :, first:], ks, vs, causal=True, q_offset=off + first,
+                                  scale=scale, lib=lib)
+            o[q0 + first:q1] = os_[0].transpose(1, 0, 2)
+        return o
+    f.__name__ = kind.replace(" ", "_")
+    return f
+
+
+VARLEN_MUTANTS = ["top-left alignment", "keys from query offsets", "rows shifted by one",
+                  "keyless rows get the mean of V"]
+
+
+@pytest.mark.parametrize("kind", VARLEN_MUTANTS)
+def test_planted_varlen_mistake_is_caught(lib, monkeypatch, kind):
+    monkeypatch.setattr(oracle, "attn_fwd_varlen", _varlen_mutant(kind))
+    caught = False
+    for pin in (oracle_pins.pin_varlen_library, oracle_pins.pin_varlen_sequence_independence,
+                oracle_pins.pin_varlen_reorder, oracle_pins.pin_varlen_full_prompt_row0):
+        try:
+            pin(lib)
+        except Exception:
+            caught = True
+    assert caught, f"varlen mutant '{kind}' passed every varlen pin"
+
+
 def test_pin_module_importable():
     assert len(oracle_pins.PINS) >= 15
