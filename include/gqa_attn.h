@@ -115,6 +115,44 @@ int gqa_attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
                          int dtype, void* stream);
 
 /*
+ * Packed variable-length forward: nseq sequences of different lengths back
+ * to back in token-major tensors, one launch, no padding.
+ *
+ *   q, o          : [total_q, Hq, d]   (token-major: token, head, d)
+ *   k, v          : [total_k, Hkv, d]
+ *   cu_seqlens_q  : int32[nseq + 1], device memory; sequence s owns query
+ *                   rows [cu_seqlens_q[s], cu_seqlens_q[s+1])
+ *   cu_seqlens_k  : int32[nseq + 1], device memory; its key rows
+ *   max_seqlen_q  : host int >= every sequence's query count (the schedule
+ *                   is sized from it; rows beyond it are not computed)
+ *
+ * Each sequence is the forward of its own rows, with the head mapping of
+ * gqa_attn_fwd: prompts batched into one launch, as the microLLM-rocm
+ * optimization log batches prompts of different lengths into one prefill
+ * (experiment 101), over token-major tensors (its experiments 201-204).
+ * Its Nq queries are its last Nq tokens -- the chunk of a longer prompt in
+ * the kaispace.site note "Chunked Prefill", the whole prompt when Nq = Nk --
+ * so with causal = 1 query i sees keys j <= Nk - Nq + i; a row that sees no
+ * key (Nk = 0, or i < Nq - Nk) is all zero.  The offsets must be
+ * non-decreasing and within the tensors; they are read on the device and
+ * not checked.  Work units are (sequence, K/V head, query-position block)
+ * taken heaviest first from the persistent schedule's queues; units past a
+ * sequence's queries cost one take.
+ *
+ * Requirements (else nothing is launched): pointers non-NULL
+ * (GQA_ERR_NULL_POINTER); nseq, max_seqlen_q, Hq, Hkv, d >= 1,
+ * max_seqlen_q <= 2^30, 64 key rows (64 * Hkv * d elements) under 2 GiB, at most
+ * 2^31 - 1 work units (GQA_ERR_BAD_SHAPE); Hq a multiple of Hkv (GQA_ERR_HEAD_GROUPING); d in
+ * {32, 64, 128}, dtype known, scale finite, q/k/v/o 16-byte aligned and the
+ * offset arrays 4-byte aligned (GQA_ERR_UNSUPPORTED).  O must not overlap
+ * Q, K or V.  Same scale, dtype, stream and error behaviour as gqa_attn_fwd.
+ */
+int gqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                        int max_seqlen_q, int Hq, int Hkv, int d, int causal, float scale,
+                        int dtype, void* stream);
+
+/*
  * Bytes of device workspace gqa_attn_decode needs for these sizes (an upper
  * bound that does not depend on seqlens).  Returns 0 for invalid sizes.
  */

@@ -26,7 +26,7 @@ STATUS_NAMES = {
     0: "GQA_OK", 1: "GQA_ERR_NULL_POINTER", 2: "GQA_ERR_BAD_SHAPE", 3: "GQA_ERR_HEAD_GROUPING",
     4: "GQA_ERR_UNSUPPORTED", 5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_NO_DEVICE", 7: "GQA_ERR_HIP",
 }
-EXPORTED = ("gqa_attn_fwd", "gqa_attn_fwd_strided", "gqa_attn_decode",
+EXPORTED = ("gqa_attn_fwd", "gqa_attn_fwd_strided", "gqa_attn_fwd_varlen", "gqa_attn_decode",
             "gqa_attn_decode_noalloc", "gqa_attn_decode_append", "gqa_attn_decode_workspace_bytes", "gqa_attn_bwd",
             "gqa_attn_bwd_workspace_bytes", "gqa_attn_mixed", "gqa_status_string",
             "gqa_last_error_string")
@@ -51,6 +51,8 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_fwd_strided.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i64p, i64p, i, i, f,
                                          i, vp]
     lib.gqa_attn_fwd_strided.restype = i
+    lib.gqa_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.gqa_attn_fwd_varlen.restype = i
     lib.gqa_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.gqa_attn_decode_workspace_bytes.restype = sz
     lib.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -179,6 +181,50 @@ def attn_fwd_strided(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causa
                                       B, Hq, Hkv, Nq, Nk, d, qs, kvs, int(bool(causal)),
                                       int(q_offset), float(scale), _DTYPES[q.dtype],
                                       _stream_handle(dev))
+    _raise(st)
+    return out
+
+
+def attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int, *,
+                    causal: bool = False, scale: float | None = None,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """Packed variable-length forward via gqa_attn_fwd_varlen.
+
+    q [total_q, Hq, d], k and v [total_k, Hkv, d] (token-major, contiguous,
+    one dtype, one GPU); cu_seqlens_q / cu_seqlens_k int32 [nseq + 1] on the
+    same GPU (sequence s owns rows [cu[s], cu[s+1])); max_seqlen_q: a host
+    int >= every sequence's query count.  Each sequence's queries are its
+    last tokens; causal: query i sees keys j <= Nk - Nq + i.  scale defaults
+    to 1/sqrt(d)."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _check_tensor("q", q, 3, q.dtype, dev)
+    _check_tensor("k", k, 3, q.dtype, dev)
+    _check_tensor("v", v, 3, q.dtype, dev)
+    _check_tensor("cu_seqlens_q", cu_seqlens_q, 1, torch.int32, dev)
+    _check_tensor("cu_seqlens_k", cu_seqlens_k, 1, torch.int32, dev)
+    _, Hq, d = q.shape
+    _, Hkv, _ = k.shape
+    if k.shape[2] != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    nseq = cu_seqlens_q.shape[0] - 1
+    if nseq < 1 or cu_seqlens_k.shape[0] != nseq + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold nseq + 1 >= 2 offsets")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, 3, q.dtype, dev)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must have the shape of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(dev):
+        st = lib.gqa_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), nseq,
+                                     int(max_seqlen_q), Hq, Hkv, d, int(bool(causal)),
+                                     float(scale), _DTYPES[q.dtype], _stream_handle(dev))
     _raise(st)
     return out
 

@@ -1,4 +1,5 @@
-"""Build libgqa_attn.so in-tree with hipcc for gfx950.
+"""Build libgqa_attn.so (and the measurement microbenchmarks,
+libgqa_microbench.so) in-tree with hipcc for gfx950.
 
     python -m mqa_flashattention_amd.build          # compile
     python -m mqa_flashattention_amd.build --asm    # also keep the gfx950 assembly
@@ -19,10 +20,12 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = [os.path.join(CSRC, "gqa_attn.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("attn_tile.hpp", "prefill_kernel.hpp",
-                                           "decode_kernel.hpp", "mixed_kernel.hpp",
-                                           "backward_kernel.hpp")] + [
+                                           "decode_kernel.hpp", "decode_part.hpp",
+                                           "mixed_kernel.hpp", "backward_kernel.hpp")] + [
     os.path.join(INCLUDE, "gqa_attn.h")]
 LIBRARY = os.path.join(PKG, "libgqa_attn.so")
+MICROBENCH_SOURCE = os.path.join(CSRC, "microbench.hip")
+MICROBENCH = os.path.join(PKG, "libgqa_microbench.so")
 ARCH = "gfx950"
 
 
@@ -43,16 +46,22 @@ def compile_flags() -> list[str]:
             "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def build(verbose: bool = False, keep_asm: bool = False) -> str:
-    """Compile the HIP library; returns its path.  Always recompiles."""
-    tmp = LIBRARY + ".tmp"
-    cmd = [hipcc(), *compile_flags(), *SOURCES, "-o", tmp]
+def _compile(sources, output, verbose, keep_asm=False):
+    tmp = output + ".tmp"
+    cmd = [hipcc(), *compile_flags(), *sources, "-o", tmp]
     if keep_asm:
         cmd += ["-save-temps=obj"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, cwd=CSRC)
-    os.replace(tmp, LIBRARY)
+    os.replace(tmp, output)
+
+
+def build(verbose: bool = False, keep_asm: bool = False) -> str:
+    """Compile the HIP library and the microbenchmark library; returns the
+    library's path.  Always recompiles."""
+    _compile(SOURCES, LIBRARY, verbose, keep_asm)
+    _compile([MICROBENCH_SOURCE], MICROBENCH, verbose)
     return LIBRARY
 
 

@@ -20,6 +20,7 @@
 
 #include "backward_kernel.hpp"
 #include "decode_kernel.hpp"
+#include "decode_part.hpp"
 #include "gqa_attn.h"
 #include "mixed_kernel.hpp"
 #include "prefill_kernel.hpp"
@@ -203,8 +204,11 @@ void decompose(gqa::PrefillArgs& a, int M) {
   a.Gu = a.g < M ? a.g : M;
   a.R = M / a.Gu;
   a.HB = (a.g + a.Gu - 1) / a.Gu;
-  a.NQB = (a.Nq + a.R - 1) / a.R;
-  a.T = a.B * a.Hkv * a.HB * a.NQB;
+  a.NQB = a.Nq > 0 ? (a.Nq - 1) / a.R + 1 : 0;
+  // callers reject sizes past INT_MAX units; the clamp only keeps this
+  // product defined before they look
+  const long long T = (long long)a.B * a.Hkv * a.HB * a.NQB;
+  a.T = (int)std::min<long long>(T, kIntMax);
 }
 
 // Key tiles of the units of position block qb (host copy of the kernels'
@@ -402,6 +406,109 @@ int scratch_address(int dev, void** out) {
   return GQA_OK;
 }
 
+// ------------------------------------------------------------------ packed varlen
+
+// The persistent schedule over (sequence, K/V head, head block, position
+// block < ceil(max_seqlen_q / R)) units; units past a sequence's query rows
+// return at once.
+template <typename T, class C, bool CAUSAL>
+int launch_varlen(gqa::PrefillArgs& a, int dev_id, const DeviceInfo& dev, hipStream_t stream) {
+  const void* kern = reinterpret_cast<const void*>(&gqa::prefill_varlen_kernel<T, C, CAUSAL>);
+  const long long slots = (long long)dev.cus * occupancy(kern, C::NT);
+  const long long grid = std::min<long long>(a.T, slots);
+  StreamState ss;
+  int st = stream_state(dev_id, stream, 0, &ss);
+  if (st != GQA_OK) return st;
+  a.ctr = ss.ctr;
+  a.zero = 0;
+  a.ws = nullptr;
+  (void)hipGetLastError();  // a stale error belongs to an earlier call
+  hipLaunchKernelGGL((gqa::prefill_varlen_kernel<T, C, CAUSAL>), dim3((unsigned)grid),
+                     dim3(C::NT), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "prefill varlen kernel launch");
+  return GQA_OK;
+}
+
+template <typename T, template <int> class Cfg>
+int dispatch_varlen(gqa::PrefillArgs& a, int d, int causal, int dev_id, const DeviceInfo& dev,
+                    hipStream_t s) {
+  switch (d) {
+    case 32:
+      return causal ? launch_varlen<T, Cfg<32>, true>(a, dev_id, dev, s)
+                    : launch_varlen<T, Cfg<32>, false>(a, dev_id, dev, s);
+    case 64:
+      return causal ? launch_varlen<T, Cfg<64>, true>(a, dev_id, dev, s)
+                    : launch_varlen<T, Cfg<64>, false>(a, dev_id, dev, s);
+    default:
+      return causal ? launch_varlen<T, Cfg<128>, true>(a, dev_id, dev, s)
+                    : launch_varlen<T, Cfg<128>, false>(a, dev_id, dev, s);
+  }
+}
+
+int varlen_entry(const void* q, const void* k, const void* v, void* o, const int32_t* cu_q,
+                 const int32_t* cu_k, int nseq, int max_seqlen_q, int Hq, int Hkv, int d,
+                 int causal, float scale, int dtype, void* stream) {
+  // ---- validation: host only, before any HIP call
+  if (!q || !k || !v || !o || !cu_q || !cu_k)
+    return fail(GQA_ERR_NULL_POINTER, "q, k, v, o, cu_seqlens_q and cu_seqlens_k must be non-NULL");
+  if (nseq < 1 || max_seqlen_q < 1 || Hq < 1 || Hkv < 1 || d < 1)
+    return fail(GQA_ERR_BAD_SHAPE,
+                "sizes must be >= 1 (nseq=%d max_seqlen_q=%d Hq=%d Hkv=%d d=%d)", nseq,
+                max_seqlen_q, Hq, Hkv, d);
+  if (max_seqlen_q > (1 << 30))
+    return fail(GQA_ERR_BAD_SHAPE, "max_seqlen_q=%d above 2^30", max_seqlen_q);
+  if (Hq % Hkv != 0)
+    return fail(GQA_ERR_HEAD_GROUPING, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != GQA_DTYPE_F32 && dtype != GQA_DTYPE_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (!head_dim_ok(d)) return fail(GQA_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+  if (!std::isfinite(scale)) return fail(GQA_ERR_UNSUPPORTED, "scale must be finite");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(GQA_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(cu_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_k) & 3u))
+    return fail(GQA_ERR_UNSUPPORTED, "offset arrays must be 4-byte aligned");
+  const int esz = dtype == GQA_DTYPE_BF16 ? 2 : 4;
+  if ((long long)Hkv * d * esz * 64 > kIntMax)
+    return fail(GQA_ERR_BAD_SHAPE, "too many K/V heads for 32-bit tile offsets");
+  gqa::PrefillArgs a = gqa::PrefillArgs{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.B = nseq;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = max_seqlen_q;
+  a.Nk = 0;  // per sequence, on the device
+  // token-major [token, head, d]: the batch index of a unit is its sequence,
+  // whose rows the kernel reaches through the offset arrays
+  a.q_sb = 0;
+  a.q_sh = d;
+  a.q_sn = (long long)Hq * d;
+  a.kv_sb = 0;
+  a.kv_sh = d;
+  a.kv_rowb = Hkv * d * esz;
+  a.g = Hq / Hkv;
+  decompose(a, 32 * kPrefillWaves);
+  const long long T = (long long)nseq * Hkv * a.HB * (((long long)max_seqlen_q + a.R - 1) / a.R);
+  if (T > kIntMax) return fail(GQA_ERR_BAD_SHAPE, "too many work units (%lld)", T);
+  a.q_offset = 0;
+  a.c = softmax_coef(scale);
+  a.thr = gqa::kRescaleSlack / a.c;
+  a.negate_q = scale < 0.f ? 1 : 0;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+
+  int dev = 0;
+  DeviceInfo info;
+  int st = current_device(&dev, &info);
+  if (st != GQA_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == GQA_DTYPE_BF16) return dispatch_varlen<uint16_t, CfgBf16S>(a, d, causal, dev, info, hs);
+  return dispatch_varlen<float, CfgF32S>(a, d, causal, dev, info, hs);
+}
+
 // ------------------------------------------------------------------ decode
 
 constexpr int kMinSplit = 32;
@@ -447,6 +554,74 @@ int dispatch_decode(gqa::DecodeArgs& a, int d, hipStream_t s) {
     case 32: return launch_decode<T, Cfg<32>, APPEND>(a, s);
     case 64: return launch_decode<T, Cfg<64>, APPEND>(a, s);
     default: return launch_decode<T, Cfg<128>, APPEND>(a, s);
+  }
+}
+
+// bf16 decode (decode_part.hpp): one workgroup of W waves per (part, K/V
+// head, column group, row), its waves on interleaved 32-token tiles of the
+// part, merged through LDS into one record per query head; the merge kernel
+// then combines a row's records.  Waves hold 16 query columns per block:
+// one block for groups of up to 16 heads, two above (in ceil(g / (16 NCB))
+// column groups).  The part length aims for about kPartWavesPerCu waves per
+// CU when every row is full -- several rounds of workgroups, which the
+// dispatcher balances over rows of different lengths -- and at most
+// kPartMaxParts parts per row.
+#ifndef GQA_PART_W
+#define GQA_PART_W 4
+#endif
+#ifndef GQA_PART_WAVES_PER_CU
+#define GQA_PART_WAVES_PER_CU 8
+#endif
+constexpr int kPartMaxParts = 64;     // records per row the merge kernel reads at once
+constexpr int kPartWavesPerCu = GQA_PART_WAVES_PER_CU;
+
+template <int D, int NCB>
+using PartCfgOf = gqa::PartCfg<D, NCB, NCB == 1 ? GQA_PART_W : (GQA_PART_W > 1 ? GQA_PART_W / 2 : 1)>;
+
+// Column groups and part length of a bf16 decode (sets a.NCB, a.S_TOK, a.NS).
+template <class P>
+void part_plan(gqa::DecodeArgs& a, int cus) {
+  const long long ncg = (a.g + P::COLS - 1) / P::COLS;
+  const long long tiles_row = (a.Smax + 31) / 32;
+  const long long tiles = (long long)a.B * a.Hkv * ncg * tiles_row;
+  const long long target = (long long)kPartWavesPerCu * cus;
+  long long tw = (tiles + target - 1) / target;
+  const long long tw_min = (tiles_row + (long long)kPartMaxParts * P::W - 1) /
+                           ((long long)kPartMaxParts * P::W);
+  tw = std::max(std::max(tw, tw_min), 1LL);
+  a.NCB = (int)ncg;
+  a.S_TOK = (int)std::min<long long>(tw * P::W * 32, kIntMax);
+  a.NS = (int)((a.Smax + (long long)a.S_TOK - 1) / a.S_TOK);
+}
+
+template <int D, int NCB, bool APPEND>
+int launch_decode_part(gqa::DecodeArgs& a, int cus, hipStream_t stream) {
+  using P = PartCfgOf<D, NCB>;
+  part_plan<P>(a, cus);
+  dim3 grid((unsigned)a.NS, (unsigned)(a.Hkv * a.NCB), (unsigned)a.B);
+  hipLaunchKernelGGL((gqa::decode_part_kernel<P, APPEND>), grid, dim3(P::NT), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "decode part kernel launch");
+  hipLaunchKernelGGL((gqa::decode_merge_kernel<D, APPEND>), dim3((unsigned)a.Hq, (unsigned)a.B),
+                     dim3(256), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "decode merge kernel launch");
+  return GQA_OK;
+}
+
+template <bool APPEND>
+int dispatch_decode_part(gqa::DecodeArgs& a, int d, int cus, hipStream_t s) {
+  const bool two = a.g > 16;
+  switch (d) {
+    case 32:
+      return two ? launch_decode_part<32, 2, APPEND>(a, cus, s)
+                 : launch_decode_part<32, 1, APPEND>(a, cus, s);
+    case 64:
+      return two ? launch_decode_part<64, 2, APPEND>(a, cus, s)
+                 : launch_decode_part<64, 1, APPEND>(a, cus, s);
+    default:
+      return two ? launch_decode_part<128, 2, APPEND>(a, cus, s)
+                 : launch_decode_part<128, 1, APPEND>(a, cus, s);
   }
 }
 
@@ -634,14 +809,13 @@ int decode_entry(const void* q, const void* kcache, const void* vcache, const in
     if (st != GQA_OK) return st;
     a.ws = reinterpret_cast<float*>(p);
   }
-  decode_splits(a, info.cus);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (append) {
-    if (dtype == GQA_DTYPE_BF16) return dispatch_decode<uint16_t, DecCfgBf16, true>(a, d, hs);
-    return dispatch_decode<float, DecCfgF32, true>(a, d, hs);
-  }
-  if (dtype == GQA_DTYPE_BF16) return dispatch_decode<uint16_t, DecCfgBf16, false>(a, d, hs);
+  if (dtype == GQA_DTYPE_BF16)
+    return append ? dispatch_decode_part<true>(a, d, info.cus, hs)
+                  : dispatch_decode_part<false>(a, d, info.cus, hs);
+  decode_splits(a, info.cus);
+  if (append) return dispatch_decode<float, DecCfgF32, true>(a, d, hs);
   return dispatch_decode<float, DecCfgF32, false>(a, d, hs);
 }
 
@@ -679,8 +853,17 @@ int launch_mixed(gqa::MixedArgs& m, int dev_id, const DeviceInfo& dev, hipStream
   }
   if (!quad) kern = reinterpret_cast<const void*>(&gqa::mixed_kernel<T, C, CD>);
   const long long slots = (long long)dev.cus * occupancy(kern, threads);
+  constexpr bool REG = !std::is_same<T, float>::value;
+  if constexpr (REG)  // bf16: each group of W waves takes a decode part
+    dw = (threads / 64) / (m.d.g > 16 ? PartCfgOf<C::D, 2>::W : PartCfgOf<C::D, 1>::W);
   if (a.d.B > 0) {
-    decode_splits(a.d, dev.cus, a.p.T >= slots ? 8 : 4);
+    if constexpr (REG) {
+      // bf16: the parts of gqa_attn_decode (the same records, and outputs)
+      if (a.d.g > 16) part_plan<PartCfgOf<C::D, 2>>(a.d, dev.cus);
+      else part_plan<PartCfgOf<C::D, 1>>(a.d, dev.cus);
+    } else {
+      decode_splits(a.d, dev.cus, a.p.T >= slots ? 8 : 4);
+    }
     const long long nd = (long long)a.d.NS * a.d.Hkv * a.d.NCB * a.d.B;
     if (nd > kIntMax / 2) return fail(GQA_ERR_BAD_SHAPE, "too many decode splits (%lld)", nd);
     a.nd = (int)nd;
@@ -704,8 +887,12 @@ int launch_mixed(gqa::MixedArgs& m, int dev_id, const DeviceInfo& dev, hipStream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "mixed kernel launch");
   if (a.nd > 0) {
-    hipLaunchKernelGGL((gqa::decode_combine_kernel<T, C::D, false>),
-                       dim3((unsigned)a.d.Hq, (unsigned)a.d.B), dim3(256), 0, stream, a.d);
+    if constexpr (REG)
+      hipLaunchKernelGGL((gqa::decode_merge_kernel<C::D, false>),
+                         dim3((unsigned)a.d.Hq, (unsigned)a.d.B), dim3(256), 0, stream, a.d);
+    else
+      hipLaunchKernelGGL((gqa::decode_combine_kernel<T, C::D, false>),
+                         dim3((unsigned)a.d.Hq, (unsigned)a.d.B), dim3(256), 0, stream, a.d);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "decode combine kernel launch");
   }
@@ -986,6 +1173,15 @@ int gqa_attn_fwd_strided(const void* q, const void* k, const void* v, void* o, i
                 (long long)kv_strides[2]);
   return fwd_entry(q, k, v, o, B, Hq, Hkv, Nq, Nk, d, q_strides, kv_strides, causal, q_offset,
                    scale, dtype, stream);
+}
+
+int gqa_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                        int max_seqlen_q, int Hq, int Hkv, int d, int causal, float scale,
+                        int dtype, void* stream) {
+  g_last_error.clear();
+  return varlen_entry(q, k, v, o, cu_seqlens_q, cu_seqlens_k, nseq, max_seqlen_q, Hq, Hkv, d,
+                      causal, scale, dtype, stream);
 }
 
 size_t gqa_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Smax, int d) {

@@ -29,7 +29,10 @@
 //    all of a unit's keys would be the critical path.
 #pragma once
 
+#include <type_traits>
+
 #include "decode_kernel.hpp"
+#include "decode_part.hpp"
 #include "prefill_kernel.hpp"
 
 namespace gqa {
@@ -39,6 +42,19 @@ namespace gqa {
 constexpr int kMixedDecodeCounter = kNumQueues + 1;
 // LDS a mixed workgroup may use, so that two still fit on a CU.
 constexpr int kMixedLdsBytes = 80 * 1024;
+// Waves per bf16 decode part (one 16-column block; two blocks take half as
+// many): the part kernel's, so that the records match gqa_attn_decode's.
+#ifndef GQA_PART_W
+#define GQA_PART_W 4
+#endif
+constexpr int kMixedPartW = GQA_PART_W;
+// LDS of NWAVES waves' worth of bf16 decode parts.
+template <int D, int NWAVES>
+constexpr int mixed_part_lds_bytes() {
+  constexpr int one = PartCfg<D, 1, kMixedPartW>::LDS_BYTES * (NWAVES / kMixedPartW);
+  constexpr int two = PartCfg<D, 2, kMixedPartW / 2>::LDS_BYTES * (NWAVES / (kMixedPartW / 2));
+  return one > two ? one : two;
+}
 
 struct MixedArgs {
   PrefillArgs p;  // the chunk (p.B == 0: none); p.ctr holds the counters
@@ -56,32 +72,68 @@ constexpr int mixed_decode_waves() {
 template <class C, class CD>
 constexpr int mixed_lds_bytes() {
   constexpr int pre = 2 * C::STAGE_BYTES;
-  constexpr int dec = mixed_decode_waves<C, CD>() * CD::STAGE_BYTES;
+  constexpr int dec = C::F32 ? mixed_decode_waves<C, CD>() * CD::STAGE_BYTES
+                             : mixed_part_lds_bytes<C::D, C::NW>();
   return pre > dec ? pre : dec;
 }
 
-// Decode splits, after the prefill units: take i covers splits
-// DW*i .. DW*i + DW - 1 (wave w < DW runs the w-th in its own LDS area at
-// smem + w * CD::STAGE_BYTES); split x = (s, y, b) with s fastest, as the
-// decode grid orders them.  All threads of the workgroup call it.
-template <typename T, class CD, int DW>
-__device__ __forceinline__ void mixed_decode_phase(const MixedArgs& m, char* smem, int* s_take) {
+// Decode work, after the prefill units.  bf16: the parts of
+// gqa_attn_decode (decode_part.hpp), each run by a group of P::W waves in an
+// LDS area of its own -- the same records, so the same outputs, as a
+// gqa_attn_decode call; take i covers parts DE*i .. DE*i + DE - 1 (DE =
+// groups per workgroup), part x = (s, y, b) with s fastest, as the decode
+// grid orders them.  fp32: DW waves (the LDS areas that fit) take one split
+// each, staged through LDS (decode_split).  All threads of the workgroup
+// call it.
+template <class P>
+__device__ __forceinline__ void mixed_part_takes(const MixedArgs& m, char* smem, int* s_take,
+                                                 int nwaves) {
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
-  const int lane = tid & 63;
+  const int de = nwaves / P::W;
+  const int grp = (tid >> 6) / P::W;
   const int ny = m.d.Hkv * m.d.NCB;
   for (;;) {
-    __syncthreads();  // shared word read, LDS free of the previous item
+    __syncthreads();  // shared word read, LDS free of the previous part
     if (tid == 0) *s_take = atomicAdd(m.p.ctr + kMixedDecodeCounter * kCounterStride, 1);
     __syncthreads();
     const int take = __builtin_amdgcn_readfirstlane(*s_take);
-    if ((long long)take * DW >= m.nd) break;
-    const int x = take * DW + w;
-    if (w < DW && x < m.nd) {
-      const int s_idx = x % m.d.NS;
-      const int rest = x / m.d.NS;
-      decode_split<T, CD, false, true>(m.d, smem + w * CD::STAGE_BYTES, s_idx, rest % ny,
-                                       rest / ny, lane);
+    if ((long long)take * de >= m.nd) break;
+    const int x = take * de + grp;
+    const bool valid = grp < de && x < m.nd;
+    const int xs = valid ? x : 0;
+    const int s_idx = xs % m.d.NS;
+    const int rest = xs / m.d.NS;
+    // every group reaches the part's barrier, with work or without
+    part_group<P, false>(m.d, smem + grp * P::LDS_BYTES, s_idx, rest % ny, rest / ny,
+                         tid - grp * P::W * 64, valid);
+  }
+}
+
+template <typename T, class CD, int DW, int NWAVES>
+__device__ __forceinline__ void mixed_decode_phase(const MixedArgs& m, char* smem, int* s_take) {
+  if constexpr (!std::is_same<T, float>::value) {
+    if (m.d.g > 16)
+      mixed_part_takes<PartCfg<CD::D, 2, kMixedPartW / 2>>(m, smem, s_take, NWAVES);
+    else
+      mixed_part_takes<PartCfg<CD::D, 1, kMixedPartW>>(m, smem, s_take, NWAVES);
+  } else {
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int ny = m.d.Hkv * m.d.NCB;
+    for (;;) {
+      __syncthreads();  // shared word read, LDS free of the previous item
+      if (tid == 0) *s_take = atomicAdd(m.p.ctr + kMixedDecodeCounter * kCounterStride, 1);
+      __syncthreads();
+      const int take = __builtin_amdgcn_readfirstlane(*s_take);
+      if ((long long)take * DW >= m.nd) break;
+      const int x = take * DW + w;
+      if (w < DW && x < m.nd) {
+        const int s_idx = x % m.d.NS;
+        const int rest = x / m.d.NS;
+        decode_split<T, CD, false, true>(m.d, smem + w * CD::STAGE_BYTES, s_idx, rest % ny,
+                                         rest / ny, lane);
+      }
     }
   }
 }
@@ -126,7 +178,7 @@ mixed_kernel(MixedArgs m) {
     persistent_unit<T, C, true>(a, smem, t, q, w, j);
   }
 
-  mixed_decode_phase<T, CD, DW>(m, smem, &s_unit);
+  mixed_decode_phase<T, CD, DW, C::NW>(m, smem, &s_unit);
   leave_persistent(a, kMixedDecodeCounter);
 }
 
@@ -146,8 +198,8 @@ template <typename T, class CQ, class CD>
 __global__ void __launch_bounds__(4 * CQ::NT) __attribute__((amdgpu_waves_per_eu(2)))
 mixed_quad_kernel(MixedArgs m) {
   constexpr int DW = mixed_quad_decode_waves<CQ, CD>();
-  constexpr int LDS = quad_lds_bytes<CQ>() > DW * CD::STAGE_BYTES ? quad_lds_bytes<CQ>()
-                                                                  : DW * CD::STAGE_BYTES;
+  constexpr int DEC = CQ::F32 ? DW * CD::STAGE_BYTES : mixed_part_lds_bytes<CQ::D, 4 * CQ::NW>();
+  constexpr int LDS = quad_lds_bytes<CQ>() > DEC ? quad_lds_bytes<CQ>() : DEC;
   __shared__ __attribute__((aligned(16))) char smem[LDS];
   static_assert(CQ::D == CD::D, "one head dim for both parts");
   __shared__ int s_unit;
@@ -181,7 +233,7 @@ mixed_quad_kernel(MixedArgs m) {
     const int kvg = q + kNumQueues * (rest / a.HB);
     quad_unit<T, CQ, true>(a, smem, (kvg * a.HB + hb) * a.NQB + qb);
   }
-  mixed_decode_phase<T, CD, DW>(m, smem, &s_unit);
+  mixed_decode_phase<T, CD, DW, 4 * CQ::NW>(m, smem, &s_unit);
   leave_persistent(a, kMixedDecodeCounter);
 }
 

@@ -76,6 +76,10 @@ struct PrefillArgs {
   int zero;  // always 0 (the probe's atomic add, kept a read-modify-write)
   int* ctr;  // counter i at ctr[i * kCounterStride]: next item of queue i < kNumQueues,
              // workgroups finished for i = kNumQueues
+  // packed varlen batches: sequence b owns query rows [cu_q[b], cu_q[b+1])
+  // and key rows [cu_k[b], cu_k[b+1]) of token-major tensors (NULL otherwise)
+  const int32_t* cu_q;
+  const int32_t* cu_k;
 };
 
 constexpr int kNumQueues = 8;  // XCDs of an MI355X
@@ -340,7 +344,10 @@ __device__ __forceinline__ void finish_rows(const PrefillArgs& a, char* stg, flo
   const int j = lane & 31;
   const int h2 = lane >> 5;
   constexpr int RB = C::D * C::ESZ + 16;  // staging row stride, bytes
-  const float inv = 1.0f / halves_sum(lrun);
+  // a row that saw no key (possible only in a packed varlen batch whose
+  // sequence has more queries than keys) has l = 0 and is zero
+  const float lsum = halves_sum(lrun);
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   char* row = stg + j * RB;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
@@ -424,14 +431,14 @@ __device__ __forceinline__ void take_unit(const PrefillArgs& a, int home, int nk
 // Runs item t of queue q of the persistent schedule: maps it to its unit
 // (b, hkv, hb, qb), walks the unit's key tiles and stores its rows.  All
 // threads of the workgroup call it together.
-template <typename T, class C, bool CAUSAL>
-__device__ __forceinline__ void persistent_unit(const PrefillArgs& a, char* smem, int t, int q,
-                                                int w, int j) {
+// Item t of queue q of the persistent schedule -> unit (b, hkv, hb, qb).
+__device__ __forceinline__ void persistent_map(const PrefillArgs& a, bool causal, int t, int q,
+                                               int& b, int& hkv, int& hb, int& qb) {
   const int nkv = a.B * a.Hkv;
   const int per_group = a.HB * a.NQB;
   const int groups = queue_units(q, nkv, per_group) / per_group;
-  int qb, gi, hb;
-  if (CAUSAL) {
+  int gi;
+  if (causal) {
     const int per_qb = groups * a.HB;
     qb = a.NQB - 1 - t / per_qb;
     const int rest = t % per_qb;
@@ -444,8 +451,15 @@ __device__ __forceinline__ void persistent_unit(const PrefillArgs& a, char* smem
     qb = rest % a.NQB;
   }
   const int kvg = q + kNumQueues * gi;
-  const int hkv = kvg % a.Hkv;
-  const int b = kvg / a.Hkv;
+  hkv = kvg % a.Hkv;
+  b = kvg / a.Hkv;
+}
+
+template <typename T, class C, bool CAUSAL>
+__device__ __forceinline__ void persistent_unit(const PrefillArgs& a, char* smem, int t, int q,
+                                                int w, int j) {
+  int b, hkv, hb, qb;
+  persistent_map(a, CAUSAL, t, q, b, hkv, hb, qb);
 
   const int ntiles = unit_tiles<C, CAUSAL>(a, qb);
   const int rot = (int)((7u * (unsigned)t + 3u * (unsigned)q) % (unsigned)ntiles);
@@ -505,6 +519,81 @@ prefill_kernel(PrefillArgs a) {
     const int q = __builtin_amdgcn_readfirstlane(s_queue);
     if (t < 0) break;
     persistent_unit<T, C, CAUSAL>(a, smem, t, q, w, j);
+  }
+  leave_persistent(a, kNumQueues);
+}
+
+// Packed varlen batches (sequences of different lengths back to back in
+// token-major tensors): the persistent schedule over units (sequence b,
+// hkv, hb, qb) with qb below ceil(max_seqlen_q / R); a unit past its
+// sequence's query rows does nothing.  Each unit runs on its own sequence:
+// bases moved to the sequence's first query and key row, its own Nq and Nk,
+// and, causal, its queries as its last Nq tokens (q_offset = Nk - Nq, which
+// may be negative: rows that see no key come out zero).
+template <typename T, class C, bool CAUSAL>
+__device__ __forceinline__ void varlen_unit(const PrefillArgs& a, char* smem, int t, int q,
+                                            int w, int j) {
+  int b, hkv, hb, qb;
+  persistent_map(a, CAUSAL, t, q, b, hkv, hb, qb);
+  const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
+  const int k0 = a.cu_k[b], k1 = a.cu_k[b + 1];
+  const int nq = __builtin_amdgcn_readfirstlane(q1 - q0);
+  const int nk = __builtin_amdgcn_readfirstlane(k1 - k0 > 0 ? k1 - k0 : 0);
+  if (qb * a.R >= nq) return;  // past this sequence's queries (workgroup-uniform)
+  PrefillArgs u = a;
+  u.Nq = nq;
+  u.Nk = nk;
+  u.NQB = (nq + a.R - 1) / a.R;
+  u.q_offset = CAUSAL ? nk - nq : 0;
+  u.q = reinterpret_cast<const T*>(a.q) + (size_t)q0 * a.q_sn;
+  u.o = reinterpret_cast<T*>(a.o) + (size_t)q0 * a.q_sn;
+  const size_t kv_row = (size_t)a.kv_rowb / C::ESZ;  // elements from one key row to the next
+  u.k = reinterpret_cast<const T*>(a.k) + (size_t)k0 * kv_row;
+  u.v = reinterpret_cast<const T*>(a.v) + (size_t)k0 * kv_row;
+
+  const int ntiles = nk > 0 ? unit_tiles<C, CAUSAL>(u, qb) : 0;
+  const Column col = lane_column<C>(u, 0, hkv, hb, qb, w, j);
+  float mrun = kNegInf, lrun = 0.f;
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  if (ntiles > 0) {
+    const int rot = (int)((7u * (unsigned)t + 3u * (unsigned)q) % (unsigned)ntiles);
+    run_segment<T, C, CAUSAL>(u, smem, 0, hkv, qb, 0, ntiles, rot, col, mrun, lrun, acc);
+  }
+  finish_rows<T, C>(u, smem + w * stage_out_bytes<C>(), lrun, acc, 0, hkv, hb, qb, w);
+}
+
+template <typename T, class C, bool CAUSAL>
+__global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+prefill_varlen_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+  static_assert(C::NW * stage_out_bytes<C>() <= 2 * C::STAGE_BYTES, "output staging too large");
+  __shared__ int s_unit;
+  __shared__ int s_queue;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int j = lane & 31;
+  const int home = blockIdx.x % kNumQueues;
+  const int nkv = a.B * a.Hkv;
+  const int per_group = a.HB * a.NQB;
+  bool home_empty = false;  // wave 0: the home queue has run dry
+  for (;;) {
+    __syncthreads();  // every wave has read the previous item's shared words
+    if (w == 0) {
+      int t, q;
+      take_unit(a, home, nkv, per_group, home_empty, lane, t, q);
+      if (lane == 0) {
+        s_unit = t;
+        s_queue = q;
+      }
+    }
+    __syncthreads();
+    const int t = __builtin_amdgcn_readfirstlane(s_unit);
+    const int q = __builtin_amdgcn_readfirstlane(s_queue);
+    if (t < 0) break;
+    varlen_unit<T, C, CAUSAL>(a, smem, t, q, w, j);
   }
   leave_persistent(a, kNumQueues);
 }

@@ -14,6 +14,9 @@ Recipe (one torch CPU generator per draw, ``manual_seed(seed)``):
            uniform integers) from the same generator.
   mixed:   the chunk as a forward draw with ``seed``, the decode rows as a
            decode draw with ``seed + 1``.
+  varlen:  per-sequence lengths (when drawn) ``torch.randint(lo, hi + 1,
+           (nseq,))`` from a generator seeded ``seed + 31``; then Q, K, V as
+           the forward draw, token-major [total, H, d].
 
 The shapes are the workloads the pages turn on:
   * LLaMA-3-8B attention shape (seq 2K, Hq 32, Hkv 8, d 128) from the
@@ -164,6 +167,46 @@ def append_inputs(s: DecodeShape, seed: int = 0):
     kn = torch.randn((s.B, s.Hkv, s.d), generator=g, dtype=torch.float32).to(s.dtype)
     vn = torch.randn((s.B, s.Hkv, s.d), generator=g, dtype=torch.float32).to(s.dtype)
     return q, kn, vn, kc, vc, (lens - 1).to(torch.int32)
+
+
+@dataclass(frozen=True)
+class VarlenShape:
+    """A packed batch of nseq prompts, each a whole prompt (queries = keys),
+    lengths uniform in [len_lo, len_hi]."""
+    nseq: int
+    Hq: int
+    Hkv: int
+    d: int
+    len_lo: int
+    len_hi: int
+    causal: bool = True
+    dtype: torch.dtype = torch.bfloat16
+
+
+# Prompts of mixed lengths batched into one prefill (microLLM-rocm
+# optimization log, experiment 101, batches prompts of different lengths; the
+# LLaMA-3-8B attention shape of the BootstrapAI log's "Kernel 9").
+VARLEN_PREFILL = VarlenShape(nseq=8, Hq=32, Hkv=8, d=128, len_lo=128, len_hi=2048)
+
+
+def varlen_lengths(s: VarlenShape, seed: int = 0) -> list[int]:
+    g = torch.Generator(device="cpu").manual_seed(seed + 31)
+    return [int(x) for x in torch.randint(s.len_lo, s.len_hi + 1, (s.nseq,), generator=g)]
+
+
+def varlen_inputs(lens_q, lens_k, Hq: int, Hkv: int, d: int, dtype=torch.bfloat16,
+                  seed: int = 0):
+    """CPU tensors (q [sum lens_q, Hq, d], k and v [sum lens_k, Hkv, d],
+    cu_seqlens_q, cu_seqlens_k [nseq + 1] int32) of a packed batch."""
+    cq = torch.zeros(len(lens_q) + 1, dtype=torch.int32)
+    ck = torch.zeros(len(lens_k) + 1, dtype=torch.int32)
+    cq[1:] = torch.tensor(lens_q, dtype=torch.int64).cumsum(0).to(torch.int32)
+    ck[1:] = torch.tensor(lens_k, dtype=torch.int64).cumsum(0).to(torch.int32)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((int(cq[-1]), Hq, d), generator=g, dtype=torch.float32)
+    k = torch.randn((int(ck[-1]), Hkv, d), generator=g, dtype=torch.float32)
+    v = torch.randn((int(ck[-1]), Hkv, d), generator=g, dtype=torch.float32)
+    return q.to(dtype), k.to(dtype), v.to(dtype), cq, ck
 
 
 def random_tensor(shape, seed: int, dtype=torch.float32, scale: float = 1.0):

@@ -165,6 +165,34 @@ def test_fwd_strided_null_stride_arrays():
                                             0, 0, ctypes.c_float(0.1), BF16, None) == NULLP
 
 
+def var(q=P[0], k=P[1], v=P[2], o=P[3], cq=P[4], ck=P[5], nseq=3, max_q=100, Hq=8, Hkv=2, d=64,
+        causal=1, scale=0.125, dtype=BF16, stream=None):
+    return binding.lib.gqa_attn_fwd_varlen(q, k, v, o, cq, ck, nseq, max_q, Hq, Hkv, d, causal,
+                                           ctypes.c_float(scale), dtype, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(o=None), NULLP), (dict(cq=None), NULLP), (dict(ck=None), NULLP),
+    (dict(nseq=0), SHAPE), (dict(max_q=0), SHAPE), (dict(max_q=(1 << 30) + 1), SHAPE),
+    (dict(Hq=0), SHAPE), (dict(d=0), SHAPE),
+    (dict(Hkv=2 ** 17, Hq=2 ** 17, d=128), SHAPE),       # 64 key rows past 2 GiB
+    (dict(nseq=2 ** 20, max_q=2 ** 20, Hq=64, Hkv=64), SHAPE),  # too many work units
+    (dict(Hq=6, Hkv=4), GROUP),
+    (dict(d=48), UNSUP), (dict(dtype=2), UNSUP), (dict(scale=float("inf")), UNSUP),
+    (dict(k=ctypes.c_void_p(0x20008)), UNSUP), (dict(cq=ctypes.c_void_p(0x50002)), UNSUP),
+])
+def test_fwd_varlen_rejects_invalid_arguments(kw, code):
+    assert var(**kw) == code
+    assert binding.lib.gqa_last_error_string()
+
+
+def test_varlen_binding_checks_tensors_before_the_library():
+    q = torch.zeros(10, 4, 32, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4, 10], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        binding.attn_fwd_varlen(q, q[:, :2], q[:, :2], cu, cu, 6)  # CPU tensors are refused
+
+
 def app(q=P[0], kn=P[6], vn=P[7], kc=P[1], vc=P[2], pos=P[4], o=P[3], B=8, Hq=12, Hkv=2,
         Smax=2048, d=128, scale=0.09, dtype=BF16, ws=P[5], ws_bytes=None, stream=None):
     if ws_bytes is None:
@@ -208,6 +236,7 @@ def test_valid_call_without_gpu_reports_no_device():
     assert dec_na() == NODEV
     assert app() == NODEV
     assert fwd_s() == NODEV
+    assert var() == NODEV
     # zero K/V batch stride (broadcast reads) is valid
     assert fwd_s(kvs=(0, 64, 128)) == NODEV
 

@@ -143,3 +143,21 @@ def test_append_equals_store_then_decode(dtype):
     ref = attn_decode(q.to(DEV), ks.to(DEV), vs.to(DEV), (pos + 1).to(DEV))
     torch.cuda.synchronize()
     assert torch.equal(out, ref.cpu())
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Smax,d", [(40, 12, 2, 1500, 128), (20, 40, 1, 2000, 64)],
+                         ids=["gqa6_d128", "g40_d64"])
+def test_append_large_batches(B, Hq, Hkv, Smax, d):
+    """Larger batches (several parts per row, several rounds of workgroups):
+    positions on part and tile boundaries, inactive rows first, in the middle
+    and last."""
+    g = torch.Generator().manual_seed(B + Smax)
+    pos = torch.randint(0, Smax, (B,), generator=g, dtype=torch.int32)
+    special = [-1, 0, 31, 32, 127, 128, 255, 256, Smax - 1, Smax, -5, 1000 * Smax]
+    pos[:len(special)] = torch.tensor(special, dtype=torch.int32)
+    pos[B // 2] = -1
+    pos[B - 1] = Smax + 3
+    q, kn, vn, kc, vc = _inputs(B, Hq, Hkv, Smax, d, torch.bfloat16, 150 + d)
+    out = _check(q, kn, vn, kc, vc, pos)
+    inactive = [i for i, p in enumerate(pos.tolist()) if not 0 <= p < Smax]
+    assert torch.all(out[inactive] == 0)

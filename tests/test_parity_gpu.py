@@ -194,6 +194,38 @@ def test_decode_multi_tile_splits(B, Hq, Hkv, Smax, d, dtype):
     assert _err(out, oracle.attn_decode(q, kc, vc, lens)) <= TOL[dtype]
 
 
+# Larger batches: several parts per row and several rounds of workgroups.
+# Empty rows (length 0 or negative) at the start, in the middle and at the
+# end; MHA, GQA and two column groups per K/V head; slots past each length
+# poisoned with NaN.
+LARGE_DECODE_SHAPES = [(40, 12, 2, 1500, 128), (20, 40, 1, 2000, 64), (33, 8, 8, 1200, 32),
+                 (128, 12, 2, 2048, 128)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Smax,d", LARGE_DECODE_SHAPES,
+                         ids=["gqa6_d128", "g40_d64", "mha_d32", "b128_d128"])
+def test_decode_large_batches(B, Hq, Hkv, Smax, d):
+    g = torch.Generator().manual_seed(B * Smax + d)
+    lens = torch.randint(1, Smax + 1, (B,), generator=g, dtype=torch.int32)
+    special = [0, 0, 1, 31, 32, 33, Smax, Smax + 5, -3]
+    lens[:len(special)] = torch.tensor(special, dtype=torch.int32)
+    lens[B // 2] = 0
+    lens[B - 1] = 0
+    q = random_tensor((B, Hq, d), 61, torch.bfloat16)
+    kc = random_tensor((B, Hkv, Smax, d), 62, torch.bfloat16)
+    vc = random_tensor((B, Hkv, Smax, d), 63, torch.bfloat16)
+    kp, vp = kc.clone(), vc.clone()
+    for b in range(B):
+        n = max(0, min(int(lens[b]), Smax))
+        kp[b, :, n:] = float("nan")
+        vp[b, :, n:] = float("nan")
+    out = attn_decode(q.to(DEV), kp.to(DEV), vp.to(DEV), lens.to(DEV))
+    torch.cuda.synchronize()
+    assert _err(out, oracle.attn_decode(q, kc, vc, lens)) <= 2e-2
+    empty = [b for b in range(B) if int(lens[b]) <= 0]
+    assert torch.all(out.cpu()[empty] == 0)
+
+
 def test_decode_across_sizes_and_streams():
     """Calls of growing and shrinking row counts on one stream, then the same
     inputs on two streams: every output equals the first call's, bit for bit."""
