@@ -29,9 +29,20 @@
  *  - Every argument is validated on the host before any HIP call; on any
  *    error nothing is launched and the output is not written.  There is no
  *    fallback path: an unsupported case returns GQA_ERR_UNSUPPORTED.
- *  - Library state: one small scheduler counter per (device, stream),
- *    allocated on first use and kept until the process ends.  Calls on one
- *    stream are ordered; calls on different streams use different counters.
+ *  - Library state: one small block of scheduler counters per (device,
+ *    stream), allocated and cleared on the first call that needs it, and,
+ *    for forwards with fewer units than resident workgroups, a per-stream
+ *    buffer of partial records grown when a call needs more (after draining
+ *    the stream); both are kept until the process ends.  Calls on one
+ *    stream are ordered; calls on different streams use different state.
+ *  - HIP graphs: a call may be captured once one eager call with the same
+ *    sizes has run on the capturing stream -- it then allocates nothing and
+ *    records no memset, and each persistent launch leaves its counters at
+ *    zero for the next replay.  A call that would have to set that state up
+ *    while its stream is capturing fails with GQA_ERR_UNSUPPORTED and
+ *    launches nothing.  Replays use the capturing stream's state, so a
+ *    replay must not overlap other calls on that stream's state (replay on
+ *    the capturing stream, or order the streams).
  *  - Return value: a gqa_status_t.  gqa_last_error_string() gives the
  *    detail of the most recent failure on the calling thread.
  */

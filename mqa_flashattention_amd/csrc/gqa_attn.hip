@@ -118,8 +118,12 @@ hipError_t zero_ints(int* p, long long n, hipStream_t stream) {
 //    mixed launch's decode-split counter, zeroed in stream order when
 //    allocated; each persistent launch leaves them at zero when it ends;
 //  * ws: partial records of the prefill units that the balanced schedule
-//    cuts, grown on demand (after
-//    the stream drains, so no queued launch still uses the old buffer).
+//    cuts, grown on demand (after the stream drains, so no queued launch
+//    still uses the old buffer).
+// Neither may be set up while the stream is being captured into a HIP graph
+// (an allocation and a drain are not graph work): such a call fails, and one
+// eager call with the same sizes on the stream beforehand makes the
+// captured one allocation-free.
 constexpr int kCounterInts = (gqa::kMixedDecodeCounter + 1) * gqa::kCounterStride;
 struct StreamState {
   int* ctr = nullptr;
@@ -132,6 +136,16 @@ int stream_state(int dev, hipStream_t stream, size_t ws_bytes, StreamState* out)
   std::lock_guard<std::mutex> lock(g_mu);
   StreamState& s = g_streams[std::make_pair(dev, reinterpret_cast<void*>(stream))];
   hipError_t e;
+  if (!s.ctr || ws_bytes > s.ws_bytes) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(GQA_ERR_UNSUPPORTED,
+                  "this call would set up the stream's scheduler state (%s) while the stream "
+                  "is captured; make one call with the same sizes on this stream before capture",
+                  !s.ctr ? "first call on the stream" : "larger split workspace");
+  }
   if (!s.ctr) {
     e = hipMalloc(&s.ctr, kCounterInts * sizeof(int));
     if (e != hipSuccess) {
@@ -316,10 +330,7 @@ int launch_prefill(gqa::PrefillArgs& a, int dev_id, const DeviceInfo& dev, hipSt
       p.nsl = p.B * p.Hkv * p.HB;
       pairs = (long long)p.nsl * ((p.NQB + 1) / 2);
     }
-    if (balanced && pairs >= dev.cus) {
-      StreamState ss;
-      int st = stream_state(dev_id, stream, 0, &ss);
-      if (st != GQA_OK) return st;
+    if (balanced && pairs >= dev.cus) {  // (no counters, no workspace)
       (void)hipGetLastError();  // a stale error belongs to an earlier call
       hipLaunchKernelGGL((gqa::prefill_pair_kernel<T, CP, CAUSAL>), dim3((unsigned)pairs),
                          dim3(2 * CP::NT), 0, stream, p);

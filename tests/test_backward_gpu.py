@@ -48,8 +48,12 @@ def _check(s: FwdShape, seed: int = 0):
     for name, g, w in zip(("dq", "dk", "dv"), grads, want):
         got = g.cpu().double().numpy()
         assert np.all(np.isfinite(got)), f"{name}: non-finite values"
-        excess = np.abs(got - w) - (ATOL[s.dtype] + RTOL[s.dtype] * np.abs(w))
+        err = np.abs(got - w)
+        excess = err - (ATOL[s.dtype] + RTOL[s.dtype] * np.abs(w))
         worst = np.unravel_index(int(np.argmax(excess)), excess.shape)
+        print(f"{s} {name}: max abs error {float(err.max()):.3e} (max |ref| "
+              f"{float(np.abs(w).max()):.3e}), max excess over atol + rtol|ref| "
+              f"{float(excess[worst]):.3e}", flush=True)
         assert excess[worst] <= 0, (f"{s} {name}: error {abs(got[worst] - w[worst]):.3e} at "
                                     f"{worst} where |ref| = {abs(w[worst]):.3e}")
 
