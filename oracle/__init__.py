@@ -257,6 +257,44 @@ def attn_decode_append(q, k_new, v_new, kcache, vcache, positions, *,
     return o, kc, vc
 
 
+def attn_decode_slots(q, kcache, vcache, slots, lengths, *, k_new=None, v_new=None,
+                      scale: float | None = None, lib: ctypes.CDLL | None = None):
+    """Decode over a pool of cache rows through a slot table (float64).
+
+    Row b of the batch uses cache row slots[b] of kcache, vcache
+    [Ncache, Hkv, Smax, d] -- positions reached through a small per-row
+    table (microLLM-rocm optimization log, experiment 098); a slot outside
+    [0, Ncache) makes the row inactive (zero output, no cache access), which
+    leaves it out of the batch's work as active-row compaction does
+    (experiment 097).  Without k_new / v_new: the decode definition over the
+    row's cache row with lengths[b] cached tokens; returns O.  With them:
+    the decode step with append on that cache row at position lengths[b];
+    returns (O, K pool, V pool) with the pools updated (inputs untouched).
+    Composed from attn_decode / attn_decode_append on the gathered rows --
+    no arithmetic of its own."""
+    kc, vc = _f64(kcache), _f64(vcache)
+    if hasattr(slots, "detach"):
+        slots = slots.detach().to("cpu").numpy()
+    if hasattr(lengths, "detach"):
+        lengths = lengths.detach().to("cpu").numpy()
+    sl = np.asarray(slots, dtype=np.int64)
+    ln = np.asarray(lengths, dtype=np.int64)
+    ncache = kc.shape[0]
+    active = (sl >= 0) & (sl < ncache)
+    rows = np.where(active, sl, 0)
+    kg, vg = kc[rows], vc[rows]                       # [B, Hkv, Smax, d]
+    if k_new is None:
+        eff = np.where(active, ln, 0).astype(np.int32)
+        return attn_decode(q, kg, vg, eff, scale=scale, lib=lib)
+    eff = np.where(active, ln, -1).astype(np.int32)   # -1: an inactive append row
+    o, kg2, vg2 = attn_decode_append(q, k_new, v_new, kg, vg, eff, scale=scale, lib=lib)
+    kc2, vc2 = kc.copy(), vc.copy()
+    for b in np.nonzero(active)[0]:
+        kc2[rows[b]] = kg2[b]
+        vc2[rows[b]] = vg2[b]
+    return o, kc2, vc2
+
+
 def attn_mixed(q, k, v, q_offset: int, qd, kcache, vcache, seqlens, *,
                scale: float | None = None, lib: ctypes.CDLL | None = None):
     """(O_chunk, O_decode) as float64 for a mixed batch of one layer.

@@ -411,6 +411,100 @@ def pin_append_equal_keys_mean(lib):
             assert _maxerr(o[b, h], ref) <= 1e-12, f"row {b} head {h}"
 
 
+# --------------------------------------------------------------------------- slot table
+
+def _pool(seed, ncache, Hkv, Smax, d):
+    return _rand((ncache, Hkv, Smax, d), seed), _rand((ncache, Hkv, Smax, d), seed + 1)
+
+
+def pin_slots_library(lib):
+    """Decode through a slot table vs the library routine on each row's own cache
+    row: row b attends the first lengths[b] tokens of pool row slots[b] (rows may
+    share a slot); appending, it attends pool row slots[b]'s first p tokens then
+    its new K/V row, and the returned pools differ from the inputs exactly at
+    position p of each active row's slot; a slot outside [0, Ncache) gives a
+    zero row and touches nothing."""
+    rng = np.random.default_rng(77)
+    for t in range(6):
+        ncache = int(rng.integers(5, 9))
+        Hkv = int(rng.choice([1, 2]))
+        g = int(rng.choice([1, 3]))
+        Smax = int(rng.integers(3, 30))
+        d = int(rng.choice([8, 16]))
+        B = 5
+        kc, vc = _pool(1100 + 10 * t, ncache, Hkv, Smax, d)
+        q = _rand((B, Hkv * g, d), 1105 + 10 * t)
+        slots = rng.permutation(ncache)[:B].astype(np.int32)
+        slots[3] = -1 - int(rng.integers(0, 2))
+        slots[4] = ncache + int(rng.integers(0, 2))
+        scale = 1.0 / math.sqrt(d)
+        # plain decode, one slot read by two rows
+        plain = slots.copy()
+        plain[1] = plain[0]
+        lens = rng.integers(1, Smax + 1, size=B).astype(np.int32)
+        o = oracle.attn_decode_slots(q, kc, vc, plain, lens, scale=scale, lib=lib)
+        for b in range(B):
+            sb = int(plain[b])
+            if sb < 0 or sb >= ncache:
+                assert np.all(o[b] == 0), f"case {t} row {b}: inactive row not zero"
+                continue
+            n = int(lens[b])
+            ref = _sdpa(q[b:b + 1, :, None, :], kc[sb][None, :, :n], vc[sb][None, :, :n],
+                        False, 0, scale)[0, :, 0, :]
+            assert _maxerr(o[b], ref) <= TOL, f"case {t} row {b}"
+        # append
+        kn, vn = _rand((B, Hkv, d), 1107 + 10 * t), _rand((B, Hkv, d), 1108 + 10 * t)
+        pos = rng.integers(0, Smax, size=B).astype(np.int32)
+        o, ko, vo = oracle.attn_decode_slots(q, kc, vc, slots, pos, k_new=kn, v_new=vn,
+                                             scale=scale, lib=lib)
+        wk, wv = kc.copy(), vc.copy()
+        for b in range(B):
+            sb = int(slots[b])
+            if sb < 0 or sb >= ncache:
+                assert np.all(o[b] == 0), f"case {t} row {b}: inactive append row not zero"
+                continue
+            p = int(pos[b])
+            kk = np.concatenate([kc[sb, :, :p], kn[b, :, None, :]], axis=1)
+            vv = np.concatenate([vc[sb, :, :p], vn[b, :, None, :]], axis=1)
+            ref = _sdpa(q[b:b + 1, :, None, :], kk[None], vv[None], False, 0, scale)[0, :, 0, :]
+            assert _maxerr(o[b], ref) <= TOL, f"case {t} append row {b}"
+            wk[sb, :, p] = kn[b]
+            wv[sb, :, p] = vn[b]
+        assert np.array_equal(ko, wk) and np.array_equal(vo, wv), f"case {t}: pools"
+
+
+def pin_slots_identity(lib):
+    """slots[b] = b over a pool of B rows is the plain batch, bit for bit."""
+    B, Hkv, g, Smax, d = 4, 2, 2, 11, 8
+    kc, vc = _pool(1200, B, Hkv, Smax, d)
+    q = _rand((B, Hkv * g, d), 1202)
+    lens = np.array([11, 0, 5, 1], dtype=np.int32)
+    ident = np.arange(B, dtype=np.int32)
+    assert np.array_equal(oracle.attn_decode_slots(q, kc, vc, ident, lens, lib=lib),
+                          oracle.attn_decode(q, kc, vc, lens, lib=lib))
+    kn, vn = _rand((B, Hkv, d), 1203), _rand((B, Hkv, d), 1204)
+    pos = np.array([10, -1, 4, 0], dtype=np.int32)
+    a = oracle.attn_decode_slots(q, kc, vc, ident, pos, k_new=kn, v_new=vn, lib=lib)
+    b = oracle.attn_decode_append(q, kn, vn, kc, vc, pos, lib=lib)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def pin_slots_relabel(lib):
+    """Moving the pool's rows to other places and relabelling the slot table to
+    match changes nothing."""
+    ncache, B, Hkv, g, Smax, d = 6, 4, 1, 4, 9, 8
+    kc, vc = _pool(1300, ncache, Hkv, Smax, d)
+    q = _rand((B, Hkv * g, d), 1302)
+    slots = np.array([2, 5, 0, 3], dtype=np.int32)
+    lens = np.array([9, 3, 7, 2], dtype=np.int32)
+    o = oracle.attn_decode_slots(q, kc, vc, slots, lens, lib=lib)
+    perm = np.array([4, 0, 5, 1, 3, 2])      # pool row r moves to place perm[r]
+    kp, vp = np.empty_like(kc), np.empty_like(vc)
+    kp[perm], vp[perm] = kc, vc
+    o2 = oracle.attn_decode_slots(q, kp, vp, perm[slots].astype(np.int32), lens, lib=lib)
+    assert np.array_equal(o, o2)
+
+
 # --------------------------------------------------------------------------- backward
 
 def _sdpa_grads(q, k, v, dout, causal, q_offset, scale):
@@ -653,6 +747,9 @@ PINS = [
     pin_append_library,
     pin_append_first_slot,
     pin_append_equal_keys_mean,
+    pin_slots_library,
+    pin_slots_identity,
+    pin_slots_relabel,
     pin_bwd_library,
     pin_bwd_finite_differences,
     pin_bwd_closed_forms,

@@ -270,5 +270,49 @@ def test_planted_varlen_mistake_is_caught(lib, monkeypatch, kind):
     assert caught, f"varlen mutant '{kind}' passed every varlen pin"
 
 
+# Planted mistakes in the slot-table composition (Python): each wrong
+# attn_decode_slots must fail one of the slot pins.
+def _slots_mutant(kind):
+    real = oracle.attn_decode_slots
+
+    def f(q, kcache, vcache, slots, lengths, *, k_new=None, v_new=None, scale=None, lib=None):
+        sl = np.asarray(slots, dtype=np.int64).copy()
+        if kind == "slot table ignored":
+            sl = np.arange(len(sl))
+            sl = np.minimum(sl, np.asarray(kcache).shape[0] - 1)
+        if kind == "inactive rows read pool row 0":
+            sl = np.where((sl >= 0) & (sl < np.asarray(kcache).shape[0]), sl, 0)
+        res = real(q, kcache, vcache, sl.astype(np.int32), lengths, k_new=k_new, v_new=v_new,
+                   scale=scale, lib=lib)
+        if kind == "append writes row b of the pool" and k_new is not None:
+            o, kc2, vc2 = res
+            kc2, vc2 = oracle._f64(kcache).copy(), oracle._f64(vcache).copy()
+            pos = np.asarray(lengths)
+            for b in range(len(sl)):
+                if 0 <= sl[b] < kc2.shape[0] and 0 <= pos[b] < kc2.shape[2] and b < kc2.shape[0]:
+                    kc2[b, :, pos[b]] = oracle._f64(k_new)[b]
+                    vc2[b, :, pos[b]] = oracle._f64(v_new)[b]
+            res = (o, kc2, vc2)
+        return res
+    return f
+
+
+SLOTS_MUTANTS = ["slot table ignored", "inactive rows read pool row 0",
+                 "append writes row b of the pool"]
+
+
+@pytest.mark.parametrize("kind", SLOTS_MUTANTS)
+def test_planted_slots_mistake_is_caught(lib, monkeypatch, kind):
+    monkeypatch.setattr(oracle, "attn_decode_slots", _slots_mutant(kind))
+    caught = False
+    for pin in (oracle_pins.pin_slots_library, oracle_pins.pin_slots_identity,
+                oracle_pins.pin_slots_relabel):
+        try:
+            pin(lib)
+        except Exception:
+            caught = True
+    assert caught, f"slot-table mutant '{kind}' passed every slot pin"
+
+
 def test_pin_module_importable():
     assert len(oracle_pins.PINS) >= 15
