@@ -253,6 +253,43 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new,
                            int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode over a pool of cache rows reached through a slot table: row b of
+ * the batch reads -- and, appending, writes -- cache row slots[b], so a
+ * serving loop can keep its sequences wherever the pool has room, reorder
+ * or compact its batch, and leave finished or waiting rows out, without
+ * moving any cache (the microLLM-rocm optimization log: positions through a
+ * small per-row table, experiment 098, and compaction of the active rows,
+ * experiment 097).
+ *
+ *   q, o           : [B, Hq, d]            (batch row b)
+ *   kcache, vcache : [Ncache, Hkv, Smax, d]
+ *   slots          : int32[B], device; slots[b] in [0, Ncache) names row b's
+ *                    cache row, any other value makes row b inactive: its
+ *                    output is all zero and nothing of the cache is read or
+ *                    written for it
+ *   lengths        : int32[B], device; without k_new / v_new, the number of
+ *                    cached tokens row b attends (clamped to [0, Smax]);
+ *                    with them, the position p of row b's new token, as
+ *                    gqa_attn_decode_append's positions (p outside [0, Smax)
+ *                    makes the row inactive)
+ *   k_new, v_new   : both NULL (plain decode) or both [B, Hkv, d] (append:
+ *                    row b's new K/V rows go to position p of cache row
+ *                    slots[b], and the row attends positions 0 .. p)
+ *
+ * Rows may share a slot when nothing is appended; appending rows must have
+ * different slots (two writes to one cache row race).  With slots[b] = b and
+ * Ncache = B the results are those of gqa_attn_decode / _append bit for bit.
+ * Workspace: gqa_attn_decode_workspace_bytes(B, Hq, Hkv, Smax, d).  Inactive
+ * rows are found on the device; their parts end at once.  Errors as
+ * gqa_attn_decode / _append; Ncache < 1 -> GQA_ERR_BAD_SHAPE; a NULL slots
+ * or lengths, or only one of k_new / v_new -> GQA_ERR_NULL_POINTER.
+ */
+int gqa_attn_decode_slots(const void* q, const void* k_new, const void* v_new, void* kcache,
+                          void* vcache, int Ncache, const int32_t* slots, const int32_t* lengths,
+                          void* o, int B, int Hq, int Hkv, int Smax, int d, float scale,
+                          int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Mixed batch of one layer in one persistent launch: the causal query chunk
  * of a chunked prefill and single-token decode rows.
  *

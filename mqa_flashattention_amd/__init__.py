@@ -11,7 +11,7 @@ entry point does, and raises if it has not been built.
 from __future__ import annotations
 
 __all__ = ["attn_fwd", "attn_fwd_strided", "attn_fwd_varlen", "attn_decode", "attn_decode_noalloc",
-           "attn_decode_append", "attn_bwd",
+           "attn_decode_append", "attn_decode_slots", "attn_bwd",
            "attn_mixed", "decode_workspace_bytes", "bwd_workspace_bytes", "library_path",
            "GqaError"]
 

@@ -27,9 +27,9 @@ STATUS_NAMES = {
     4: "GQA_ERR_UNSUPPORTED", 5: "GQA_ERR_WORKSPACE", 6: "GQA_ERR_NO_DEVICE", 7: "GQA_ERR_HIP",
 }
 EXPORTED = ("gqa_attn_fwd", "gqa_attn_fwd_strided", "gqa_attn_fwd_varlen", "gqa_attn_decode",
-            "gqa_attn_decode_noalloc", "gqa_attn_decode_append", "gqa_attn_decode_workspace_bytes", "gqa_attn_bwd",
-            "gqa_attn_bwd_workspace_bytes", "gqa_attn_mixed", "gqa_status_string",
-            "gqa_last_error_string")
+            "gqa_attn_decode_noalloc", "gqa_attn_decode_append", "gqa_attn_decode_slots",
+            "gqa_attn_decode_workspace_bytes", "gqa_attn_bwd", "gqa_attn_bwd_workspace_bytes",
+            "gqa_attn_mixed", "gqa_status_string", "gqa_last_error_string")
 
 
 class GqaError(RuntimeError):
@@ -62,6 +62,9 @@ def _load() -> ctypes.CDLL:
     lib.gqa_attn_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp,
                                            sz, vp]
     lib.gqa_attn_decode_append.restype = i
+    lib.gqa_attn_decode_slots.argtypes = [vp, vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, f, i,
+                                          vp, sz, vp]
+    lib.gqa_attn_decode_slots.restype = i
     lib.gqa_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.gqa_attn_bwd_workspace_bytes.restype = sz
     lib.gqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp,
@@ -408,6 +411,68 @@ def attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor
                                         workspace.data_ptr(),
                                         workspace.numel() * workspace.element_size(),
                                         _stream_handle(dev))
+    _raise(st)
+    return out
+
+
+def attn_decode_slots(q: torch.Tensor, kcache: torch.Tensor, vcache: torch.Tensor,
+                      slots: torch.Tensor, lengths: torch.Tensor, *,
+                      k_new: torch.Tensor | None = None, v_new: torch.Tensor | None = None,
+                      scale: float | None = None, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode over a cache pool through a slot table, via gqa_attn_decode_slots.
+
+    q [B, Hq, d]; kcache, vcache [Ncache, Hkv, Smax, d]; slots and lengths
+    int32 [B] on the same GPU.  Row b reads cache row slots[b] (a slot outside
+    [0, Ncache) makes the row inactive: zero output, no cache access).
+    Without k_new / v_new, lengths[b] is the row's cached length; with them
+    ([B, Hkv, d] each) it is the new token's position p, whose K/V rows are
+    written to cache row slots[b] at p (in place) before the row attends
+    positions 0 .. p."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    _check_tensor("q", q, 3, q.dtype, dev)
+    _check_tensor("kcache", kcache, 4, q.dtype, dev)
+    _check_tensor("vcache", vcache, 4, q.dtype, dev)
+    _check_tensor("slots", slots, 1, torch.int32, dev)
+    _check_tensor("lengths", lengths, 1, torch.int32, dev)
+    B, Hq, d = q.shape
+    Ncache, Hkv, Smax, _ = kcache.shape
+    if kcache.shape[3] != d or tuple(vcache.shape) != tuple(kcache.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} kcache{tuple(kcache.shape)}")
+    if slots.shape[0] != B or lengths.shape[0] != B:
+        raise ValueError("slots and lengths must have B entries")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _check_tensor("k_new", k_new, 3, q.dtype, dev)
+        _check_tensor("v_new", v_new, 3, q.dtype, dev)
+        if tuple(k_new.shape) != (B, Hkv, d) or tuple(v_new.shape) != (B, Hkv, d):
+            raise ValueError(f"k_new and v_new must be [B, Hkv, d] = {(B, Hkv, d)}")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, 3, q.dtype, dev)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must have the shape of q")
+    need = decode_workspace_bytes(B, Hq, Hkv, Smax, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the GPU of q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    with torch.cuda.device(dev):
+        st = lib.gqa_attn_decode_slots(q.data_ptr(),
+                                       k_new.data_ptr() if k_new is not None else None,
+                                       v_new.data_ptr() if v_new is not None else None,
+                                       kcache.data_ptr(), vcache.data_ptr(), Ncache,
+                                       slots.data_ptr(), lengths.data_ptr(), out.data_ptr(), B,
+                                       Hq, Hkv, Smax, d, float(scale), _DTYPES[q.dtype],
+                                       workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream_handle(dev))
     _raise(st)
     return out
 

@@ -42,6 +42,11 @@ struct DecodeArgs {
   void* vc_out;            // append: the V cache again
   void* o;
   float* ws;  // [B][Hq][NS][D + 4]: acc[D], m (scaled), l, 2 pad (16-byte records)
+  // slot table: row b reads (and, appending, writes) cache row slots[b] of
+  // Ncache; a slot outside [0, Ncache) marks an inactive row.  NULL: row b
+  // is cache row b.
+  const int32_t* slots;
+  int Ncache;
   int B, Hq, Hkv, Smax;
   int g;      // Hq / Hkv
   int NCB;    // 32-head column blocks per K/V head, ceil(g / 32)
@@ -56,11 +61,28 @@ __device__ __forceinline__ int clamp_len(int32_t n, int smax) {
   return n < 0 ? 0 : (n > smax ? smax : n);
 }
 
+// Whether row b's slot (if there is a slot table) names a cache row.
+__device__ __forceinline__ bool slot_ok(const DecodeArgs& a, int b) {
+  if (!a.slots) return true;
+  const int32_t s = a.slots[b];
+  return s >= 0 && s < a.Ncache;
+}
+
+// Cache row of batch row b: its slot, or b without a slot table (0 for an
+// inactive row, which reads and writes nothing).
+__device__ __forceinline__ int cache_row(const DecodeArgs& a, int b) {
+  if (!a.slots) return b;
+  const int32_t s = a.slots[b];
+  return (s >= 0 && s < a.Ncache) ? s : 0;
+}
+
 // Cache slots row b attends: the cached length clamped to [0, Smax]; with
 // append, position p in [0, Smax) gives p + 1 (the new token included) and
-// any other position marks an inactive row (0: no store, zero output).
+// any other position marks an inactive row (0: no store, zero output), as
+// does a slot outside the cache.
 template <bool APPEND>
 __device__ __forceinline__ int row_len(const DecodeArgs& a, int b) {
+  if (!slot_ok(a, b)) return 0;
   const int32_t x = a.seqlens[b];
   if constexpr (APPEND) return (x >= 0 && x < a.Smax) ? x + 1 : 0;
   else return clamp_len(x, a.Smax);
@@ -132,7 +154,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, char* smem, in
         nk = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.knew) + src)[lane];
         nv = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.vnew) + src)[lane];
         if (cb == 0) {
-          const size_t dst = (((size_t)b * a.Hkv + hkv) * a.Smax + pos) * C::D;
+          const size_t dst = (((size_t)cache_row(a, b) * a.Hkv + hkv) * a.Smax + pos) * C::D;
           reinterpret_cast<u32x4*>(reinterpret_cast<T*>(a.kc_out) + dst)[lane] = nk;
           reinterpret_cast<u32x4*>(reinterpret_cast<T*>(a.vc_out) + dst)[lane] = nv;
         }
@@ -150,7 +172,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, char* smem, in
   load_q_frag<T, C>(qf, Q + (valid ? ((size_t)b * a.Hq + h) * C::D : 0), valid,
                     a.negate_q != 0, h2);
 
-  const size_t head_off = (((size_t)b * a.Hkv + hkv) * a.Smax + start) * C::D;
+  const size_t head_off = (((size_t)cache_row(a, b) * a.Hkv + hkv) * a.Smax + start) * C::D;
   const T* kbase = uniform_ptr(reinterpret_cast<const T*>(a.kc) + head_off);
   const T* vbase = uniform_ptr(reinterpret_cast<const T*>(a.vc) + head_off);
 

@@ -196,6 +196,7 @@ __device__ __forceinline__ void part_reset(PartState<P>& st) {
 // token is key len - 1).
 struct PartSeg {
   int b, hkv, cg, start, ntok, len;
+  int crow;               // the row's cache row (its slot)
   const uint16_t* kbase;  // key row `start` of the head, wave-uniform
   const uint16_t* vbase;
 };
@@ -210,7 +211,8 @@ __device__ __forceinline__ PartSeg part_seg(const DecodeArgs& a, int b, int hkv,
   sg.start = start;
   sg.ntok = ntok;
   sg.len = len;
-  const size_t head_off = (((size_t)b * a.Hkv + hkv) * a.Smax + start) * P::D;
+  sg.crow = cache_row(a, b);
+  const size_t head_off = (((size_t)sg.crow * a.Hkv + hkv) * a.Smax + start) * P::D;
   sg.kbase = uniform_ptr(reinterpret_cast<const uint16_t*>(a.kc) + head_off);
   sg.vbase = uniform_ptr(reinterpret_cast<const uint16_t*>(a.vc) + head_off);
   return sg;
@@ -283,7 +285,7 @@ __device__ __forceinline__ void part_step(const DecodeArgs& a, const PartSeg& sg
         constexpr int CH = P::ROWB / 16;
         if (lane < CH) {
           const size_t dst =
-              (((size_t)sg.b * a.Hkv + sg.hkv) * a.Smax + sg.start + new_key) * P::D;
+              (((size_t)sg.crow * a.Hkv + sg.hkv) * a.Smax + sg.start + new_key) * P::D;
           reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.kc_out) + dst)[lane] =
               reinterpret_cast<const u32x4*>(kn)[lane];
           reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.vc_out) + dst)[lane] =

@@ -737,7 +737,8 @@ int fwd_entry(const void* q, const void* k, const void* v, void* o, int B, int H
 int decode_setup(const void* q, const void* kcache, const void* vcache, const int32_t* lens,
                  const void* knew, const void* vnew, void* kc_out, void* vc_out, void* o, int B,
                  int Hq, int Hkv, int Smax, int d, float scale, int dtype, void* workspace,
-                 size_t workspace_bytes, gqa::DecodeArgs* out, bool check_ws = true) {
+                 size_t workspace_bytes, gqa::DecodeArgs* out, bool check_ws = true,
+                 const int32_t* slots = nullptr, int Ncache = 0) {
   const bool append = knew != nullptr;
   if (B < 1 || Hq < 1 || Hkv < 1 || Smax < 1 || d < 1)
     return fail(GQA_ERR_BAD_SHAPE, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Smax=%d d=%d)", B, Hq,
@@ -774,6 +775,8 @@ int decode_setup(const void* q, const void* kcache, const void* vcache, const in
   a.vc_out = vc_out;
   a.o = o;
   a.ws = reinterpret_cast<float*>(workspace);
+  a.slots = slots;
+  a.Ncache = slots ? Ncache : B;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -796,11 +799,13 @@ void decode_splits(gqa::DecodeArgs& a, int cus, int waves_per_cu = 4) {
 int decode_entry(const void* q, const void* kcache, const void* vcache, const int32_t* lens,
                  const void* knew, const void* vnew, void* kc_out, void* vc_out, void* o, int B,
                  int Hq, int Hkv, int Smax, int d, float scale, int dtype, void* workspace,
-                 size_t workspace_bytes, void* stream, bool static_ws = false) {
+                 size_t workspace_bytes, void* stream, bool static_ws = false,
+                 const int32_t* slots = nullptr, int Ncache = 0) {
   const bool append = knew != nullptr;
   gqa::DecodeArgs a;
   int st = decode_setup(q, kcache, vcache, lens, knew, vnew, kc_out, vc_out, o, B, Hq, Hkv, Smax,
-                        d, scale, dtype, workspace, workspace_bytes, &a, !static_ws);
+                        d, scale, dtype, workspace, workspace_bytes, &a, !static_ws, slots,
+                        Ncache);
   if (st != GQA_OK) return st;
   if (static_ws) {
     const size_t need = decode_ws_bytes(B, Hq, Smax, d, kMinSplit);
@@ -1221,6 +1226,22 @@ int gqa_attn_decode_append(const void* q, const void* k_new, const void* v_new, 
                 "q, k_new, v_new, kcache, vcache, positions and o must be non-NULL");
   return decode_entry(q, kcache, vcache, positions, k_new, v_new, kcache, vcache, o, B, Hq, Hkv,
                       Smax, d, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+int gqa_attn_decode_slots(const void* q, const void* k_new, const void* v_new, void* kcache,
+                          void* vcache, int Ncache, const int32_t* slots, const int32_t* lengths,
+                          void* o, int B, int Hq, int Hkv, int Smax, int d, float scale,
+                          int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!q || !kcache || !vcache || !slots || !lengths || !o)
+    return fail(GQA_ERR_NULL_POINTER, "q, kcache, vcache, slots, lengths and o must be non-NULL");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(GQA_ERR_NULL_POINTER, "k_new and v_new must both be given or both be NULL");
+  if (Ncache < 1) return fail(GQA_ERR_BAD_SHAPE, "Ncache must be >= 1 (got %d)", Ncache);
+  const bool append = k_new != nullptr;
+  return decode_entry(q, kcache, vcache, lengths, k_new, v_new, append ? kcache : nullptr,
+                      append ? vcache : nullptr, o, B, Hq, Hkv, Smax, d, scale, dtype, workspace,
+                      workspace_bytes, stream, false, slots, Ncache);
 }
 
 int gqa_attn_decode_noalloc(const void* q, const void* kcache, const void* vcache,

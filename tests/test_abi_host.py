@@ -228,6 +228,31 @@ def test_decode_workspace_bytes():
         assert ws(*bad) == 0
 
 
+def slt(q=P[0], kn=None, vn=None, kc=P[1], vc=P[2], ncache=16, slots=P[4], lens=P[5], o=P[3],
+        B=8, Hq=12, Hkv=2, Smax=2048, d=128, scale=0.09, dtype=BF16, ws=P[6], ws_bytes=None,
+        stream=None):
+    if ws_bytes is None:
+        ws_bytes = binding.decode_workspace_bytes(B, Hq, Hkv, Smax, d)
+    return binding.lib.gqa_attn_decode_slots(q, kn, vn, kc, vc, ncache, slots, lens, o, B, Hq,
+                                             Hkv, Smax, d, ctypes.c_float(scale), dtype, ws,
+                                             ws_bytes, stream)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(kc=None), NULLP), (dict(slots=None), NULLP),
+    (dict(lens=None), NULLP), (dict(o=None), NULLP), (dict(kn=P[7]), NULLP),
+    (dict(vn=P[7]), NULLP),
+    (dict(ncache=0), SHAPE), (dict(B=0), SHAPE), (dict(Smax=-1), SHAPE),
+    (dict(Hq=12, Hkv=5), GROUP),
+    (dict(d=48), UNSUP), (dict(dtype=7), UNSUP), (dict(scale=float("nan")), UNSUP),
+    (dict(kn=ctypes.c_void_p(0x30004), vn=P[7]), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=64), WS),
+])
+def test_decode_slots_rejects_invalid_arguments(kw, code):
+    assert slt(**kw) == code
+    assert binding.lib.gqa_last_error_string()
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="valid arguments would launch on a GPU")
 def test_valid_call_without_gpu_reports_no_device():
     assert fwd() == NODEV
@@ -237,6 +262,8 @@ def test_valid_call_without_gpu_reports_no_device():
     assert app() == NODEV
     assert fwd_s() == NODEV
     assert var() == NODEV
+    assert slt() == NODEV
+    assert slt(kn=P[7], vn=P[0]) == NODEV
     # zero K/V batch stride (broadcast reads) is valid
     assert fwd_s(kvs=(0, 64, 128)) == NODEV
 
