@@ -1122,8 +1122,8 @@ def summarize_trace(stats_csv: str, command: str, out_name: str):
         for r in csv.DictReader(f):
             if "gqa::" not in r["Name"] and "_peak_kernel" not in r["Name"]:
                 continue
-            n = r["Name"].split("(")[0].replace("void ", "")
-            n = n.replace("(anonymous namespace)::", "")
+            n = r["Name"].replace("(anonymous namespace)::", "")
+            n = n.split("(")[0].replace("void ", "")
             rows.append((_short(n), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
                          float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
     lines = [f"# Kernel durations: {out_name}", "", "    " + command, "",
