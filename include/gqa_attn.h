@@ -32,8 +32,9 @@
  *  - Library state: one small block of scheduler counters per (device,
  *    stream), allocated and cleared on the first call that needs it, and,
  *    for forwards with fewer units than resident workgroups, a per-stream
- *    buffer of partial records grown when a call needs more (after draining
- *    the stream); both are kept until the process ends.  Calls on one
+ *    buffer of partial records grown when a call needs more (a replaced
+ *    buffer is kept, so launches already queued and graphs captured earlier
+ *    stay valid); all of it is kept until the process ends.  Calls on one
  *    stream are ordered; calls on different streams use different state.
  *  - HIP graphs: a call may be captured once one eager call with the same
  *    sizes has run on the capturing stream -- it then allocates nothing and

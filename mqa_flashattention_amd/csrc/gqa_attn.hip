@@ -17,6 +17,7 @@
 #include <string>
 #include <type_traits>
 #include <utility>
+#include <vector>
 
 #include "backward_kernel.hpp"
 #include "decode_kernel.hpp"
@@ -118,17 +119,19 @@ hipError_t zero_ints(int* p, long long n, hipStream_t stream) {
 //    mixed launch's decode-split counter, zeroed in stream order when
 //    allocated; each persistent launch leaves them at zero when it ends;
 //  * ws: partial records of the prefill units that the balanced schedule
-//    cuts, grown on demand (after the stream drains, so no queued launch
-//    still uses the old buffer).
+//    cuts, grown on demand to at least twice its size.  A replaced buffer is
+//    kept, not freed, until the process ends: launches still queued, and
+//    HIP graphs captured earlier, keep using it.
 // Neither may be set up while the stream is being captured into a HIP graph
-// (an allocation and a drain are not graph work): such a call fails, and one
-// eager call with the same sizes on the stream beforehand makes the
-// captured one allocation-free.
+// (an allocation is not graph work): such a call fails, and one eager call
+// with the same sizes on the stream beforehand makes the captured one
+// allocation-free.
 constexpr int kCounterInts = (gqa::kMixedDecodeCounter + 1) * gqa::kCounterStride;
 struct StreamState {
   int* ctr = nullptr;
   float* ws = nullptr;
   size_t ws_bytes = 0;
+  std::vector<void*> retired;  // replaced record buffers (see above)
 };
 std::map<std::pair<int, void*>, StreamState> g_streams;
 
@@ -160,19 +163,17 @@ int stream_state(int dev, hipStream_t stream, size_t ws_bytes, StreamState* out)
     }
   }
   if (ws_bytes > s.ws_bytes) {
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize before workspace growth");
-    if (s.ws) (void)hipFree(s.ws);
-    s.ws = nullptr;
-    s.ws_bytes = 0;
-    e = hipMalloc(&s.ws, ws_bytes);
-    if (e != hipSuccess) {
-      s.ws = nullptr;
-      return hip_fail(e, "hipMalloc(split workspace)");
-    }
-    s.ws_bytes = ws_bytes;
+    const size_t grow = std::max(ws_bytes, 2 * s.ws_bytes);
+    float* fresh = nullptr;
+    e = hipMalloc(&fresh, grow);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(split workspace)");
+    if (s.ws) s.retired.push_back(s.ws);
+    s.ws = fresh;
+    s.ws_bytes = grow;
   }
-  *out = s;
+  out->ctr = s.ctr;
+  out->ws = s.ws;
+  out->ws_bytes = s.ws_bytes;
   return GQA_OK;
 }
 

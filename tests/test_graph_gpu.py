@@ -73,6 +73,39 @@ def test_varlen_graph_replay_matches_eager():
                          [o], s)
 
 
+def test_graph_survives_a_later_larger_workspace():
+    """A graph captured on the balanced schedule keeps replaying correctly after
+    a larger eager call on the same stream has grown the stream's record
+    buffer (the replaced buffer stays allocated)."""
+    small = FwdShape(1, 8, 2, 512, 512, 128, False, 0)
+    big = FwdShape(1, 8, 2, 1024, 1024, 128, False, 0)   # balanced, 4x the records
+    q, k, v = (t.to(DEV) for t in fwd_inputs(small, 24))
+    o = torch.empty_like(q)
+    s = torch.cuda.Stream()
+
+    def call():
+        attn_fwd(q, k, v, scale=small.scale, out=o)
+
+    with torch.cuda.stream(s):
+        call()
+    s.synchronize()
+    ref = o.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    qb, kb, vb = (t.to(DEV) for t in fwd_inputs(big, 25))
+    with torch.cuda.stream(s):
+        ob = attn_fwd(qb, kb, vb, scale=big.scale)   # grows the record buffer
+    s.synchronize()
+    for _ in range(3):
+        o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref)
+    assert torch.isfinite(ob).all()
+
+
 def test_capture_before_setup_fails_cleanly():
     """The first persistent call on a fresh stream must allocate its
     counters, which capture cannot hold: it fails and launches nothing; the
