@@ -6,19 +6,21 @@
 // decode tokens of other sequences.  Here both kinds of work come from one
 // persistent launch (the work-queue scheduler of the BootstrapAI evolution
 // log, "Kernel 8 -- persistent kernel", here with two kinds of item): a
-// workgroup first takes the chunk's prefill units, heaviest first, and once
-// they are gone takes decode splits from one more counter, DW at a time (one
-// per wave, each wave in an LDS area of its own).  So the decode splits go
-// to the CUs that the prefill units leave idle -- at the start when the
-// chunk has fewer units than resident workgroups, and in the tail.  The
-// decode rows' partial states are merged by the decode combine pass,
-// launched after this kernel.
+// workgroup first takes the chunk's prefill units, heaviest first (or, with
+// no more units than workgroups, runs the unit of its own index), and then
+// takes decode work from one more counter: bf16, the parts of
+// gqa_attn_decode, one per group of waves; fp32, splits, one per wave in an
+// LDS area of its own.  So the decode work goes to the CUs that the prefill
+// units leave idle -- at the start when the chunk has fewer units than
+// resident workgroups, and in the tail.  The decode rows' partial states are
+// merged by the decode merge (bf16) or combine (fp32) pass, launched after
+// this kernel.
 //
 // Prefill and decode waves never share a CU: the prefill units use the
-// whole register budget of two waves per SIMD, which leaves the decode
-// splits one register staging set per wave (two in the decode kernel).  On
-// the batches measured so far this launch is slower than a prefill call
-// followed by a decode call.
+// whole register budget of two waves per SIMD.  On the LLaMA-3-8B batches
+// measured, this launch runs at the speed of a prefill call followed by a
+// decode call (512-query chunk) or 4 % slower (128-query chunk, whose 64
+// units leave the chunk on 64 CUs).
 //
 // Two prefill unit shapes, as for a prefill launch:
 //  * mixed_kernel: 4-wave workgroups on 128-column units from the XCD
@@ -156,12 +158,12 @@ mixed_kernel(MixedArgs m) {
   const int lane = tid & 63;
   const int j = lane & 31;
 
-  // ---- prefill units
+  // ---- prefill units (none without a chunk: no take at all)
   const int home = blockIdx.x % kNumQueues;
   const int nkv = a.B * a.Hkv;
   const int per_group = a.HB * a.NQB;
   bool home_empty = false;  // wave 0: the home queue has run dry
-  for (;;) {
+  for (; a.T > 0;) {
     __syncthreads();  // every wave has read the previous item's shared words
     if (w == 0) {
       int t, q;
@@ -207,6 +209,18 @@ mixed_quad_kernel(MixedArgs m) {
   const PrefillArgs& a = m.p;
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  if (a.T <= (int)gridDim.x) {
+    // at most one unit per workgroup: workgroup i runs unit i as the quad
+    // prefill launch maps it (a K/V group's units on one XCD), with no take
+    if ((int)blockIdx.x < a.T) {
+      const int i = blockIdx.x;
+      const int t = (a.T % 8 == 0) ? (i % 8) * (a.T / 8) + i / 8 : i;
+      quad_unit<T, CQ, true>(a, smem, t);
+    }
+    mixed_decode_phase<T, CD, DW, 4 * CQ::NW>(m, smem, &s_unit);
+    leave_persistent(a, kMixedDecodeCounter);
+    return;
+  }
   const int home = blockIdx.x % kNumQueues;
   const int nkv = a.B * a.Hkv;
   const int per_group = a.HB * a.NQB;

@@ -475,9 +475,12 @@ __device__ __forceinline__ void persistent_unit(const PrefillArgs& a, char* smem
 // The last workgroup to leave a persistent launch (all others have made
 // their final, failing fetches) sets counters 0 .. last back to zero for
 // the next launch; counter kNumQueues counts the workgroups that left.
+// Wave 0 (thread 0 among its lanes) made every take and probe of its
+// workgroup and used each returned value, so those atomics are complete
+// before its count below is issued: no fence is needed (an agent-scope fence here writes back and invalidates the
+// whole L2 at every workgroup's exit).
 __device__ __forceinline__ void leave_persistent(const PrefillArgs& a, int last) {
   if (threadIdx.x == 0) {
-    __threadfence();
     const int done = atomicAdd(a.ctr + kNumQueues * kCounterStride, 1);
     if (done == (int)gridDim.x - 1) {
       for (int i = 0; i <= last; ++i) atomicExch(a.ctr + i * kCounterStride, 0);
