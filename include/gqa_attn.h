@@ -184,8 +184,9 @@ size_t gqa_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Smax, int d);
  * Cache heads are addressed in place through the head mapping, with no
  * per-query-head copies (microLLM-rocm optimization log, experiment 004,
  * and the per-head capacity stride of experiment 062); the KV sequence is
- * cut into splits whose partial softmax states are merged by a second pass
- * (the split-sequence cached attention of experiments 283/284).
+ * cut into parts (bf16) or splits (fp32) whose partial softmax states are
+ * merged by a second pass (the split-sequence cached attention of
+ * experiments 283/284), in a fixed order, so results repeat bit for bit.
  *
  * workspace: device memory of at least gqa_attn_decode_workspace_bytes(...)
  * bytes, owned by the caller; its contents on entry do not matter.  One
@@ -312,25 +313,28 @@ int gqa_attn_decode_slots(const void* q, const void* k_new, const void* v_new, v
  * chunks (compute-bound) beside decode tokens (memory-bound).  Both come
  * from one persistent launch whose workgroups take the chunk's units (the
  * GQA head mapping and heaviest-first unit queues of the persistent prefill
- * schedule) and then the decode splits from the same counters -- the
+ * schedule) and then the decode work from the same counters -- the
  * "Kernel 10" of the BootstrapAI evolution log, persistent scheduling with
  * the GQA head mapping -- so decode work fills the CUs the chunk leaves
- * idle.  A second launch merges the decode rows' split states.  A chunk of
- * few, long units (at most two 64-column units per CU, >= 8 key tiles each)
- * runs as the quad schedule's units, others as the persistent schedule's;
- * the chunk's outputs equal gqa_attn_fwd's bit for bit when it picks the
- * same schedule, and to within rounding order otherwise.  The decode rows
- * use gqa_attn_decode's splits, and equal its outputs bit for bit, unless
- * the chunk's units fill every resident workgroup; then they are cut into
- * about twice as many splits (eight decode waves per CU, run in the chunk's
- * tail) and equal its outputs to within rounding order.
+ * idle.  A second launch merges the decode rows' partial states.  A chunk
+ * of few, long units (at most two 64-column units per CU, >= 8 key tiles
+ * each) runs as the quad schedule's units, others as the persistent
+ * schedule's; the chunk's outputs equal gqa_attn_fwd's bit for bit when it
+ * picks the same schedule, and to within rounding order otherwise.  bf16
+ * decode rows run gqa_attn_decode's parts and equal its outputs bit for
+ * bit.  fp32 decode rows use gqa_attn_decode's splits, and equal its
+ * outputs bit for bit, unless the chunk's units fill every resident
+ * workgroup; then they are cut into about twice as many splits (eight
+ * decode waves per CU, run in the chunk's tail) and equal its outputs to
+ * within rounding order.
  *
  * workspace: at least gqa_attn_decode_workspace_bytes(Bd, Hq, Hkv, Smax, d)
  * bytes when Bd > 0, as for gqa_attn_decode.  Calls that may run
  * concurrently must use different streams (each stream has its own
  * scheduler counters) and different workspaces.  The first call on a
  * stream allocates and clears that stream's counters; later calls allocate
- * nothing and record no memset, so they may be captured in a HIP graph.
+ * nothing and record no memset, so they may be captured in a HIP graph
+ * (see the conventions at the top).
  *
  * Errors: B < 0 or Bd < 0 -> GQA_ERR_BAD_SHAPE; a NULL pointer of a part
  * that is present -> GQA_ERR_NULL_POINTER; otherwise each present part is
