@@ -44,6 +44,7 @@ CASES = [  # (B, Hq, Hkv, Smax, d, dtype, ncache)
     (6, 32, 8, 700, 64, torch.bfloat16, 9),
     (5, 4, 1, 333, 32, torch.bfloat16, 7),
     (7, 8, 2, 300, 64, torch.float32, 11),
+    (6, 40, 1, 500, 128, torch.bfloat16, 8),    # g = 40: two 16-head column blocks per wave
 ]
 
 

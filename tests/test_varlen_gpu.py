@@ -68,6 +68,12 @@ def test_varlen_head_modes(Hkv):
     _run([77, 513, 2, 190], [77, 600, 2, 190], 8, Hkv, 64, torch.bfloat16, True, seed=3)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(40, 1), (160, 1)], ids=["g40", "g160"])
+def test_varlen_large_groups(Hq, Hkv):
+    """Groups wider than a unit's 128 columns (several head blocks per K/V head)."""
+    _run([33, 200, 5], [33, 260, 5], Hq, Hkv, 128, torch.bfloat16, True, seed=6)
+
+
 def test_varlen_keyless_rows_are_zero():
     """Causal rows i < Nq - Nk see no key; a sequence with Nk = 0 has none."""
     got, _, cq, ck = _run([40, 6, 9], [10, 0, 9], 4, 2, 64, torch.bfloat16, True, seed=5,
