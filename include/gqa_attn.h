@@ -316,11 +316,15 @@ int gqa_attn_decode_slots(const void* q, const void* k_new, const void* v_new, v
  * schedule) and then the decode work from the same counters -- the
  * "Kernel 10" of the BootstrapAI evolution log, persistent scheduling with
  * the GQA head mapping -- so decode work fills the CUs the chunk leaves
- * idle.  A second launch merges the decode rows' partial states.  A chunk
- * of few, long units (at most two 64-column units per CU, >= 8 key tiles
- * each) runs as the quad schedule's units, others as the persistent
- * schedule's; the chunk's outputs equal gqa_attn_fwd's bit for bit when it
- * picks the same schedule, and to within rounding order otherwise.  bf16
+ * idle.  The chunk runs as gqa_attn_fwd would run it: quad units when that
+ * call takes them (few, long units); else, with too few units to balance
+ * whole ones, the balanced schedule's key-tile chunks, sized for half of
+ * the resident workgroups so the decode work starts at once on the rest;
+ * else the persistent schedule's units.  Merge launches follow: the
+ * chunk's units cut by the balanced schedule, then the decode rows'
+ * partial states.  The chunk's outputs equal gqa_attn_fwd's bit for bit
+ * when both cut its keys the same way (the quad and persistent units), and
+ * to within rounding order otherwise.  bf16
  * decode rows run gqa_attn_decode's parts and equal its outputs bit for
  * bit.  fp32 decode rows use gqa_attn_decode's splits, and equal its
  * outputs bit for bit, unless the chunk's units fill every resident
@@ -332,9 +336,10 @@ int gqa_attn_decode_slots(const void* q, const void* k_new, const void* v_new, v
  * bytes when Bd > 0, as for gqa_attn_decode.  Calls that may run
  * concurrently must use different streams (each stream has its own
  * scheduler counters) and different workspaces.  The first call on a
- * stream allocates and clears that stream's counters; later calls allocate
- * nothing and record no memset, so they may be captured in a HIP graph
- * (see the conventions at the top).
+ * stream allocates and clears that stream's counters, and a call whose
+ * chunk needs more partial-record space than the stream holds grows it;
+ * later calls of the same sizes allocate nothing and record no memset, so
+ * they may be captured in a HIP graph (see the conventions at the top).
  *
  * Errors: B < 0 or Bd < 0 -> GQA_ERR_BAD_SHAPE; a NULL pointer of a part
  * that is present -> GQA_ERR_NULL_POINTER; otherwise each present part is

@@ -838,41 +838,67 @@ int decode_entry(const void* q, const void* kcache, const void* vcache, const in
 
 // ------------------------------------------------------------------ mixed batch
 
-// One launch over the chunk's units and the decode splits, one workgroup
-// per resident slot (fewer if there is less work), then the decode rows'
-// combine pass.  A chunk of few, long units (at most two 64-column units
-// per CU, each of >= 8 key tiles) runs as quad units, whose four groups
-// split each unit's keys; any other chunk as the persistent schedule's
-// 128-column units.  The decode splits are sized for eight decode waves per
-// CU when the chunk's units fill every resident workgroup (the splits then
-// run in the chunk's tail, where shorter ones end sooner), else for four,
-// as gqa_attn_decode sizes them (the splits run beside the units or alone,
-// where fewer, longer ones cost less: measured 31 against 47 us for the
-// LLaMA mixed batch's decode rows alone).
+// One launch over the chunk and the decode work, one workgroup per resident
+// slot (fewer if there is less work), then the merge passes.  The chunk runs
+// as a prefill call of its shape would run it:
+//  * quad units, whose four groups split each 64-column unit's keys, when
+//    that call would take them (few, long units);
+//  * else, with too few units to balance whole ones, the balanced
+//    schedule's pieces (equal key-tile chunks, cut units merged by the
+//    prefill merge pass), sized for 1 / kMixedChunkDiv of the resident
+//    workgroups, so the others start on the decode work at once instead of
+//    waiting for the chunk's few units to end;
+//  * else the persistent schedule's 128-column units.
+// The decode rows are split as gqa_attn_decode splits them (bf16: the same
+// parts, so the same records and bits) and taken by the workgroups that the
+// chunk leaves idle.
+#ifndef GQA_MIXED_CHUNK_DIV
+#define GQA_MIXED_CHUNK_DIV 2
+#endif
+constexpr int kMixedChunkDiv = GQA_MIXED_CHUNK_DIV;
 template <typename T, class C, class CD>
 int launch_mixed(gqa::MixedArgs& m, int dev_id, const DeviceInfo& dev, hipStream_t stream) {
   using CQ = gqa::TileCfg<T, C::D, C::BC, 2, C::KVS>;
-  bool quad = false;
+  enum { kPersistent, kQuad, kBalanced } kind = kPersistent;
   gqa::MixedArgs mq = m;
   if constexpr (8 * CQ::STAGE_BYTES <= kLdsBytes) {
-    if (m.p.T > 0) decompose(mq.p, 64);  // (no chunk: g = 0, nothing to decompose)
-    quad = m.p.T > 0 && mq.p.T <= 2LL * dev.cus && unit_tiles<CQ>(mq.p, true, 0) >= 8;
-  }
-  gqa::MixedArgs& a = quad ? mq : m;
-  const void* kern = nullptr;
-  int threads = C::NT, dw = gqa::mixed_decode_waves<C, CD>();
-  if constexpr (8 * CQ::STAGE_BYTES <= kLdsBytes) {
-    if (quad) {
-      kern = reinterpret_cast<const void*>(&gqa::mixed_quad_kernel<T, CQ, CD>);
-      threads = 4 * CQ::NT;
-      dw = gqa::mixed_quad_decode_waves<CQ, CD>();
+    if (m.p.T > 0) {
+      decompose(mq.p, 64);
+      const long long t64 = mq.p.T;
+      if (m.p.T < dev.cus && 4 * t64 >= 3LL * dev.cus && t64 <= dev.cus &&
+          unit_tiles<CQ>(mq.p, true, 0) >= 8)
+        kind = kQuad;
     }
   }
-  if (!quad) kern = reinterpret_cast<const void*>(&gqa::mixed_kernel<T, C, CD>);
+  long long cuts = 0;
+  const void* bal_kern = reinterpret_cast<const void*>(&gqa::mixed_balanced_kernel<T, C, CD>);
+  if (kind != kQuad && m.p.T > 0) {
+    const long long chunk_slots =
+        std::max(1LL, (long long)dev.cus * occupancy(bal_kern, C::NT) / kMixedChunkDiv);
+    if (plan_balanced<C>(m.p, true, chunk_slots, &cuts)) kind = kBalanced;
+  }
+  gqa::MixedArgs& a = kind == kQuad ? mq : m;
+  const void* kern = nullptr;
+  int threads = C::NT;
+  if constexpr (8 * CQ::STAGE_BYTES <= kLdsBytes) {
+    if (kind == kQuad) {
+      kern = reinterpret_cast<const void*>(&gqa::mixed_quad_kernel<T, CQ, CD>);
+      threads = 4 * CQ::NT;
+    }
+  }
+  if (kind == kBalanced) kern = bal_kern;
+  if (kind == kPersistent) kern = reinterpret_cast<const void*>(&gqa::mixed_kernel<T, C, CD>);
   const long long slots = (long long)dev.cus * occupancy(kern, threads);
   constexpr bool REG = !std::is_same<T, float>::value;
-  if constexpr (REG)  // bf16: each group of W waves takes a decode part
+  int dw = 1;
+  if constexpr (REG) {  // bf16: each group of W waves takes a decode part
     dw = (threads / 64) / (m.d.g > 16 ? PartCfgOf<C::D, 2>::W : PartCfgOf<C::D, 1>::W);
+  } else {
+    dw = gqa::mixed_decode_waves<C, CD>();
+    if constexpr (8 * CQ::STAGE_BYTES <= kLdsBytes) {
+      if (kind == kQuad) dw = gqa::mixed_quad_decode_waves<CQ, CD>();
+    }
+  }
   if (a.d.B > 0) {
     if constexpr (REG) {
       // bf16: the parts of gqa_attn_decode (the same records, and outputs)
@@ -885,24 +911,40 @@ int launch_mixed(gqa::MixedArgs& m, int dev_id, const DeviceInfo& dev, hipStream
     if (nd > kIntMax / 2) return fail(GQA_ERR_BAD_SHAPE, "too many decode splits (%lld)", nd);
     a.nd = (int)nd;
   }
-  const long long work = (long long)a.p.T + ((long long)a.nd + dw - 1) / dw;
-  const long long grid = std::max<long long>(1, std::min<long long>(work, slots));
+  const long long pieces = kind == kBalanced ? (long long)a.p.nsl * a.p.Pp : 0;
+  const long long items = kind == kBalanced ? pieces : a.p.T;
+  const long long work = items + ((long long)a.nd + dw - 1) / dw;
+  const long long grid = std::max<long long>(
+      std::max<long long>(1, pieces), std::min<long long>(work, slots));
+  const size_t ws_bytes =
+      cuts > 0 ? (size_t)pieces * 2 * gqa::part_floats<C>() * sizeof(float) : 0;
   StreamState ss;
-  int st = stream_state(dev_id, stream, 0, &ss);
+  int st = stream_state(dev_id, stream, ws_bytes, &ss);
   if (st != GQA_OK) return st;
   a.p.ctr = ss.ctr;
   a.p.zero = 0;
+  a.p.ws = cuts > 0 ? ss.ws : nullptr;
   (void)hipGetLastError();  // a stale error belongs to an earlier call
   if constexpr (8 * CQ::STAGE_BYTES <= kLdsBytes) {
-    if (quad)
+    if (kind == kQuad)
       hipLaunchKernelGGL((gqa::mixed_quad_kernel<T, CQ, CD>), dim3((unsigned)grid),
                          dim3(4 * CQ::NT), 0, stream, a);
   }
-  if (!quad)
+  if (kind == kBalanced)
+    hipLaunchKernelGGL((gqa::mixed_balanced_kernel<T, C, CD>), dim3((unsigned)grid), dim3(C::NT),
+                       0, stream, a);
+  if (kind == kPersistent)
     hipLaunchKernelGGL((gqa::mixed_kernel<T, C, CD>), dim3((unsigned)grid), dim3(C::NT), 0,
                        stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "mixed kernel launch");
+  if (cuts > 0) {
+    hipLaunchKernelGGL((gqa::prefill_merge_kernel<T, C, true>),
+                       dim3((unsigned)(a.p.nsl * (a.p.Pp - 1) * C::NW)), dim3(64 * C::DB), 0,
+                       stream, a.p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "prefill merge kernel launch");
+  }
   if (a.nd > 0) {
     if constexpr (REG)
       hipLaunchKernelGGL((gqa::decode_merge_kernel<C::D, false>),

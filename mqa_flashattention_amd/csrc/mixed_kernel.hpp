@@ -17,18 +17,20 @@
 // this kernel.
 //
 // Prefill and decode waves never share a CU: the prefill units use the
-// whole register budget of two waves per SIMD.  On the LLaMA-3-8B batches
-// measured, this launch runs at the speed of a prefill call followed by a
-// decode call (512-query chunk) or 4 % slower (128-query chunk, whose 64
-// units leave the chunk on 64 CUs).
+// whole register budget of two waves per SIMD.
 //
-// Two prefill unit shapes, as for a prefill launch:
+// Three prefill shapes, as a prefill launch of the chunk would choose:
 //  * mixed_kernel: 4-wave workgroups on 128-column units from the XCD
 //    queues of the persistent schedule, for chunks with many units;
 //  * mixed_quad_kernel: 8-wave workgroups on 64-column units whose keys
 //    four 2-wave groups split (the quad schedule), for chunks with few,
 //    long units -- a long chunk over a long prompt, where one wave walking
-//    all of a unit's keys would be the critical path.
+//    all of a unit's keys would be the critical path;
+//  * mixed_balanced_kernel: the balanced schedule's equal chunks of key
+//    tiles on part of the workgroups, for chunks with too few units to
+//    balance whole ones (a short chunk over a long prompt, whose few units
+//    would otherwise hold the launch while most CUs sit idle); the cut
+//    units' partial states are merged after the launch.
 #pragma once
 
 #include <type_traits>
@@ -182,6 +184,24 @@ mixed_kernel(MixedArgs m) {
 
   mixed_decode_phase<T, CD, DW, C::NW>(m, smem, &s_unit);
   leave_persistent(a, kMixedDecodeCounter);
+}
+
+// Causal chunk pieces of the balanced schedule (config C: workgroup g <
+// nsl * Pp runs piece g, as prefill_balanced_kernel does), then decode work.
+// The host sizes Pp for part of the resident workgroups, so the others start
+// on the decode parts at once; the pieces' partial records are merged by
+// the prefill merge pass after this kernel.
+template <typename T, class C, class CD>
+__global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+mixed_balanced_kernel(MixedArgs m) {
+  constexpr int DW = mixed_decode_waves<C, CD>();
+  __shared__ __attribute__((aligned(16))) char smem[mixed_lds_bytes<C, CD>()];
+  static_assert(C::NW * stage_out_bytes<C>() <= 2 * C::STAGE_BYTES, "output staging too large");
+  static_assert(C::D == CD::D, "one head dim for both parts");
+  __shared__ int s_take;
+  if ((int)blockIdx.x < m.p.nsl * m.p.Pp) balanced_chunk<T, C, true>(m.p, smem, blockIdx.x);
+  mixed_decode_phase<T, CD, DW, C::NW>(m, smem, &s_take);
+  leave_persistent(m.p, kMixedDecodeCounter);
 }
 
 // Decode waves of a mixed_quad_kernel workgroup (8 waves, the quad

@@ -601,23 +601,19 @@ prefill_varlen_kernel(PrefillArgs a) {
   leave_persistent(a, kNumQueues);
 }
 
-// Workgroup g = c * nsl + s runs chunk c of slice s, so the workgroups of a
+// Chunk c of slice s for workgroup g = c * nsl + s, so the workgroups of a
 // slice share an XCD whenever nsl is a multiple of kNumQueues.  Segments
 // that cover a whole unit store the result; a cut unit's first segment in
 // the chunk goes to record slot 0 and its last to slot 1 (a segment that is
-// not the chunk's first always reaches the chunk's end).
+// not the chunk's first always reaches the chunk's end).  All threads of
+// the workgroup call it; the LDS ring is free on return.
 template <typename T, class C, bool CAUSAL>
-__global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
-prefill_balanced_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
-  static_assert(C::NW * stage_out_bytes<C>() <= 2 * C::STAGE_BYTES, "output staging too large");
-
+__device__ __forceinline__ void balanced_chunk(const PrefillArgs& a, char* smem, int g) {
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int j = lane & 31;
 
-  const int g = blockIdx.x;
   const int s = g % a.nsl;
   const int c = g / a.nsl;
   const int hb = s % a.HB;
@@ -649,6 +645,15 @@ prefill_balanced_kernel(PrefillArgs a) {
     pre += n;
     ++pos;
   }
+}
+
+// The balanced schedule: one chunk per workgroup.
+template <typename T, class C, bool CAUSAL>
+__global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+prefill_balanced_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+  static_assert(C::NW * stage_out_bytes<C>() <= 2 * C::STAGE_BYTES, "output staging too large");
+  balanced_chunk<T, C, CAUSAL>(a, smem, blockIdx.x);
 }
 
 // Causal launches with about one unit pair per resident workgroup: workgroup

@@ -5,12 +5,16 @@ q_offset + i) and decode rows of the same layer; both outputs are compared
 element by element with oracle.attn_mixed on the same inputs.  Bar: the
 forward's, max |O_gpu - O_oracle| <= 1e-4 for fp32 and <= 2e-2 for bf16.
 Cases span every head dim, MHA / GQA / MQA and groups wider than one column
-block, both prefill unit shapes (128-column persistent units; quad units
-for chunks of few long units), ragged chunk and cache lengths (empty, one
-slot, full capacity), a missing part, the LLaMA-3-8B mixed workload at full
-size, the decode rows' agreement with gqa_attn_decode (bitwise where they
-use its splits) and the quad chunk's bitwise identity with gqa_attn_fwd, determinism, and back-to-back calls of different
-sizes sharing one stream's scheduler counters.
+block, the three chunk schedules (the balanced schedule's key-tile chunks
+with cut units merged after the launch, for chunks of few units -- every
+small case; quad units for chunks of few long units, as a prefill call of
+that shape takes them; 128-column persistent units for chunks of many
+units), ragged chunk and cache lengths (empty, one slot, full capacity), a
+missing part, both LLaMA-3-8B mixed workloads at full size, the decode
+rows' agreement with gqa_attn_decode (bitwise where they use its splits)
+and the quad chunk's bitwise identity with gqa_attn_fwd, determinism, and
+back-to-back calls of different sizes sharing one stream's scheduler
+counters.
 """
 from __future__ import annotations
 
@@ -64,10 +68,12 @@ SMALL = [
     _pair(1, 8, 1, 33, 33, 0, 6, 257, 200, 257, 128, torch.bfloat16),       # MQA, prompt start
     _pair(2, 4, 4, 64, 96, 32, 2, 96, 90, 96, 128, torch.float32),          # MHA
     _pair(1, 40, 1, 20, 90, 70, 3, 300, 1, 300, 32, torch.bfloat16),        # g = 40: 2 blocks
-    # chunks of few long units: quad units (keys split four ways)
+    # chunks of few long units: balanced pieces, every unit cut
     _pair(3, 16, 4, 127, 1000, 873, 9, 1000, 1, 1000, 64, torch.float32),
     _pair(1, 16, 2, 128, 1024, 896, 4, 1024, 1, 1024, 64, torch.bfloat16),  # group of 8
     _pair(2, 4, 1, 64, 800, 736, 3, 800, 1, 800, 32, torch.bfloat16),
+    # 192 64-column units of >= 8 key tiles: quad units, as a prefill call takes them
+    _pair(1, 16, 4, 768, 1536, 768, 5, 1536, 1, 1536, 64, torch.bfloat16),
 ]
 
 
@@ -117,6 +123,20 @@ def test_llama3_8b_mixed_full():
     """The LLaMA-3-8B mixed workload at full size, every output element."""
     w = WORKLOADS["llama3_8b_mixed"]
     _run(w.fwd[0], w.decode, seed=0)
+
+
+def test_llama3_8b_mixed_c128_full():
+    """The 128-query mixed workload at full size (balanced pieces on half the
+    workgroups, every unit cut), every output element."""
+    w = WORKLOADS["llama3_8b_mixed_c128"]
+    _run(w.fwd[0], w.decode, seed=1)
+
+
+def test_mixed_many_units_persistent():
+    """A chunk of 640 128-column units (more than the balanced schedule takes):
+    the persistent units, then the decode parts."""
+    c, r = _pair(1, 32, 8, 2560, 3072, 512, 4, 1024, 1, 1024, 128, torch.bfloat16)
+    _run(c, r, seed=5)
 
 
 def test_mixed_decode_rows_match_decode():
