@@ -397,9 +397,9 @@ def test_key_split_parity_and_determinism(s):
 
 def test_key_split_workspace_regrows_between_sizes():
     """Launches with cut units, of growing and shrinking sizes, on one stream."""
-    shapes = [FwdShape(1, 4, 1, 32, 600, 64, False, 0),
+    shapes = [FwdShape(1, 4, 1, 32, 2000, 64, False, 0),
               FwdShape(1, 8, 1, 128, 8192, 128, False, 0),
-              FwdShape(1, 4, 1, 32, 600, 64, False, 0)]
+              FwdShape(1, 4, 1, 32, 2000, 64, False, 0)]
     for n, s in enumerate(shapes):
         _check_fwd(s, 40 + n)
 
