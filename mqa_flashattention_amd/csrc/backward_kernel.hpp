@@ -25,9 +25,11 @@
 //    accumulates dV^T += dO^T P and dK^T += Q^T dS.  The query steps of a
 //    key block are cut into up to kBwdQuerySplitMax parts, one workgroup
 //    each, whose fp32 results bwd_merge_kernel adds in part order.
-// In both, a staged tile occupies two LDS stages: one holds the first
-// operand row-major (the A operand of S or S^T) with the second transposed,
-// the other the second operand row-major with the first transposed.
+// Each staged tile is loaded from global memory once and written to LDS
+// row-major (the A operand of S or S^T, or of dP) and transposed (the A
+// operand of the contraction over its rows).  Where two such buffers fit
+// (bf16), the next tile is written to the other one while this one is
+// used, one barrier per step.
 #pragma once
 
 #include "prefill_kernel.hpp"
@@ -54,6 +56,114 @@ struct BwdArgs {
 // fill the CUs; bwd_merge_kernel adds the parts' dK, dV in part order.
 // With one part the kernel writes dK, dV itself.
 constexpr int kBwdQuerySplitMax = 8;
+
+// LDS buffers of staged tiles in the backward kernels: two (tile t + 1
+// written while tile t is used) when they fit in half of a CU's LDS, so
+// that two workgroups still share a CU; else one, written between two
+// barriers.
+template <class C>
+constexpr int bwd_buffers() {
+  return 4 * C::STAGE_BYTES <= 80 * 1024 ? 2 : 1;
+}
+
+// The rows of one staged tile (keys or queries key0 .. key0 + BC - 1 of one
+// head) in registers, loaded once and written to LDS twice: row-major (the
+// A operand of a score MFMA) and transposed (the A operand of a product
+// over these rows).  The thread's 16-byte chunks follow the transposed
+// store's pattern (store_tile's V part: VK consecutive rows of one column
+// chunk; fp32: the row-major pattern, whose V layout is row-major too).
+template <class C>
+struct RowRegs {
+  u32x4 c[C::V_LOADS];
+};
+
+template <class C>
+__device__ __forceinline__ bool rowreg_valid(int tid, int i) {
+  if constexpr (C::F32)
+    return C::K_CHUNKS % C::NT == 0 || tid + i * C::NT < C::K_CHUNKS;
+  else
+    return C::V_BLOCKS % C::NT == 0 || tid + (i / C::VK) * C::NT < C::V_BLOCKS;
+}
+
+// Row and 16-byte column chunk of the thread's chunk i.
+template <class C>
+__device__ __forceinline__ void rowreg_pos(int tid, int i, int& row, int& col) {
+  if constexpr (C::F32) {
+    const int id = tid + i * C::NT;
+    row = id / C::ROW_CHUNKS;
+    col = id % C::ROW_CHUNKS;
+  } else {
+    const int id = tid + (i / C::VK) * C::NT;
+    row = (id % C::KGROUPS) * C::VK + i % C::VK;
+    col = id / C::KGROUPS;
+  }
+}
+
+// Issue the loads of rows key0 .. key0 + BC - 1 below nrows of the head at
+// base (rows rowb bytes apart when C::KVS, else D elements), through a
+// buffer resource over the existing rows: rows past nrows read as zeros
+// (load_tile's resource).
+template <typename T, class C>
+__device__ __forceinline__ void load_rows(RowRegs<C>& r, const T* __restrict__ base, int key0,
+                                          int nrows, int tid, int rowb) {
+  const int ROWB = C::KVS ? rowb : C::D * C::ESZ;
+  const int rows = nrows - key0 < C::BC ? (nrows - key0 > 0 ? nrows - key0 : 0) : C::BC;
+  const uint64_t off = (uint64_t)(uint32_t)key0 * (uint32_t)ROWB;
+  const int span = rows > 0 ? (rows - 1) * ROWB + C::D * C::ESZ : 0;
+  const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)span);
+  const auto rs = buffer_rsrc(reinterpret_cast<const char*>(base) + off, bytes);
+#pragma unroll
+  for (int i = 0; i < C::V_LOADS; ++i) {
+    if (rowreg_valid<C>(tid, i)) {
+      int row, col;
+      rowreg_pos<C>(tid, i, row, col);
+      r.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, row * ROWB + col * 16, 0, 0);
+    }
+  }
+}
+
+// Row-major copy (stride KSTR), as store_tile writes K.
+template <typename T, class C>
+__device__ __forceinline__ void store_rows(const RowRegs<C>& r, T* __restrict__ Ks, int tid) {
+#pragma unroll
+  for (int i = 0; i < C::V_LOADS; ++i) {
+    if (rowreg_valid<C>(tid, i)) {
+      int row, col;
+      rowreg_pos<C>(tid, i, row, col);
+      *reinterpret_cast<u32x4*>(Ks + row * C::KSTR + col * C::EPC) = r.c[i];
+    }
+  }
+}
+
+// The copy store_tile writes for V: transposed (bf16) or row-major with
+// stride VSTR (fp32).
+template <typename T, class C>
+__device__ __forceinline__ void store_rows_t(const RowRegs<C>& r, T* __restrict__ Vs, int tid) {
+  if constexpr (C::F32) {
+#pragma unroll
+    for (int i = 0; i < C::V_LOADS; ++i) {
+      if (rowreg_valid<C>(tid, i)) {
+        int row, col;
+        rowreg_pos<C>(tid, i, row, col);
+        *reinterpret_cast<u32x4*>(Vs + row * C::VSTR + col * C::EPC) = r.c[i];
+      }
+    }
+  } else {
+    using Run = VRun<C::VK>;
+#pragma unroll
+    for (int n = 0; n < C::V_PER_T; ++n) {
+      const int id = tid + n * C::NT;
+      if (C::V_BLOCKS % C::NT == 0 || id < C::V_BLOCKS) {
+        const int kg = id % C::KGROUPS;
+        const int dc = id / C::KGROUPS;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<typename Run::type*>(Vs + (dc * 8 + i) * C::VSTR + kg * C::VK) =
+              Run::get(&r.c[n * C::VK], i);
+      }
+    }
+  }
+}
 
 // Sum over this lane's elements of x * y (two B-operand fragments of one
 // column); the other half-wave holds the rest of the row.
@@ -104,11 +214,14 @@ template <typename T, class C, bool CAUSAL>
 __global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(BwdArgs ba) {
   const PrefillArgs& a = ba.f;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
-  T* const KsA = reinterpret_cast<T*>(smem);  // K row-major (V transposed, unused)
-  T* const VsA = KsA + C::K_ELEMS;
-  T* const KsB = reinterpret_cast<T*>(smem + C::STAGE_BYTES);  // V row-major
-  T* const VsB = KsB + C::K_ELEMS;                             // K transposed
+  // buffers of staged key tiles, used in turn: buffer sg holds K row-major,
+  // V row-major and K transposed (as store_tile lays them out)
+  constexpr int BUF = (2 * C::K_ELEMS + C::V_ELEMS) * C::ESZ;
+  constexpr int NBUF = 2 * BUF <= 80 * 1024 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * BUF];
+  auto Krow = [&](int sg) { return reinterpret_cast<T*>(smem + sg * BUF); };
+  auto Vrow = [&](int sg) { return Krow(sg) + C::K_ELEMS; };
+  auto Kt = [&](int sg) { return Krow(sg) + 2 * C::K_ELEMS; };
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -145,25 +258,26 @@ bwd_dq_kernel(BwdArgs ba) {
   // accumulated with the forward's online softmax: weights against a running
   // reference m, raised lazily (acc and l rescaled), divided by l at the end,
   // where lse = m c + log2 l also falls out for the dK/dV kernel.
-  TileRegs<C> ra, rb;
+  RowRegs<C> rk, rv;  // K and V rows of the next tile
   f32x16 acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
   float m = kNegInf, l = 0.f;
-  load_tile<T, C>(ra, kbase, vbase, 0, a.Nk, tid, a.kv_rowb);
-  load_tile<T, C>(rb, vbase, kbase, 0, a.Nk, tid, a.kv_rowb);
+  load_rows<T, C>(rk, kbase, 0, a.Nk, tid, a.kv_rowb);
+  load_rows<T, C>(rv, vbase, 0, a.Nk, tid, a.kv_rowb);
+  store_rows<T, C>(rk, Krow(0), tid);
+  store_rows<T, C>(rv, Vrow(0), tid);
+  store_rows_t<T, C>(rk, Kt(0), tid);
+  __syncthreads();
   for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();
-    store_tile<T, C>(ra, KsA, VsA, tid);
-    store_tile<T, C>(rb, KsB, VsB, tid);
-    __syncthreads();
+    const int cur = kt % NBUF;
     if (kt + 1 < ntiles) {
-      load_tile<T, C>(ra, kbase, vbase, (kt + 1) * C::BC, a.Nk, tid, a.kv_rowb);
-      load_tile<T, C>(rb, vbase, kbase, (kt + 1) * C::BC, a.Nk, tid, a.kv_rowb);
+      load_rows<T, C>(rk, kbase, (kt + 1) * C::BC, a.Nk, tid, a.kv_rowb);
+      load_rows<T, C>(rv, vbase, (kt + 1) * C::BC, a.Nk, tid, a.kv_rowb);
     }
     f32x16 s[C::KB], dp[C::KB];
-    qk_tile<T, C>(s, qf, KsA, j, h2);    // S^T = K Q^T
-    qk_tile<T, C>(dp, dof, KsB, j, h2);  // dP^T = V dO^T
+    qk_tile<T, C>(s, qf, Krow(cur), j, h2);    // S^T = K Q^T
+    qk_tile<T, C>(dp, dof, Vrow(cur), j, h2);  // dP^T = V dO^T
     const int key0 = kt * C::BC;
     if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
     // key 0 is visible to every row, so the first tile raises m in every lane
@@ -180,7 +294,17 @@ bwd_dq_kernel(BwdArgs ba) {
       }
     typename C::Frag dsf[C::KB][C::PF];
     to_frag<C>(s, dsf);
-    pv_tile<T, C>(acc, dsf, VsB, j, h2);  // dQ^T += K^T dS^T (unnormalised)
+    pv_tile<T, C>(acc, dsf, Kt(cur), j, h2);  // dQ^T += K^T dS^T (unnormalised)
+    if (kt + 1 < ntiles) {
+      // with two buffers the other one was last read in step kt - 1, before
+      // the barrier that ended it; with one, wait for every wave here
+      if (NBUF == 1) __syncthreads();
+      const int nxt = (cur + 1) % NBUF;
+      store_rows<T, C>(rk, Krow(nxt), tid);
+      store_rows<T, C>(rv, Vrow(nxt), tid);
+      store_rows_t<T, C>(rk, Kt(nxt), tid);
+    }
+    __syncthreads();
   }
   const float lsum = halves_sum(l);
   const float lse = m * c + log2f(lsum);
@@ -198,15 +322,20 @@ bwd_dq_kernel(BwdArgs ba) {
 // grid (ceil(Nk / (32 NW)) * qsplit, Hkv, B), C::NT threads: wave
 // w owns keys k0 + 32 w .. k0 + 32 w + 31 of K/V head (b, hkv), over part
 // `part` of the block's query steps; it writes fp32 partial dK (scaled) and
-// dV to the part's records.
+// dV to the part's records.  With two LDS buffers the staged query tiles
+// alternate: tile st + 1 is written while tile st is used, so the LDS
+// writes (and their wait for the tile's global loads) leave the critical
+// path and one barrier per step remains.
 template <typename T, class C, bool CAUSAL>
 __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
   const PrefillArgs& a = ba.f;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
-  T* const KsA = reinterpret_cast<T*>(smem);  // Q row-major
-  T* const VsA = KsA + C::K_ELEMS;            // dO transposed
-  T* const KsB = reinterpret_cast<T*>(smem + C::STAGE_BYTES);  // dO row-major
-  T* const VsB = KsB + C::K_ELEMS;                             // Q transposed
+  constexpr int NBUF = bwd_buffers<C>();
+  __shared__ __attribute__((aligned(16))) char smem[2 * NBUF * C::STAGE_BYTES];
+  // buffer sg: Q row-major + dO transposed, then dO row-major + Q transposed
+  auto KsA = [&](int sg) { return reinterpret_cast<T*>(smem + 2 * sg * C::STAGE_BYTES); };
+  auto VsA = [&](int sg) { return KsA(sg) + C::K_ELEMS; };
+  auto KsB = [&](int sg) { return reinterpret_cast<T*>(smem + (2 * sg + 1) * C::STAGE_BYTES); };
+  auto VsB = [&](int sg) { return KsB(sg) + C::K_ELEMS; };
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -241,7 +370,7 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
     acc_dk[db] = f32x16{};
     acc_dv[db] = f32x16{};
   }
-  TileRegs<C> ra, rb;
+  RowRegs<C> rq, rdo;  // Q and dO rows of the next tile
   // row statistics of a tile, per accumulator register: register r of
   // block kb is query row 32 kb + key_of_reg(r, h2), i.e. runs of 8
   // consecutive rows -- two 16-byte loads per run, through a resource over
@@ -258,8 +387,8 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
     const size_t hoff = (size_t)(b * a.Hq + tile_head(st)) * a.Nq * C::D;
     const T* qbase = uniform_ptr(reinterpret_cast<const T*>(a.q) + hoff);
     const T* dobase = uniform_ptr(reinterpret_cast<const T*>(ba.dout) + hoff);
-    load_tile<T, C>(ra, qbase, dobase, tile_i0(st), a.Nq, tid, rowb);
-    load_tile<T, C>(rb, dobase, qbase, tile_i0(st), a.Nq, tid, rowb);
+    load_rows<T, C>(rq, qbase, tile_i0(st), a.Nq, tid, rowb);
+    load_rows<T, C>(rdo, dobase, tile_i0(st), a.Nq, tid, rowb);
     const uint32_t srow = (uint32_t)((size_t)(b * a.Hq + tile_head(st)) * a.Nq + tile_i0(st));
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -274,12 +403,16 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
             float4, __builtin_amdgcn_raw_buffer_load_b128(stats, (int)(off + dd_off), 0, 0));
       }
   };
-  if (nsteps > 0) issue(0);
+  if (nsteps > 0) {
+    issue(0);
+    store_rows<T, C>(rq, KsA(0), tid);
+    store_rows_t<T, C>(rdo, VsA(0), tid);
+    store_rows<T, C>(rdo, KsB(0), tid);
+    store_rows_t<T, C>(rq, VsB(0), tid);
+    __syncthreads();
+  }
   for (int st = 0; st < nsteps; ++st) {
-    __syncthreads();
-    store_tile<T, C>(ra, KsA, VsA, tid);
-    store_tile<T, C>(rb, KsB, VsB, tid);
-    __syncthreads();
+    const int cur = st % NBUF;
     const int i0 = tile_i0(st);
     float lse_r[C::KB][16], dd_r[C::KB][16];
 #pragma unroll
@@ -297,8 +430,8 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
       }
     if (st + 1 < nsteps) issue(st + 1);
     f32x16 s[C::KB], dp[C::KB];
-    qk_tile<T, C>(s, kf, KsA, j, h2);   // S = Q K^T
-    qk_tile<T, C>(dp, vf, KsB, j, h2);  // dP = dO V^T
+    qk_tile<T, C>(s, kf, KsA(cur), j, h2);   // S = Q K^T
+    qk_tile<T, C>(dp, vf, KsB(cur), j, h2);  // dP = dO V^T
     // every row of the tile exists and sees every key of this wave: no
     // per-element test (wave-uniform)
     const bool whole = i0 + C::BC <= a.Nq && (!CAUSAL || k0 + 32 * w + 31 <= a.q_offset + i0);
@@ -328,8 +461,19 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
     typename C::Frag pf[C::KB][C::PF], dsf[C::KB][C::PF];
     to_frag<C>(s, pf);
     to_frag<C>(dp, dsf);
-    pv_tile<T, C>(acc_dv, pf, VsA, j, h2);   // dV^T += dO^T P
-    pv_tile<T, C>(acc_dk, dsf, VsB, j, h2);  // dK^T += Q^T dS
+    pv_tile<T, C>(acc_dv, pf, VsA(cur), j, h2);   // dV^T += dO^T P
+    pv_tile<T, C>(acc_dk, dsf, VsB(cur), j, h2);  // dK^T += Q^T dS
+    if (st + 1 < nsteps) {
+      // with two buffers the other one was last read in step st - 1, before
+      // the barrier that ended it; with one, wait for every wave here
+      if (NBUF == 1) __syncthreads();
+      const int nxt = (cur + 1) % NBUF;
+      store_rows<T, C>(rq, KsA(nxt), tid);
+      store_rows_t<T, C>(rdo, VsA(nxt), tid);
+      store_rows<T, C>(rdo, KsB(nxt), tid);
+      store_rows_t<T, C>(rq, VsB(nxt), tid);
+    }
+    __syncthreads();
   }
 
   if (kvalid && ba.qsplit == 1) {  // one part: the result itself
