@@ -825,8 +825,9 @@ def other_workloads(K):
             "chunk_gflop": round(prefill_flops(wm.fwd[0]) / 1e9, 4),
             "decode_mb": round(decode_bytes(wm.decode, lens_m) / 1e6, 4),
             "note": f"gqa_attn_mixed: the {wm.fwd[0].Nq}-query chunk and {wm.decode.B} decode "
-                    "rows in one persistent launch + the decode merge, against gqa_attn_fwd "
-                    "then gqa_attn_decode; decode caches HBM-cold"}
+                    "rows in one persistent launch + its merge launches (the chunk's cut "
+                    "units when it runs on the balanced schedule, the decode rows), against "
+                    "gqa_attn_fwd then gqa_attn_decode; decode caches HBM-cold"}
     ms, ms_sep, lens, err = time_varlen_workload(max(10, K // 2), 3)
     from mqa_flashattention_amd.workloads import VARLEN_PREFILL as vs
     tf = varlen_flops(lens, vs.Hq, vs.d) / (ms * 1e-3) / 1e12
