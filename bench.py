@@ -158,6 +158,41 @@ def time_fwd_workload(s, steps, warmup, bthd=False):
     return e0.elapsed_time(e1) / steps
 
 
+def time_persistent_causal(steps, warmup):
+    """The LLaMA-3-8B causal prefill layer at batch 4: 2048 units of 128
+    columns, more than two per resident workgroup, so the launch runs on the
+    persistent schedule (per-XCD atomic queues, heaviest position blocks
+    first, stealing).  A sample of rows is checked against the oracle first.
+    Returns (shape, event-timed average duration in ms)."""
+    import numpy as np
+    import torch
+
+    import oracle  # test infrastructure: parity gate only
+    from mqa_flashattention_amd import attn_fwd
+    from mqa_flashattention_amd.workloads import WORKLOADS, FwdShape, fwd_inputs
+    ps = WORKLOADS["llama3_8b_prefill"].fwd[0]
+    s = FwdShape(4, ps.Hq, ps.Hkv, ps.Nq, ps.Nk, ps.d, True, 0, ps.dtype)
+    host = fwd_inputs(s, 0)
+    q, k, v = (t.cuda() for t in host)
+    out = attn_fwd(q, k, v, causal=True, scale=s.scale)
+    torch.cuda.synchronize()
+    n = s.B * s.Hq * s.Nq
+    ids = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(6).integers(0, n, 62)]))
+    ref = oracle.attn_fwd_rows(host[0], host[1], host[2], ids, causal=True, scale=s.scale)
+    check(out.reshape(-1, s.d)[torch.from_numpy(ids).cuda()], ref, 2e-2,
+          "batch-4 LLaMA prefill (persistent schedule)")
+    for _ in range(warmup):
+        attn_fwd(q, k, v, causal=True, scale=s.scale, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        attn_fwd(q, k, v, causal=True, scale=s.scale, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    return s, e0.elapsed_time(e1) / steps
+
+
 def time_append_workload(s, steps, warmup):
     """Event-timed average duration (ms) of one gqa_attn_decode_append call,
     each call on a different one of DECODE_SETS cache pairs (HBM-cold), after
@@ -792,6 +827,14 @@ def other_workloads(K):
         "ms": round(ms, 5), "tflops": round(tf, 2),
         "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
         "note": "token-major [B, N, H, d] Q/K/V/O through gqa_attn_fwd_strided, no copies"}
+    s4, ms = time_persistent_causal(max(10, K // 4), 3)
+    tf = prefill_flops(s4) / (ms * 1e-3) / 1e12
+    extra["llama3_8b_prefill_b4[persistent]"] = {
+        "ms": round(ms, 5), "tflops": round(tf, 2),
+        "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+        "note": "the LLaMA-3-8B causal layer at batch 4 (2048 128-column units): the "
+                "persistent schedule's per-XCD atomic queues, heaviest first, with stealing; "
+                "sampled rows checked against the oracle"}
     sa = WORKLOADS["kv_decode_append_b8"].decode
     ms, positions = time_append_workload(sa, max(20, K), 5)
     gb = append_bytes(sa, positions) / (ms * 1e-3) / 1e9
