@@ -500,6 +500,220 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
   }
 }
 
+typedef float acc4 __attribute__((ext_vector_type(4)));
+
+// bf16 dK/dV on the 16x16x32 MFMA: 16 keys per wave, four waves (64 keys)
+// per workgroup, the same grid, query parts and records as bwd_dkdv_kernel.
+// Half the keys per wave halves the accumulators and the K/V fragments, so
+// two waves fit on each SIMD (the 32-key kernel holds one).  In one step a
+// wave forms, for a staged 32-query tile (C: its LDS layout, the 4-wave
+// staging of bwd_dkdv_kernel),
+//   S = Q K^T and dP = dO V^T: two 16-query blocks, A = Q (or dO) rows from
+//   LDS, B = the wave's K (or V) fragment in registers; MFMA row m of block
+//   qb reads query 8 (m / 4) + 4 qb + m % 4, so that lane (n, G) ends up
+//   with queries 8 G .. 8 G + 7 of its key n -- exactly the B operand the
+//   next products take (the row permutation of the decode part kernel);
+//   dV^T += dO^T P and dK^T += Q^T dS: D / 16 blocks of 16 head dims,
+//   A = dO^T (or Q^T) from the transposed LDS copy, B = P (or dS) from
+//   registers.
+template <class C, bool CAUSAL>
+__global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+bwd_dkdv16_kernel(BwdArgs ba) {
+  using T = uint16_t;
+  static_assert(!C::F32 && C::BC == 32 && C::NW == 4, "bf16, 32-query tiles, 4 waves");
+  constexpr int D = C::D;
+  constexpr int DT = D / 32;  // 32-deep steps of the score MFMAs
+  constexpr int DB = D / 16;  // 16-row blocks of dK^T and dV^T
+  const PrefillArgs& a = ba.f;
+  constexpr int NBUF = bwd_buffers<C>();
+  __shared__ __attribute__((aligned(16))) char smem[2 * NBUF * C::STAGE_BYTES];
+  // buffer sg: Q row-major + dO transposed, then dO row-major + Q transposed
+  auto KsA = [&](int sg) { return reinterpret_cast<T*>(smem + 2 * sg * C::STAGE_BYTES); };
+  auto VsA = [&](int sg) { return KsA(sg) + C::K_ELEMS; };
+  auto KsB = [&](int sg) { return reinterpret_cast<T*>(smem + (2 * sg + 1) * C::STAGE_BYTES); };
+  auto VsB = [&](int sg) { return KsB(sg) + C::K_ELEMS; };
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 15;  // the lane's key within the wave's 16
+  const int G = lane >> 4;  // the lane's group: queries 8 G .. 8 G + 7 of a tile
+
+  const int part = blockIdx.x % ba.qsplit;
+  const int k0 = (blockIdx.x / ba.qsplit) * 64;
+  const int hkv = blockIdx.y;
+  const int b = blockIdx.z;
+  const int key = k0 + 16 * w + n;
+  const bool kvalid = key < a.Nk;
+  const size_t key_row = ((size_t)(b * a.Hkv + hkv) * a.Nk + (kvalid ? key : 0)) * D;
+  bf16x8 kf[DT], vf[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.k) + key_row + 32 * t + 8 * G);
+    const u32x4 vw = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.v) + key_row + 32 * t + 8 * G);
+    kf[t] = __builtin_bit_cast(bf16x8, kvalid ? kw : zero);
+    vf[t] = __builtin_bit_cast(bf16x8, kvalid ? vw : zero);
+  }
+
+  const int first = CAUSAL ? max(0, k0 - a.q_offset) / C::BC : 0;
+  const int nqt = (a.Nq + C::BC - 1) / C::BC - first;  // >= 1 for launched blocks
+  const int nall = a.g * nqt;
+  const int per_part = (nall + ba.qsplit - 1) / ba.qsplit;
+  const int st0 = min(nall, part * per_part);
+  const int nsteps = max(0, min(nall, st0 + per_part) - st0);
+  const float c = a.c;
+  const int rowb = D * C::ESZ;
+
+  acc4 acc_dk[DB], acc_dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    acc_dk[db] = acc4{0.f, 0.f, 0.f, 0.f};
+    acc_dv[db] = acc4{0.f, 0.f, 0.f, 0.f};
+  }
+  RowRegs<C> rq, rdo;  // Q and dO rows of the next tile
+  // row statistics of the lane's 8 queries, through a resource over the
+  // whole statistics area (rows past Nq read the next head's values or
+  // zeros; they are excluded below whatever they read)
+  const auto stats = buffer_rsrc(
+      ba.lse, __builtin_amdgcn_readfirstlane((uint32_t)(2ull * a.B * a.Hq * a.Nq * 4)));
+  const uint32_t dd_off = (uint32_t)((size_t)a.B * a.Hq * a.Nq * 4);
+  float4 lse4[2], dd4[2];
+  auto tile_head = [&](int st) { return hkv * a.g + (st0 + st) / nqt; };
+  auto tile_i0 = [&](int st) { return (first + (st0 + st) % nqt) * C::BC; };
+  auto issue = [&](int st) {
+    const size_t hoff = (size_t)(b * a.Hq + tile_head(st)) * a.Nq * D;
+    const T* qbase = uniform_ptr(reinterpret_cast<const T*>(a.q) + hoff);
+    const T* dobase = uniform_ptr(reinterpret_cast<const T*>(ba.dout) + hoff);
+    load_rows<T, C>(rq, qbase, tile_i0(st), a.Nq, tid, rowb);
+    load_rows<T, C>(rdo, dobase, tile_i0(st), a.Nq, tid, rowb);
+    const uint32_t off =
+        4u * (uint32_t)((size_t)(b * a.Hq + tile_head(st)) * a.Nq + tile_i0(st) + 8 * G);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      lse4[h] = __builtin_bit_cast(
+          float4, __builtin_amdgcn_raw_buffer_load_b128(stats, (int)(off + 16 * h), 0, 0));
+      dd4[h] = __builtin_bit_cast(
+          float4, __builtin_amdgcn_raw_buffer_load_b128(stats, (int)(off + 16 * h + dd_off), 0, 0));
+    }
+  };
+  auto stage = [&](int sg) {
+    store_rows<T, C>(rq, KsA(sg), tid);
+    store_rows_t<T, C>(rdo, VsA(sg), tid);
+    store_rows<T, C>(rdo, KsB(sg), tid);
+    store_rows_t<T, C>(rq, VsB(sg), tid);
+  };
+  if (nsteps > 0) {
+    issue(0);
+    stage(0);
+    __syncthreads();
+  }
+  for (int st = 0; st < nsteps; ++st) {
+    const int cur = st % NBUF;
+    const int i0 = tile_i0(st);
+    float lse_r[8], dd_r[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      lse_r[4 * h] = lse4[h].x;
+      lse_r[4 * h + 1] = lse4[h].y;
+      lse_r[4 * h + 2] = lse4[h].z;
+      lse_r[4 * h + 3] = lse4[h].w;
+      dd_r[4 * h] = dd4[h].x;
+      dd_r[4 * h + 1] = dd4[h].y;
+      dd_r[4 * h + 2] = dd4[h].z;
+      dd_r[4 * h + 3] = dd4[h].w;
+    }
+    if (st + 1 < nsteps) issue(st + 1);
+    acc4 s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int row = 8 * (n >> 2) + 4 * qb + (n & 3);
+      const T* qr = KsA(cur) + row * C::KSTR + 8 * G;
+      const T* dr = KsB(cur) + row * C::KSTR + 8 * G;
+      bf16x8 qa[DT], da[DT];
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        qa[t] = *reinterpret_cast<const bf16x8*>(qr + 32 * t);
+        da[t] = *reinterpret_cast<const bf16x8*>(dr + 32 * t);
+      }
+      acc4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], kf[t], x, 0, 0, 0);  // S = Q K^T
+        y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[t], vf[t], y, 0, 0, 0);  // dP = dO V^T
+      }
+      s[qb] = x;
+      dp[qb] = y;
+    }
+    // element i of block qb: query 8 G + 4 qb + i, key n of the wave
+    const bool whole = i0 + C::BC <= a.Nq && (!CAUSAL || k0 + 16 * w + 15 <= a.q_offset + i0);
+    float p[8], ds[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sv = s[e >> 2][e & 3];
+      float pv = fast_exp2(__builtin_fmaf(sv, c, -lse_r[e]));
+      if (!whole) {
+        // rows past Nq (zero Q and dO) and, when causal, rows that cannot
+        // see this key weigh 0
+        const int qi = i0 + 8 * G + e;
+        const bool vis = qi < a.Nq && (!CAUSAL || key <= a.q_offset + qi);
+        pv = vis ? pv : 0.f;
+      }
+      p[e] = pv;
+      ds[e] = pv * (dp[e >> 2][e & 3] - dd_r[e]);
+    }
+    u32x4 pw, dw;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pw[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+      dw[e] = pack_bf16(ds[2 * e], ds[2 * e + 1]);
+    }
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+    const bf16x8 dsf = __builtin_bit_cast(bf16x8, dw);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const bf16x8 ao = *reinterpret_cast<const bf16x8*>(VsA(cur) + (16 * db + n) * C::VSTR + 8 * G);
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(VsB(cur) + (16 * db + n) * C::VSTR + 8 * G);
+      acc_dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, pf, acc_dv[db], 0, 0, 0);   // dV^T += dO^T P
+      acc_dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, dsf, acc_dk[db], 0, 0, 0);  // dK^T += Q^T dS
+    }
+    if (st + 1 < nsteps) {
+      // with two buffers the other one was last read in step st - 1, before
+      // the barrier that ended it; with one, wait for every wave here
+      if (NBUF == 1) __syncthreads();
+      stage((cur + 1) % NBUF);
+    }
+    __syncthreads();
+  }
+
+  // the lane holds head dims 16 db + 4 G .. + 3 of key n
+  if (kvalid && ba.qsplit == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d0 = 16 * db + 4 * G;
+      const acc4 k4 = acc_dk[db] * ba.scale;
+      const acc4 v4 = acc_dv[db];
+      *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(ba.dk) + key_row + d0) =
+          u32x2{pack_bf16(k4[0], k4[1]), pack_bf16(k4[2], k4[3])};
+      *reinterpret_cast<u32x2*>(reinterpret_cast<T*>(ba.dv) + key_row + d0) =
+          u32x2{pack_bf16(v4[0], v4[1]), pack_bf16(v4[2], v4[3])};
+    }
+  } else if (kvalid) {
+    // records [part][dK, dV][b][hkv][key][D], fp32
+    const size_t rows = (size_t)a.B * a.Hkv * a.Nk;
+    const size_t krow = (size_t)(b * a.Hkv + hkv) * a.Nk + key;
+    float* pk = ba.part + ((size_t)(2 * part) * rows + krow) * D;
+    float* pv = ba.part + ((size_t)(2 * part + 1) * rows + krow) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d0 = 16 * db + 4 * G;
+      const acc4 k4 = acc_dk[db] * ba.scale;
+      *reinterpret_cast<float4*>(pk + d0) = float4{k4[0], k4[1], k4[2], k4[3]};
+      *reinterpret_cast<float4*>(pv + d0) =
+          float4{acc_dv[db][0], acc_dv[db][1], acc_dv[db][2], acc_dv[db][3]};
+    }
+  }
+}
+
 // dK, dV = the sum of the query parts' records, in part order, rounded
 // once to the output type.  One thread per 4 consecutive elements of
 // dK or dV; n4 = 2 * B * Hkv * Nk * D / 4.

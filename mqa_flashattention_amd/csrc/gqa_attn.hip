@@ -1053,14 +1053,22 @@ int launch_bwd(gqa::BwdArgs& ba, hipStream_t stream) {
                      stream, ba);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "backward dQ kernel launch");
-  // dK/dV: 64 keys (two waves) per workgroup, so that the LLaMA-sized
-  // launches spread over every CU (its registers allow one wave per SIMD)
+  // dK/dV: 64 keys per workgroup, so that the LLaMA-sized launches spread
+  // over every CU: bf16 at d = 128 as four 16-key waves on the 16x16x32
+  // MFMA (two waves per SIMD), otherwise two 32-key waves (their registers
+  // allow one wave per SIMD)
   using CK = gqa::TileCfg<T, C::D, C::BC, 2>;
   const unsigned kblocks = (unsigned)((ba.f.Nk + 32 * CK::NW - 1) / (32 * CK::NW));
   ba.qsplit = bwd_query_parts(ba.f.B, ba.f.Hkv, ba.f.Nk);
-  hipLaunchKernelGGL((gqa::bwd_dkdv_kernel<T, CK, CAUSAL>),
-                     dim3(kblocks * (unsigned)ba.qsplit, (unsigned)ba.f.Hkv, (unsigned)ba.f.B),
-                     dim3(CK::NT), 0, stream, ba);
+  const dim3 kgrid(kblocks * (unsigned)ba.qsplit, (unsigned)ba.f.Hkv, (unsigned)ba.f.B);
+  if constexpr (std::is_same<T, uint16_t>::value && C::D == 128) {
+    using C16 = gqa::TileCfg<T, C::D, 32, 4>;
+    hipLaunchKernelGGL((gqa::bwd_dkdv16_kernel<C16, CAUSAL>), kgrid, dim3(C16::NT), 0, stream,
+                       ba);
+  } else {
+    hipLaunchKernelGGL((gqa::bwd_dkdv_kernel<T, CK, CAUSAL>), kgrid, dim3(CK::NT), 0, stream,
+                       ba);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "backward dK/dV kernel launch");
   if (ba.qsplit == 1) return GQA_OK;

@@ -85,10 +85,13 @@ def test_bwd_llama3_8b_shape_full():
     FwdShape(1, 16, 16, 2048, 2048, 64, True, 0),  # four query parts per key block
     FwdShape(2, 16, 16, 2048, 2048, 64, True, 0),  # two
     FwdShape(4, 16, 16, 2048, 2048, 64, True, 0),  # one: dK, dV written directly
-], ids=["four_parts", "two_parts", "one_part"])
+    FwdShape(1, 16, 16, 2048, 2048, 128, True, 0),  # d = 128: the 16-key dK/dV kernel
+    FwdShape(4, 16, 16, 2048, 2048, 128, True, 0),  # d = 128, one part
+], ids=["four_parts", "two_parts", "one_part", "d128_four_parts", "d128_one_part"])
 def test_bwd_query_split_counts(s):
     """Launches large enough that each key block's query range is cut into
-    four or two parts, or not cut at all (the small shapes above use eight)."""
+    four or two parts, or not cut at all (the small shapes above use eight);
+    bf16 at d = 128 runs the 16-key dK/dV kernel, the others the 32-key one."""
     _check(s, seed=5)
 
 
