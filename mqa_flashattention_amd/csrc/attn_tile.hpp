@@ -179,10 +179,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uin
 // 16-byte chunks of a row, so a wave's load instruction covers whole rows.
 // rowb: bytes from one key row to the next, a multiple of 16; used only when
 // C::KVS (otherwise the rows are D * ESZ bytes apart).
-template <typename T, class C>
+// KPART false: V only (K staged another way; bf16).
+template <typename T, class C, bool KPART = true>
 __device__ __forceinline__ void load_tile(TileRegs<C>& r, const T* __restrict__ kbase,
                                           const T* __restrict__ vbase, int key0, int nkeys,
                                           int tid, int rowb) {
+  static_assert(KPART || !C::F32, "V-only staging is bf16");
   const int ROWB = C::KVS ? rowb : C::D * C::ESZ;
   const int rows = nkeys - key0 < C::BC ? (nkeys - key0 > 0 ? nkeys - key0 : 0) : C::BC;
   // unsigned 32 x 32 -> 64-bit byte offset: scalar multiplies (a signed
@@ -200,7 +202,7 @@ __device__ __forceinline__ void load_tile(TileRegs<C>& r, const T* __restrict__ 
   const auto krs = buffer_rsrc(reinterpret_cast<const char*>(kbase) + base, bytes);
   const auto vrs = buffer_rsrc(reinterpret_cast<const char*>(vbase) + base, bytes);
 #pragma unroll
-  for (int n = 0; n < C::K_PER_T; ++n) {
+  for (int n = 0; n < (KPART ? C::K_PER_T : 0); ++n) {
     const int id = tid + n * C::NT;
     if (C::K_CHUNKS % C::NT == 0 || id < C::K_CHUNKS) {
       const int row = id / C::ROW_CHUNKS;
@@ -270,11 +272,11 @@ struct VRun<1> {
 
 // Write a staged tile to LDS: K row-major; V row-major (fp32) or transposed
 // (bf16, V^T[d][key]).
-template <typename T, class C>
+template <typename T, class C, bool KPART = true>
 __device__ __forceinline__ void store_tile(const TileRegs<C>& r, T* __restrict__ Ks,
                                            T* __restrict__ Vs, int tid) {
 #pragma unroll
-  for (int n = 0; n < C::K_PER_T; ++n) {
+  for (int n = 0; n < (KPART ? C::K_PER_T : 0); ++n) {
     const int id = tid + n * C::NT;
     if (C::K_CHUNKS % C::NT == 0 || id < C::K_CHUNKS) {
       const int row = id / C::ROW_CHUNKS;
@@ -298,6 +300,75 @@ __device__ __forceinline__ void store_tile(const TileRegs<C>& r, T* __restrict__
               Run::get(&r.v[n * C::VK], i);
       }
     }
+  }
+}
+
+// ---- K staged by direct global -> LDS loads (bf16, D = 128, 32-key tiles).
+// A K slot holds the tile's rows unpadded, 256 bytes each, with row r's
+// 16-byte chunk c at chunk position c ^ (r % 16): a direct load writes the
+// 16-byte chunks of a wave's 64 lanes to 1 KiB of consecutive LDS (lane i
+// at byte 16 i), which leaves no room for padding, and the XOR keeps the
+// score MFMA's K fragment reads (rows k_row_perm(j), chunks 2 ks + h2)
+// spread over the banks as the padded layout does.
+template <class C>
+constexpr int dk_slot_bytes() {
+  return C::BC * C::D * 2;
+}
+
+__device__ __forceinline__ int dk_chunk_off(int row, int chunk) {
+  return row * 256 + ((chunk ^ (row & 15)) << 4);
+}
+
+// Per-lane byte offsets of k_direct's loads within a tile (rows rowb bytes
+// apart): wave w's instruction n fills rows 4 (n NW + w) .. + 3, lane i row
+// 4 (n NW + w) + i / 16 at chunk position i % 16.
+template <class C>
+struct KDirect {
+  int off[(C::BC / 4) / C::NW];
+};
+
+template <class C>
+__device__ __forceinline__ KDirect<C> k_direct_offsets(int tid, int rowb) {
+  const int ROWB = C::KVS ? rowb : 256;
+  const int w = tid >> 6;
+  const int i = tid & 63;
+  KDirect<C> kd;
+#pragma unroll
+  for (int n = 0; n < (C::BC / 4) / C::NW; ++n) {
+    const int r = 4 * (n * C::NW + w) + (i >> 4);
+    kd.off[n] = r * ROWB + (((i & 15) ^ (r & 15)) << 4);
+  }
+  return kd;
+}
+
+// Issue the direct loads of tile rows key0 .. key0 + 31 (below nkeys; rows
+// past it are written as zeros) into slot Kd.  They complete in issue order
+// with the wave's other vector-memory loads (one counter).
+template <class C>
+__device__ __forceinline__ void k_direct(const void* kbase, int key0, int nkeys, char* Kd, int tid,
+                                         int rowb, const KDirect<C>& kd) {
+  static_assert(!C::F32 && C::D == 128 && C::BC == 32, "direct K: bf16, d = 128, 32-key tiles");
+  const int ROWB = C::KVS ? rowb : 256;
+  const int rows = nkeys - key0 < C::BC ? (nkeys - key0 > 0 ? nkeys - key0 : 0) : C::BC;
+  const uint64_t base = (uint64_t)(uint32_t)key0 * (uint32_t)ROWB;
+  const int span = rows > 0 ? (rows - 1) * ROWB + 256 : 0;
+  const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)span);
+  const auto rs = buffer_rsrc(reinterpret_cast<const char*>(kbase) + base, bytes);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+  for (int n = 0; n < (C::BC / 4) / C::NW; ++n)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(Kd + (n * C::NW + w) * 1024), 16, kd.off[n],
+        0, 0, 0);
+}
+
+// The K chunks of a register-staged tile (load_tile's pattern) into slot Kd.
+template <class C>
+__device__ __forceinline__ void store_k_direct_layout(const TileRegs<C>& r, char* Kd, int tid) {
+#pragma unroll
+  for (int n = 0; n < C::K_PER_T; ++n) {
+    const int id = tid + n * C::NT;
+    *reinterpret_cast<u32x4*>(Kd + dk_chunk_off(id / C::ROW_CHUNKS, id % C::ROW_CHUNKS)) = r.k[n];
   }
 }
 
@@ -350,6 +421,23 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const typename C::Fr
     }
     s[kb] = a;
   }
+}
+
+// qk_tile over a K slot in the direct-load layout.
+template <class C>
+__device__ __forceinline__ void qk_tile_direct(f32x16 (&s)[C::KB], const bf16x8 (&qf)[C::QF],
+                                               const char* __restrict__ Kd, int lane32, int h2) {
+  const int rr = k_row_perm(lane32);
+  bf16x8 kf[C::QF];
+#pragma unroll
+  for (int ks = 0; ks < C::QF; ++ks)
+    kf[ks] = *reinterpret_cast<const bf16x8*>(Kd + dk_chunk_off(rr, 2 * ks + h2));
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 a = {};
+#pragma unroll
+  for (int ks = 0; ks < C::QF; ++ks)
+    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], a, 0, 0, 0);
+  s[0] = a;
 }
 
 // ---- online softmax, one tile at a time (composed in softmax_pv_step).

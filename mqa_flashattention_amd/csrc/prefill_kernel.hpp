@@ -223,7 +223,9 @@ __device__ __forceinline__ void kv_bases(const PrefillArgs& a, int b, int hkv, c
   vbase = uniform_ptr(reinterpret_cast<const T*>(a.v) + kv_off);
 }
 
-template <typename T, class C>
+// K1 false: tile 1's K rows are not loaded (seg_run_direct loads them
+// straight into LDS).
+template <typename T, class C, bool K1 = true>
 __device__ __forceinline__ void seg_begin(const PrefillArgs& a, SegIn<C>& in, int b, int hkv,
                                           const SegTiles& st, const Column& col) {
   const int tid = threadIdx.x % C::NT;  // index within the loading group
@@ -234,7 +236,7 @@ __device__ __forceinline__ void seg_begin(const PrefillArgs& a, SegIn<C>& in, in
   load_q_frag<T, C>(in.qf, reinterpret_cast<const T*>(a.q) + col.row_off, col.valid,
                     a.negate_q != 0, h2);
   load_tile<T, C>(in.ra, kbase, vbase, st.at(0) * C::BC, a.Nk, tid, a.kv_rowb);
-  load_tile<T, C>(in.rb, kbase, vbase, st.at(1) * C::BC, a.Nk, tid, a.kv_rowb);
+  load_tile<T, C, K1>(in.rb, kbase, vbase, st.at(1) * C::BC, a.Nk, tid, a.kv_rowb);
 }
 
 // Runs key tiles st of unit (b, hkv, ., qb) for the lane's column col, from
@@ -308,6 +310,89 @@ __device__ __forceinline__ void seg_run(const PrefillArgs& a, char* smem, SegIn<
     step(in.ra, in.rb, kt);
     if (kt + 1 < steps) step(in.rb, in.ra, kt + 1);
   }
+}
+
+// Whether the pair kernel stages K by direct global -> LDS loads (bf16,
+// d = 128, 32-key tiles) instead of through registers.
+template <class C>
+constexpr bool pair_direct_k() {
+  return !C::F32 && C::D == 128 && C::BC == 32;
+}
+
+// LDS ring of seg_run_direct: two K slots (direct-load layout), then two
+// V^T stages.
+template <class C>
+constexpr int dk_ring_bytes() {
+  return 2 * dk_slot_bytes<C>() + 2 * C::V_ELEMS * 2;
+}
+
+// s_waitcnt immediate: at most n vector-memory loads outstanding (the
+// other counters unconstrained).
+constexpr int waitcnt_vm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+// seg_run for the pair kernel's halves with K staged by direct loads (the
+// caller's seg_begin<T, C, false> leaves tile 1's K rows unloaded): tile
+// t + 1's K rows go straight into K slot (t + 1) & 1 at the start of tile t
+// (that slot was last read in tile t - 1, before the barrier that ended
+// it), and each wave waits for them before the barrier that ends tile t,
+// which then publishes them; V is staged as in seg_run (registers two tiles
+// ahead, then the transposing stores).  On return every load has completed
+// (the ring may be reused at once) and the workgroup has passed a barrier.
+template <typename T, class C, bool CAUSAL>
+__device__ __forceinline__ void seg_run_direct(const PrefillArgs& a, char* ring, SegIn<C>& in,
+                                               int b, int hkv, int qb, const SegTiles& st,
+                                               const Column& col, float& mrun, float& lrun,
+                                               f32x16 (&acc)[C::DB], int steps) {
+  static_assert(pair_direct_k<C>(), "direct K staging: bf16, d = 128, 32-key tiles");
+  const int tid = threadIdx.x % C::NT;  // index within the loading group
+  const int lane = tid & 63;
+  const int j = lane & 31;
+  const int h2 = lane >> 5;
+  auto kslot = [&](int sl) { return ring + sl * dk_slot_bytes<C>(); };
+  auto vstage = [&](int sg) {
+    return reinterpret_cast<T*>(ring + 2 * dk_slot_bytes<C>() + sg * C::V_ELEMS * 2);
+  };
+  const T* kbase;
+  const T* vbase;
+  kv_bases<T, C>(a, b, hkv, kbase, vbase);
+  const KDirect<C> kd = k_direct_offsets<C>(tid, a.kv_rowb);
+  const int full_lim = CAUSAL ? min(a.Nk, a.q_offset + qb * a.R + 1) : a.Nk;
+  const int lim = (CAUSAL && col.valid) ? min(a.q_offset + col.i, a.Nk - 1) : a.Nk - 1;
+
+  mrun = kNegInf;
+  lrun = 0.f;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+
+  store_k_direct_layout<C>(in.ra, kslot(0), tid);
+  store_tile<T, C, false>(in.ra, nullptr, vstage(0), tid);
+  __syncthreads();
+
+  // tile kt: K in slot kt & 1, V^T in stage kt & 1
+  auto step = [&](TileRegs<C>& mine, TileRegs<C>& next, int kt, int cur) {
+    k_direct<C>(kbase, st.at(kt + 1) * C::BC, a.Nk, kslot(cur ^ 1), tid, a.kv_rowb, kd);
+    load_tile<T, C, false>(mine, kbase, vbase, st.at(kt + 2) * C::BC, a.Nk, tid, a.kv_rowb);
+    if (kt < st.ntiles) {
+      f32x16 s[C::KB];
+      qk_tile_direct<C>(s, in.qf, kslot(cur), j, h2);
+      const int key0 = st.at(kt) * C::BC;
+      if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
+      softmax_pv_step<T, C>(s, mrun, lrun, acc, vstage(cur), j, h2, a.c, a.thr);
+    }
+    store_tile<T, C, false>(next, nullptr, vstage(cur ^ 1), tid);
+    // the K loads of tile kt + 1 (issued before this tile's V loads) are in
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::V_LOADS));
+    __syncthreads();
+  };
+  for (int kt = 0; kt < steps; kt += 2) {
+    step(in.ra, in.rb, kt, 0);
+    if (kt + 1 < steps) step(in.rb, in.ra, kt + 1, 1);
+  }
+  // the last tile's K loads (of a tile past the range) may still be landing
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 // seg_begin + seg_run back to back.
@@ -668,8 +753,10 @@ prefill_balanced_kernel(PrefillArgs a) {
 template <typename T, class C, bool CAUSAL>
 __global__ void __launch_bounds__(2 * C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_pair_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * C::STAGE_BYTES];
-  static_assert(4 * C::STAGE_BYTES >= C::NT * (C::DB * 16 + 2) * 4, "hand-over area too small");
+  constexpr bool DK = pair_direct_k<C>();
+  constexpr int RING = DK ? dk_ring_bytes<C>() : 2 * C::STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[2 * RING];
+  static_assert(2 * RING >= C::NT * (C::DB * 16 + 2) * 4, "hand-over area too small");
 
   const int tid = threadIdx.x;
   // wave-uniform; readfirstlane keeps what derives from them scalar
@@ -685,7 +772,7 @@ prefill_pair_kernel(PrefillArgs a) {
   const int kvg = s / a.HB;
   const int hkv = kvg % a.Hkv;
   const int b = kvg / a.Hkv;
-  char* ring = smem + half * 2 * C::STAGE_BYTES;
+  char* ring = smem + half * RING;
   // hand-over area: one block per wave slot w, DB*4 rows of 64 float4 (the
   // accumulator) then 64 float2 (m, l); consecutive lanes on consecutive
   // 16-byte addresses.  After the merge, wave w of the first half stages its
@@ -711,18 +798,21 @@ prefill_pair_kernel(PrefillArgs a) {
   int n0;
   SegTiles st = unit_seg(0, n0);
   Column col = lane_column<C>(a, b, hkv, hb, unit_qb(0), w, j);
-  seg_begin<T, C>(a, in, b, hkv, st, col);
+  seg_begin<T, C, !DK>(a, in, b, hkv, st, col);
   for (int u = 0; u < nunits; ++u) {
     const int qb = unit_qb(u);
     float mrun, lrun;
     f32x16 acc[C::DB];
-    seg_run<T, C, CAUSAL, true>(a, ring, in, b, hkv, qb, st, col, mrun, lrun, acc, n0);
+    if constexpr (DK)
+      seg_run_direct<T, C, CAUSAL>(a, ring, in, b, hkv, qb, st, col, mrun, lrun, acc, n0);
+    else
+      seg_run<T, C, CAUSAL, true>(a, ring, in, b, hkv, qb, st, col, mrun, lrun, acc, n0);
     if (u + 1 < nunits) {
       // issue the next unit's Q fragment and first tiles now: their latency
       // hides behind this unit's hand-over
       st = unit_seg(u + 1, n0);
       col = lane_column<C>(a, b, hkv, hb, unit_qb(u + 1), w, j);
-      seg_begin<T, C>(a, in, b, hkv, st, col);
+      seg_begin<T, C, !DK>(a, in, b, hkv, st, col);
     }
     // hand-over: the rings are free (seg_run ends on a barrier)
     if (half) {
