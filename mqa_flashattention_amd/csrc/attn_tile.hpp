@@ -346,7 +346,7 @@ __device__ __forceinline__ KDirect<C> k_direct_offsets(int tid, int rowb) {
 // with the wave's other vector-memory loads (one counter).
 template <class C>
 __device__ __forceinline__ void k_direct(const void* kbase, int key0, int nkeys, char* Kd, int tid,
-                                         int rowb, const KDirect<C>& kd) {
+                                         int rowb, const int* off) {
   static_assert(!C::F32 && C::D == 128 && C::BC == 32, "direct K: bf16, d = 128, 32-key tiles");
   const int ROWB = C::KVS ? rowb : 256;
   const int rows = nkeys - key0 < C::BC ? (nkeys - key0 > 0 ? nkeys - key0 : 0) : C::BC;
@@ -358,7 +358,7 @@ __device__ __forceinline__ void k_direct(const void* kbase, int key0, int nkeys,
 #pragma unroll
   for (int n = 0; n < (C::BC / 4) / C::NW; ++n)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (__attribute__((address_space(3))) void*)(Kd + (n * C::NW + w) * 1024), 16, kd.off[n],
+        rs, (__attribute__((address_space(3))) void*)(Kd + (n * C::NW + w) * 1024), 16, off[n],
         0, 0, 0);
 }
 

@@ -312,10 +312,11 @@ __device__ __forceinline__ void seg_run(const PrefillArgs& a, char* smem, SegIn<
   }
 }
 
-// Whether the pair kernel stages K by direct global -> LDS loads (bf16,
-// d = 128, 32-key tiles) instead of through registers.
+// Whether the key-split schedules (pair and quad) stage K by direct
+// global -> LDS loads (bf16, d = 128, 32-key tiles) instead of through
+// registers.
 template <class C>
-constexpr bool pair_direct_k() {
+constexpr bool use_direct_k() {
   return !C::F32 && C::D == 128 && C::BC == 32;
 }
 
@@ -332,7 +333,7 @@ constexpr int waitcnt_vm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
-// seg_run for the pair kernel's halves with K staged by direct loads (the
+// seg_run for the key-split schedules' groups with K staged by direct loads (the
 // caller's seg_begin<T, C, false> leaves tile 1's K rows unloaded): tile
 // t + 1's K rows go straight into K slot (t + 1) & 1 at the start of tile t
 // (that slot was last read in tile t - 1, before the barrier that ended
@@ -345,7 +346,7 @@ __device__ __forceinline__ void seg_run_direct(const PrefillArgs& a, char* ring,
                                                int b, int hkv, int qb, const SegTiles& st,
                                                const Column& col, float& mrun, float& lrun,
                                                f32x16 (&acc)[C::DB], int steps) {
-  static_assert(pair_direct_k<C>(), "direct K staging: bf16, d = 128, 32-key tiles");
+  static_assert(use_direct_k<C>(), "direct K staging: bf16, d = 128, 32-key tiles");
   const int tid = threadIdx.x % C::NT;  // index within the loading group
   const int lane = tid & 63;
   const int j = lane & 31;
@@ -372,7 +373,7 @@ __device__ __forceinline__ void seg_run_direct(const PrefillArgs& a, char* ring,
 
   // tile kt: K in slot kt & 1, V^T in stage kt & 1
   auto step = [&](TileRegs<C>& mine, TileRegs<C>& next, int kt, int cur) {
-    k_direct<C>(kbase, st.at(kt + 1) * C::BC, a.Nk, kslot(cur ^ 1), tid, a.kv_rowb, kd);
+    k_direct<C>(kbase, st.at(kt + 1) * C::BC, a.Nk, kslot(cur ^ 1), tid, a.kv_rowb, kd.off);
     load_tile<T, C, false>(mine, kbase, vbase, st.at(kt + 2) * C::BC, a.Nk, tid, a.kv_rowb);
     if (kt < st.ntiles) {
       f32x16 s[C::KB];
@@ -753,7 +754,7 @@ prefill_balanced_kernel(PrefillArgs a) {
 template <typename T, class C, bool CAUSAL>
 __global__ void __launch_bounds__(2 * C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_pair_kernel(PrefillArgs a) {
-  constexpr bool DK = pair_direct_k<C>();
+  constexpr bool DK = use_direct_k<C>();
   constexpr int RING = DK ? dk_ring_bytes<C>() : 2 * C::STAGE_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[2 * RING];
   static_assert(2 * RING >= C::NT * (C::DB * 16 + 2) * 4, "hand-over area too small");
@@ -991,11 +992,17 @@ __device__ __forceinline__ void quad_unit(const PrefillArgs& a, char* smem, int 
   const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
 
   SegIn<C> in;
-  seg_begin<T, C>(a, in, b, hkv, st, col);
+  constexpr bool DK = use_direct_k<C>();
+  static_assert(!DK || dk_ring_bytes<C>() <= 2 * C::STAGE_BYTES, "direct-K ring exceeds a group's");
+  seg_begin<T, C, !DK>(a, in, b, hkv, st, col);
   float mrun, lrun;
   f32x16 acc[C::DB];
-  seg_run<T, C, CAUSAL, true>(a, smem + grp * 2 * C::STAGE_BYTES, in, b, hkv, qb, st, col,
-                              mrun, lrun, acc, steps);
+  if constexpr (DK)
+    seg_run_direct<T, C, CAUSAL>(a, smem + grp * 2 * C::STAGE_BYTES, in, b, hkv, qb, st, col,
+                                 mrun, lrun, acc, steps);
+  else
+    seg_run<T, C, CAUSAL, true>(a, smem + grp * 2 * C::STAGE_BYTES, in, b, hkv, qb, st, col,
+                                mrun, lrun, acc, steps);
   // seg_run ends on a barrier: every ring is free
   if (grp > 0) {
     char* hand = smem + ((grp - 1) * C::NW + w) * HAND_BYTES;
