@@ -440,11 +440,14 @@ QUAD_SHAPES = [
     FwdShape(1, 32, 1, 400, 600, 64, False, 0),
     FwdShape(1, 160, 1, 70, 570, 64, True, 500),
     FwdShape(2, 16, 4, 512, 1024, 32, True, 512),
+    # a ragged last key tile (1000 = 31 * 32 + 8) on the direct K loads
+    FwdShape(2, 32, 8, 256, 1000, 128, True, 744),
 ]
 
 
 @pytest.mark.parametrize("s", QUAD_SHAPES, ids=["gqa_d128_offset", "f32_d64_offset", "mqa_g32",
-                                                "g160_three_head_blocks", "d32_offset"])
+                                                "g160_three_head_blocks", "d32_offset",
+                                                "gqa_d128_ragged_keys"])
 def test_quad_schedule(s):
     q, k, v, out = _check_fwd(s, 13)
     again = _fwd_gpu(q, k, v, causal=s.causal, q_offset=s.q_offset, scale=s.scale)

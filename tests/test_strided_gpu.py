@@ -54,6 +54,15 @@ def test_bthd_chunked_prefill_bitwise():
     _bitwise_case(WORKLOADS["chunked_prefill_4k"].fwd[0], 4)
 
 
+@pytest.mark.parametrize("s", [FwdShape(1, 48, 12, 2000, 2000, 128, True, 0),
+                               FwdShape(2, 32, 8, 256, 1000, 128, True, 744)],
+                         ids=["pair", "quad"])
+def test_bthd_ragged_keys_bitwise(s):
+    """Key counts that end in a partial 32-key tile, on the pair and quad
+    schedules (K rows loaded straight into LDS through the token stride)."""
+    _bitwise_case(s, 5)
+
+
 def _padded(x: torch.Tensor, pad_h: int, pad_n: int, order=(0, 1, 2)):
     """x [B, H, N, d] copied into a bigger buffer whose (batch, head, token)
     dimensions are laid out in the given outer-to-inner order, with pad_h
