@@ -303,60 +303,78 @@ __device__ __forceinline__ void store_tile(const TileRegs<C>& r, T* __restrict__
   }
 }
 
-// ---- K staged by direct global -> LDS loads (bf16, D = 128, 32-key tiles).
-// A K slot holds the tile's rows unpadded, 256 bytes each, with row r's
-// 16-byte chunk c at chunk position c ^ (r % 16): a direct load writes the
-// 16-byte chunks of a wave's 64 lanes to 1 KiB of consecutive LDS (lane i
-// at byte 16 i), which leaves no room for padding, and the XOR keeps the
-// score MFMA's K fragment reads (rows k_row_perm(j), chunks 2 ks + h2)
-// spread over the banks as the padded layout does.
+// ---- K staged by direct global -> LDS loads (bf16; d = 128 with 32-key
+// tiles or d = 64 with 64-key tiles).  A K slot holds the tile's rows
+// unpadded (D * 2 bytes each), with row r's 16-byte chunk c at chunk
+// position c ^ f(r): a direct load writes the 16-byte chunks of a wave's 64
+// lanes to 1 KiB of consecutive LDS (lane i at byte 16 i), which leaves no
+// room for padding, and the XOR keeps the score MFMA's K fragment reads
+// (rows 32 kb + k_row_perm(j), chunk 2 ks + h2) on distinct 16-byte bank
+// groups: f(r) = r mod 16 for 256-byte rows, (r / 2) mod 8 for 128-byte
+// rows (two rows per 256 bytes of banks).
+template <class C>
+constexpr bool direct_k_ok() {
+  return !C::F32 && ((C::D == 128 && C::BC == 32) || (C::D == 64 && C::BC == 64));
+}
+
 template <class C>
 constexpr int dk_slot_bytes() {
   return C::BC * C::D * 2;
 }
 
+template <class C>
 __device__ __forceinline__ int dk_chunk_off(int row, int chunk) {
-  return row * 256 + ((chunk ^ (row & 15)) << 4);
+  if constexpr (C::D == 128) return row * 256 + ((chunk ^ (row & 15)) << 4);
+  else return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 // Per-lane byte offsets of k_direct's loads within a tile (rows rowb bytes
-// apart): wave w's instruction n fills rows 4 (n NW + w) .. + 3, lane i row
-// 4 (n NW + w) + i / 16 at chunk position i % 16.
+// apart): wave w's instruction n fills the RPB rows of 1 KiB block
+// n NW + w; lane i takes row RPB (n NW + w) + i / CPR at chunk position
+// i % CPR, i.e. the row's chunk (i % CPR) ^ f(row).
 template <class C>
 struct KDirect {
-  int off[(C::BC / 4) / C::NW];
+  static constexpr int CPR = C::D / 8;               // 16-byte chunks per row
+  static constexpr int RPB = 64 / CPR;               // rows per 1 KiB block
+  static constexpr int NI = C::BC / RPB / C::NW;     // load instructions per thread
+  int off[NI];
 };
 
 template <class C>
 __device__ __forceinline__ KDirect<C> k_direct_offsets(int tid, int rowb) {
-  const int ROWB = C::KVS ? rowb : 256;
+  using K = KDirect<C>;
+  const int ROWB = C::KVS ? rowb : C::D * 2;
   const int w = tid >> 6;
   const int i = tid & 63;
-  KDirect<C> kd;
+  K kd;
 #pragma unroll
-  for (int n = 0; n < (C::BC / 4) / C::NW; ++n) {
-    const int r = 4 * (n * C::NW + w) + (i >> 4);
-    kd.off[n] = r * ROWB + (((i & 15) ^ (r & 15)) << 4);
+  for (int n = 0; n < K::NI; ++n) {
+    const int r = K::RPB * (n * C::NW + w) + i / K::CPR;
+    const int pos = i % K::CPR;
+    // the chunk whose swizzled position is pos
+    const int c = (dk_chunk_off<C>(r, pos) - r * (C::D * 2)) >> 4;
+    kd.off[n] = r * ROWB + c * 16;
   }
   return kd;
 }
 
-// Issue the direct loads of tile rows key0 .. key0 + 31 (below nkeys; rows
-// past it are written as zeros) into slot Kd.  They complete in issue order
-// with the wave's other vector-memory loads (one counter).
+// Issue the direct loads of tile rows key0 .. key0 + BC - 1 (below nkeys;
+// rows past it are written as zeros) into slot Kd, at the lane offsets off
+// (k_direct_offsets).  They complete in issue order with the wave's other
+// vector-memory loads (one counter).
 template <class C>
 __device__ __forceinline__ void k_direct(const void* kbase, int key0, int nkeys, char* Kd, int tid,
                                          int rowb, const int* off) {
-  static_assert(!C::F32 && C::D == 128 && C::BC == 32, "direct K: bf16, d = 128, 32-key tiles");
-  const int ROWB = C::KVS ? rowb : 256;
+  static_assert(direct_k_ok<C>(), "direct K: bf16, d = 128 / 32-key or d = 64 / 64-key tiles");
+  const int ROWB = C::KVS ? rowb : C::D * 2;
   const int rows = nkeys - key0 < C::BC ? (nkeys - key0 > 0 ? nkeys - key0 : 0) : C::BC;
   const uint64_t base = (uint64_t)(uint32_t)key0 * (uint32_t)ROWB;
-  const int span = rows > 0 ? (rows - 1) * ROWB + 256 : 0;
+  const int span = rows > 0 ? (rows - 1) * ROWB + C::D * 2 : 0;
   const uint32_t bytes = __builtin_amdgcn_readfirstlane((uint32_t)span);
   const auto rs = buffer_rsrc(reinterpret_cast<const char*>(kbase) + base, bytes);
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
-  for (int n = 0; n < (C::BC / 4) / C::NW; ++n)
+  for (int n = 0; n < KDirect<C>::NI; ++n)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (__attribute__((address_space(3))) void*)(Kd + (n * C::NW + w) * 1024), 16, off[n],
         0, 0, 0);
@@ -368,7 +386,8 @@ __device__ __forceinline__ void store_k_direct_layout(const TileRegs<C>& r, char
 #pragma unroll
   for (int n = 0; n < C::K_PER_T; ++n) {
     const int id = tid + n * C::NT;
-    *reinterpret_cast<u32x4*>(Kd + dk_chunk_off(id / C::ROW_CHUNKS, id % C::ROW_CHUNKS)) = r.k[n];
+    *reinterpret_cast<u32x4*>(Kd + dk_chunk_off<C>(id / C::ROW_CHUNKS, id % C::ROW_CHUNKS)) =
+        r.k[n];
   }
 }
 
@@ -427,17 +446,20 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const typename C::Fr
 template <class C>
 __device__ __forceinline__ void qk_tile_direct(f32x16 (&s)[C::KB], const bf16x8 (&qf)[C::QF],
                                                const char* __restrict__ Kd, int lane32, int h2) {
-  const int rr = k_row_perm(lane32);
-  bf16x8 kf[C::QF];
 #pragma unroll
-  for (int ks = 0; ks < C::QF; ++ks)
-    kf[ks] = *reinterpret_cast<const bf16x8*>(Kd + dk_chunk_off(rr, 2 * ks + h2));
-  __builtin_amdgcn_sched_barrier(0);
-  f32x16 a = {};
+  for (int kb = 0; kb < C::KB; ++kb) {
+    const int rr = 32 * kb + k_row_perm(lane32);
+    bf16x8 kf[C::QF];
 #pragma unroll
-  for (int ks = 0; ks < C::QF; ++ks)
-    a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], a, 0, 0, 0);
-  s[0] = a;
+    for (int ks = 0; ks < C::QF; ++ks)
+      kf[ks] = *reinterpret_cast<const bf16x8*>(Kd + dk_chunk_off<C>(rr, 2 * ks + h2));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 a = {};
+#pragma unroll
+    for (int ks = 0; ks < C::QF; ++ks)
+      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], a, 0, 0, 0);
+    s[kb] = a;
+  }
 }
 
 // ---- online softmax, one tile at a time (composed in softmax_pv_step).

@@ -313,11 +313,10 @@ __device__ __forceinline__ void seg_run(const PrefillArgs& a, char* smem, SegIn<
 }
 
 // Whether the key-split schedules (pair and quad) stage K by direct
-// global -> LDS loads (bf16, d = 128, 32-key tiles) instead of through
-// registers.
+// global -> LDS loads instead of through registers: bf16, d = 128.
 template <class C>
 constexpr bool use_direct_k() {
-  return !C::F32 && C::D == 128 && C::BC == 32;
+  return direct_k_ok<C>() && C::D == 128;
 }
 
 // LDS ring of seg_run_direct: two K slots (direct-load layout), then two
@@ -333,9 +332,9 @@ constexpr int waitcnt_vm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
-// seg_run for the key-split schedules' groups with K staged by direct loads (the
-// caller's seg_begin<T, C, false> leaves tile 1's K rows unloaded): tile
-// t + 1's K rows go straight into K slot (t + 1) & 1 at the start of tile t
+// seg_run with K staged by direct loads (the caller's
+// seg_begin<T, C, false> leaves tile 1's K rows unloaded): tile t + 1's K
+// rows go straight into K slot (t + 1) & 1 at the start of tile t
 // (that slot was last read in tile t - 1, before the barrier that ended
 // it), and each wave waits for them before the barrier that ends tile t,
 // which then publishes them; V is staged as in seg_run (registers two tiles
@@ -346,7 +345,7 @@ __device__ __forceinline__ void seg_run_direct(const PrefillArgs& a, char* ring,
                                                int b, int hkv, int qb, const SegTiles& st,
                                                const Column& col, float& mrun, float& lrun,
                                                f32x16 (&acc)[C::DB], int steps) {
-  static_assert(use_direct_k<C>(), "direct K staging: bf16, d = 128, 32-key tiles");
+  static_assert(direct_k_ok<C>(), "direct K staging: bf16, d = 128 or 64");
   const int tid = threadIdx.x % C::NT;  // index within the loading group
   const int lane = tid & 63;
   const int j = lane & 31;
@@ -396,7 +395,8 @@ __device__ __forceinline__ void seg_run_direct(const PrefillArgs& a, char* ring,
   __syncthreads();
 }
 
-// seg_begin + seg_run back to back.
+// seg_begin + seg_run (seg_run_direct for non-causal bf16 units at d = 128
+// and 64) back to back.
 template <typename T, class C, bool CAUSAL>
 __device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, int b, int hkv,
                                             int qb, int tile0, int ntiles, int rot,
@@ -404,8 +404,16 @@ __device__ __forceinline__ void run_segment(const PrefillArgs& a, char* smem, in
                                             f32x16 (&acc)[C::DB]) {
   SegIn<C> in;
   const SegTiles st{tile0, ntiles, rot};
-  seg_begin<T, C>(a, in, b, hkv, st, col);
-  seg_run<T, C, CAUSAL>(a, smem, in, b, hkv, qb, st, col, mrun, lrun, acc, ntiles);
+  // non-causal units are long (every key tile), so the direct K loads' one-tile
+  // lead costs nothing at their start; causal ones keep the register path
+  if constexpr (direct_k_ok<C>() && !CAUSAL) {
+    static_assert(dk_ring_bytes<C>() <= 2 * C::STAGE_BYTES, "direct-K ring exceeds two stages");
+    seg_begin<T, C, false>(a, in, b, hkv, st, col);
+    seg_run_direct<T, C, CAUSAL>(a, smem, in, b, hkv, qb, st, col, mrun, lrun, acc, ntiles);
+  } else {
+    seg_begin<T, C>(a, in, b, hkv, st, col);
+    seg_run<T, C, CAUSAL>(a, smem, in, b, hkv, qb, st, col, mrun, lrun, acc, ntiles);
+  }
 }
 
 // Bytes of one wave's output staging area: its 32 rows of O with a
