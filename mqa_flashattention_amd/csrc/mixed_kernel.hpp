@@ -235,7 +235,7 @@ mixed_quad_kernel(MixedArgs m) {
     if ((int)blockIdx.x < a.T) {
       const int i = blockIdx.x;
       const int t = (a.T % 8 == 0) ? (i % 8) * (a.T / 8) + i / 8 : i;
-      quad_unit<T, CQ, true>(a, smem, t);
+      quad_unit<T, CQ, true, false>(a, smem, t);
     }
     mixed_decode_phase<T, CD, DW, 4 * CQ::NW>(m, smem, &s_unit);
     leave_persistent(a, kMixedDecodeCounter);
@@ -265,7 +265,7 @@ mixed_quad_kernel(MixedArgs m) {
     const int rest = t % per_qb;
     const int hb = rest % a.HB;
     const int kvg = q + kNumQueues * (rest / a.HB);
-    quad_unit<T, CQ, true>(a, smem, (kvg * a.HB + hb) * a.NQB + qb);
+    quad_unit<T, CQ, true, false>(a, smem, (kvg * a.HB + hb) * a.NQB + qb);
   }
   mixed_decode_phase<T, CD, DW, 4 * CQ::NW>(m, smem, &s_unit);
   leave_persistent(a, kMixedDecodeCounter);

@@ -966,7 +966,9 @@ constexpr int quad_lds_bytes() {
 // schedule, run by the whole 8-wave workgroup in smem (quad_lds_bytes).
 // Ends with group 0 storing the rows; the caller puts a barrier between
 // this and any later use of smem.
-template <typename T, class C, bool CAUSAL>
+// DIRECT_OK false keeps K on the register path (the mixed launch's quad
+// kernel, which was measured slower with direct K loads).
+template <typename T, class C, bool CAUSAL, bool DIRECT_OK = true>
 __device__ __forceinline__ void quad_unit(const PrefillArgs& a, char* smem, int t) {
   static_assert(C::NW == 2, "quad groups are two waves");
   constexpr int NG = 4;
@@ -1000,7 +1002,7 @@ __device__ __forceinline__ void quad_unit(const PrefillArgs& a, char* smem, int 
   const Column col = lane_column<C>(a, b, hkv, hb, qb, w, j);
 
   SegIn<C> in;
-  constexpr bool DK = use_direct_k<C>();
+  constexpr bool DK = DIRECT_OK && use_direct_k<C>();
   static_assert(!DK || dk_ring_bytes<C>() <= 2 * C::STAGE_BYTES, "direct-K ring exceeds a group's");
   seg_begin<T, C, !DK>(a, in, b, hkv, st, col);
   float mrun, lrun;
