@@ -337,6 +337,7 @@ struct KDirect {
   static constexpr int CPR = C::D / 8;               // 16-byte chunks per row
   static constexpr int RPB = 64 / CPR;               // rows per 1 KiB block
   static constexpr int NI = C::BC / RPB / C::NW;     // load instructions per thread
+  static_assert((C::BC / RPB) % C::NW == 0, "whole 1 KiB blocks per wave");
   int off[NI];
 };
 
@@ -383,6 +384,7 @@ __device__ __forceinline__ void k_direct(const void* kbase, int key0, int nkeys,
 // The K chunks of a register-staged tile (load_tile's pattern) into slot Kd.
 template <class C>
 __device__ __forceinline__ void store_k_direct_layout(const TileRegs<C>& r, char* Kd, int tid) {
+  static_assert(C::K_CHUNKS % C::NT == 0, "every thread holds whole K chunks");
 #pragma unroll
   for (int n = 0; n < C::K_PER_T; ++n) {
     const int id = tid + n * C::NT;
