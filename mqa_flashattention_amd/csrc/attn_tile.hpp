@@ -444,17 +444,21 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const typename C::Fr
   }
 }
 
-// qk_tile over a K slot in the direct-load layout.
-template <class C>
-__device__ __forceinline__ void qk_tile_direct(f32x16 (&s)[C::KB], const bf16x8 (&qf)[C::QF],
-                                               const char* __restrict__ Kd, int lane32, int h2) {
+// qk_tile over a K slot in the direct-load layout, from precomputed LDS
+// addresses of slot 0's fragments (kp[kb][ks]: row 32 kb + k_row_perm(j),
+// chunk 2 ks + h2); slot SL's lie SL * dk_slot_bytes further, a constant
+// folded into the read instructions.
+typedef __attribute__((address_space(3))) const char lds_cchar;
+template <class C, int SL>
+__device__ __forceinline__ void qk_tile_direct_at(f32x16 (&s)[C::KB], const bf16x8 (&qf)[C::QF],
+                                                  lds_cchar* const (&kp)[C::KB][C::QF]) {
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) {
-    const int rr = 32 * kb + k_row_perm(lane32);
     bf16x8 kf[C::QF];
 #pragma unroll
     for (int ks = 0; ks < C::QF; ++ks)
-      kf[ks] = *reinterpret_cast<const bf16x8*>(Kd + dk_chunk_off<C>(rr, 2 * ks + h2));
+      kf[ks] = *reinterpret_cast<__attribute__((address_space(3))) const bf16x8*>(
+          kp[kb][ks] + SL * dk_slot_bytes<C>());
     __builtin_amdgcn_sched_barrier(0);
     f32x16 a = {};
 #pragma unroll

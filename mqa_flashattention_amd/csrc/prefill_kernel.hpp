@@ -358,6 +358,18 @@ __device__ __forceinline__ void seg_run_direct(const PrefillArgs& a, char* ring,
   const T* vbase;
   kv_bases<T, C>(a, b, hkv, kbase, vbase);
   const KDirect<C> kd = k_direct_offsets<C>(tid, a.kv_rowb);
+  // slot 0's K fragment addresses, computed once; the empty asm keeps them
+  // in registers (left alone, the compiler re-adds the slot base to each
+  // lane offset in every tile: eight more VALU instructions per tile)
+  lds_cchar* kp[C::KB][C::QF];
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+    for (int ks = 0; ks < C::QF; ++ks) {
+      kp[kb][ks] = (lds_cchar*)(ring) +
+                   dk_chunk_off<C>(32 * kb + k_row_perm(j), 2 * ks + h2);
+      asm volatile("" : "+v"(kp[kb][ks]));
+    }
   const int full_lim = CAUSAL ? min(a.Nk, a.q_offset + qb * a.R + 1) : a.Nk;
   const int lim = (CAUSAL && col.valid) ? min(a.q_offset + col.i, a.Nk - 1) : a.Nk - 1;
 
@@ -376,7 +388,10 @@ __device__ __forceinline__ void seg_run_direct(const PrefillArgs& a, char* ring,
     load_tile<T, C, false>(mine, kbase, vbase, st.at(kt + 2) * C::BC, a.Nk, tid, a.kv_rowb);
     if (kt < st.ntiles) {
       f32x16 s[C::KB];
-      qk_tile_direct<C>(s, in.qf, kslot(cur), j, h2);
+      if (cur == 0)
+        qk_tile_direct_at<C, 0>(s, in.qf, kp);
+      else
+        qk_tile_direct_at<C, 1>(s, in.qf, kp);
       const int key0 = st.at(kt) * C::BC;
       if (key0 + C::BC > full_lim) mask_tile<C>(s, key0, lim, h2);
       softmax_pv_step<T, C>(s, mrun, lrun, acc, vstage(cur), j, h2, a.c, a.thr);
