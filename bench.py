@@ -571,7 +571,61 @@ def measured_peaks():
                     "across the MFMA kernel"}
 
 
-# ---------------------------------------------------------------- per-config windows
+LDS_PATTERNS = [
+    # (pattern id of gqa_mb_lds, access, what it is)
+    (0, "16-byte read", "linear (lane * 16)"),
+    (1, "16-byte read", "forward K fragments: k_row_perm rows of 272 bytes"),
+    (2, "16-byte read", "forward V^T fragments: 32 consecutive 80-byte rows"),
+    (3, "16-byte read", "dK/dV score operands: rows 8 (n/4) + 4 qb + n%4 of 272 bytes"),
+    (4, "16-byte read", "dK/dV transposed operands: 16 consecutive 80-byte rows"),
+    (5, "16-byte read", "case 3 from 256-byte rows, row 16 qb + n, chunk XOR row"),
+    (6, "16-byte read", "case 4 from 96-byte rows"),
+    (7, "4-byte write", "linear (lane * 4)"),
+    (8, "4-byte write", "transposed staging: two-key words into 80-byte rows"),
+    (9, "16-byte write", "linear (lane * 16)"),
+    (10, "16-byte write", "row-major staging: rows 2n + i of 272 bytes"),
+]
+
+
+def lds_probe():
+    """Time every LDS access pattern of gqa_mb_lds (libgqa_microbench.so): 4 waves
+    per block, one block per CU, each wave repeating its pattern 4096 x 16
+    times; best of 5 launches after a warm-up.  The ratio to the linear
+    pattern of the same access width is the pattern's bank-conflict factor."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "mqa_flashattention_amd", "libgqa_microbench.so"))
+    lib.gqa_mb_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                               ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    reps = 4096
+    rows, base = [], {}
+    for pat, access, what in LDS_PATTERNS:
+        def run():
+            if lib.gqa_mb_lds(pat, cus, reps, ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+                raise SystemExit("LDS microbenchmark launch failed")
+        run()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = min(times)
+        base.setdefault(access, ms)
+        rows.append({"pattern": pat, "access": access, "what": what, "ms": round(ms, 4),
+                     "ns_per_wave_instruction": round(ms * 1e6 / (reps * 16 * 4), 3),
+                     "vs_linear": round(ms / base[access], 2)})
+    return rows
+
+
+# ---------------------------------------------------------------- per-config windows# ---------------------------------------------------------------- per-config windows
 
 def time_windows(fn, nwin=5, min_ms=10.0):
     """Per-call duration of fn (one launch on the current stream): 3 warm-up
@@ -1203,6 +1257,9 @@ def main(argv=None):
     ap.add_argument("--counters-run", action="store_true",
                     help="in this process: parity, the step loop, then every config's kernels "
                          "a few times without timing windows (for rocprofv3 --pmc)")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="time the LDS access patterns of the kernels' tile reads and staging "
+                         "writes (libgqa_microbench.so) and print them as JSON lines")
     ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--cpu-baseline", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args(argv)
@@ -1213,6 +1270,11 @@ def main(argv=None):
     if args.summarize_trace:
         stats, command, name = args.summarize_trace
         summarize_trace(stats, command, name)
+        return 0
+
+    if args.lds_probe:
+        for row in lds_probe():
+            print(json.dumps(row), flush=True)
         return 0
 
     if args.gpus != 1:

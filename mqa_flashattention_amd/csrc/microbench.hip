@@ -10,7 +10,12 @@
 //     (the HBM read rate once the buffer exceeds the 256 MB Infinity Cache);
 //   * the shader clock under MFMA load: wave 0 of the MFMA kernel reads the
 //     core-clock counter (s_memtime) and the constant 100 MHz counter
-//     (s_memrealtime) at its start and end.
+//     (s_memrealtime) at its start and end;
+//   * gqa_mb_lds: LDS access patterns of the attention kernels' tile reads
+//     and staging writes, each repeated by every wave; the time per pattern
+//     over the linear pattern's of the same width is its bank-conflict
+//     factor (rocprofv3's SQ_LDS_BANK_CONFLICT over SQ_INSTS_LDS gives the
+//     same answer in conflict cycles).
 // Each call is asynchronous on the given stream; the caller times it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -71,9 +76,92 @@ __global__ void __launch_bounds__(256) read_peak_kernel(const u32x4* __restrict_
   if ((x[0] ^ x[1] ^ x[2] ^ x[3]) == 0x9e3779b9u) sink[threadIdx.x] = x[0];
 }
 
+// Byte address of lane `lane`'s access in step k of LDS pattern pat, inside
+// one wave's 16 KiB window (every pattern stays below 16 KiB).
+__device__ __forceinline__ int lds_addr(int pat, int lane, int k) {
+  const int n = lane & 15, G = lane >> 4;   // 16-lane groups (the 16x16x32 MFMA's layout)
+  const int j = lane & 31, h2 = lane >> 5;  // half-waves (the 32x32x16 MFMA's layout)
+  switch (pat) {
+    case 0:  // 16-byte reads, linear
+      return lane * 16;
+    case 1: {  // forward K fragments: row k_row_perm(j) of 272-byte rows, chunk 2 k + h2
+      const int r = (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+      return r * 272 + 16 * (2 * (k & 7) + h2);
+    }
+    case 2:  // forward V^T fragments: 32 consecutive 80-byte rows, columns 32 hk + 16 h2
+      return (32 * (k & 3) + j) * 80 + 32 * ((k >> 2) & 1) + 16 * h2;
+    case 3:  // dK/dV score operands: rows 8 (n / 4) + 4 qb + n % 4 of 272-byte rows
+      return (8 * (n >> 2) + 4 * (k & 1) + (n & 3)) * 272 + 16 * G + 64 * ((k >> 1) & 3);
+    case 4:  // dK/dV transposed operands: 16 consecutive 80-byte rows
+      return (16 * (k & 7) + n) * 80 + 16 * G;
+    case 5: {  // the score operands of case 3 from 256-byte rows, row 16 qb + n, chunk ^ row
+      const int c = G + 4 * ((k >> 1) & 3);
+      return (16 * (k & 1) + n) * 256 + ((c ^ n) << 4);
+    }
+    case 6:  // the transposed operands of case 4 from 96-byte rows
+      return (16 * (k & 7) + n) * 96 + 16 * G;
+    case 7:  // 4-byte writes, linear
+      return lane * 4;
+    case 8:  // transposed staging writes: two-key words into 80-byte rows
+      return (G * 8 + (k & 7)) * 80 + n * 4;
+    case 9:  // 16-byte writes, linear
+      return lane * 16;
+    case 10:  // row-major staging writes: rows 2 n + i of 272-byte rows, chunk G
+      return (2 * n + (k & 1)) * 272 + G * 16;
+  }
+  return 0;
+}
+
+// Patterns 0-6 are 16-byte reads, 7-8 4-byte writes, 9-10 16-byte writes.
+constexpr int kLdsPatterns = 11;
+
+template <int KIND>  // 0: 16-byte read, 1: 4-byte write, 2: 16-byte write
+__global__ void __launch_bounds__(256) lds_pattern_kernel(int pat, int reps, uint32_t* sink) {
+  __shared__ __attribute__((aligned(16))) char lds[65536];
+  const int lane = threadIdx.x & 63;
+  const int base = (threadIdx.x >> 6) * 16384;  // each wave in its own window
+  for (int i = threadIdx.x; i < 65536 / 16; i += 256)
+    reinterpret_cast<u32x4*>(lds)[i] = u32x4{1u, 2u, 3u, 4u};
+  __syncthreads();
+  uint32_t acc = 0;
+  for (int r = 0; r < reps; ++r) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int a = base + lds_addr(pat, lane, k);
+      if constexpr (KIND == 0) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + a);
+        acc += v[0] ^ v[3];
+      } else if constexpr (KIND == 1) {
+        *reinterpret_cast<uint32_t*>(lds + a) = acc + k;
+      } else {
+        *reinterpret_cast<u32x4*>(lds + a) = u32x4{acc, (uint32_t)k, 0u, 0u};
+      }
+    }
+    __builtin_amdgcn_s_barrier();
+  }
+  __syncthreads();
+  // never true for these values; keeps the accesses alive
+  if ((acc ^ reinterpret_cast<const uint32_t*>(lds)[threadIdx.x]) == 0x9e3779b9u)
+    sink[threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
+
+// LDS pattern pat (0 .. 10: see lds_addr), blocks of 256 threads, reps x 16
+// accesses per wave; sink: 256 uint32 (device).
+int gqa_mb_lds(int pat, int blocks, int reps, uint32_t* sink, void* stream) {
+  if (pat < 0 || pat >= kLdsPatterns || blocks < 1 || reps < 1 || !sink) return 1;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (pat <= 6)
+    hipLaunchKernelGGL(lds_pattern_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, pat, reps, sink);
+  else if (pat <= 8)
+    hipLaunchKernelGGL(lds_pattern_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, pat, reps, sink);
+  else
+    hipLaunchKernelGGL(lds_pattern_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, st, pat, reps, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // blocks of 256 threads, iters x 4 MFMAs per wave (32768 FLOPs each).
 // clk_out (device, 2 x u64): core-clock and 100 MHz counter deltas of wave 0.

@@ -383,3 +383,21 @@ def test_mixed_binding_checks_parts_before_the_library():
         binding.attn_mixed(None, None, None, 0, q[:, :, 0], q, None, None)
     with pytest.raises(ValueError):  # CPU tensors are refused
         binding.attn_mixed(q, q[:, :2], q[:, :2], 0, None, None, None, None)
+
+
+def test_microbench_library_exports_and_rejects_bad_arguments():
+    """The measurement library (bench.py's machine peaks and --lds-probe) loads,
+    exports its three entry points, and refuses invalid arguments before any
+    HIP call (return 1)."""
+    path = os.path.join(os.path.dirname(binding.LIBRARY), "libgqa_microbench.so")
+    lib = ctypes.CDLL(path)
+    for name in ("gqa_mb_mfma_bf16", "gqa_mb_read", "gqa_mb_lds"):
+        assert hasattr(lib, name), name
+    lib.gqa_mb_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                               ctypes.c_void_p]
+    sink = ctypes.c_void_p(16)  # never dereferenced: every call below is refused first
+    assert lib.gqa_mb_lds(-1, 1, 1, sink, None) == 1
+    assert lib.gqa_mb_lds(11, 1, 1, sink, None) == 1
+    assert lib.gqa_mb_lds(0, 0, 1, sink, None) == 1
+    assert lib.gqa_mb_lds(0, 1, 0, sink, None) == 1
+    assert lib.gqa_mb_lds(0, 1, 1, None, None) == 1
