@@ -625,6 +625,52 @@ def lds_probe():
     return rows
 
 
+def valu_probe():
+    """fp32 FMA and exp2 rates (libgqa_microbench.so gqa_mb_valu): eight
+    independent chains per lane, 8 waves per CU; lane operations per clock
+    per CU from the kernel time and wave 0's clock counters (best of 5), at 8
+    and at 16 waves per CU."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "mqa_flashattention_amd", "libgqa_microbench.so"))
+    lib.gqa_mb_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    clk = torch.zeros(2, dtype=torch.int64, device=dev)
+    sink = torch.zeros(cus * 4 * 256, dtype=torch.float32, device=dev)
+    out = []
+    cases = [(op, name, iters, wpc) for wpc in (8, 16)
+             for op, name, iters in ((0, "fp32 FMA (v_fma_f32)", 1 << 16),
+                                     (1, "exp2 (v_exp_f32, plus a subtraction)", 1 << 14))]
+    for op, name, iters, wpc in cases:
+        blocks = cus * wpc // 4
+        def run():
+            if lib.gqa_mb_valu(op, blocks, iters, ctypes.c_void_p(clk.data_ptr()),
+                               ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+                raise SystemExit("VALU microbenchmark launch failed")
+        run()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3
+            if best is None or t < best[0]:
+                best = (t, clk.tolist())
+        t, (ticks, ref) = best
+        ghz = ticks / (ref / 100e6) / 1e9 if ref else None
+        lane_ops = blocks * 256 * iters * 8
+        out.append({"op": name, "waves_per_cu": wpc, "ms": round(t * 1e3, 3),
+                    "sclk_ghz": round(ghz, 3) if ghz else None,
+                    "lane_ops_per_clk_per_cu": round(lane_ops / t / (ghz * 1e9) / cus, 1) if ghz else None})
+    return out
+
+
 # ---------------------------------------------------------------- per-config windows# ---------------------------------------------------------------- per-config windows
 
 def time_windows(fn, nwin=5, min_ms=10.0):
@@ -1260,6 +1306,9 @@ def main(argv=None):
     ap.add_argument("--lds-probe", action="store_true",
                     help="time the LDS access patterns of the kernels' tile reads and staging "
                          "writes (libgqa_microbench.so) and print them as JSON lines")
+    ap.add_argument("--valu-probe", action="store_true",
+                    help="time fp32 FMA and exp2 chains (libgqa_microbench.so) and print the "
+                         "lane operations per clock per CU as JSON lines")
     ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--cpu-baseline", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args(argv)
@@ -1274,6 +1323,10 @@ def main(argv=None):
 
     if args.lds_probe:
         for row in lds_probe():
+            print(json.dumps(row), flush=True)
+        return 0
+    if args.valu_probe:
+        for row in valu_probe():
             print(json.dumps(row), flush=True)
         return 0
 

@@ -15,7 +15,11 @@
 //     and staging writes, each repeated by every wave; the time per pattern
 //     over the linear pattern's of the same width is its bank-conflict
 //     factor (rocprofv3's SQ_LDS_BANK_CONFLICT over SQ_INSTS_LDS gives the
-//     same answer in conflict cycles).
+//     same answer in conflict cycles);
+//   * gqa_mb_valu: the vector-ALU rate of the two operations the softmax
+//     spends its time on, fp32 FMA and the hardware exp2 (v_exp_f32), each
+//     as eight independent chains per lane, with wave 0's clock counters
+//     as in the MFMA kernel.
 // Each call is asynchronous on the given stream; the caller times it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -145,9 +149,58 @@ __global__ void __launch_bounds__(256) lds_pattern_kernel(int pat, int reps, uin
     sink[threadIdx.x] = acc;
 }
 
+template <int OP>  // 0: fp32 FMA, 1: exp2
+__global__ void __launch_bounds__(256) valu_rate_kernel(int iters, unsigned long long* clk,
+                                                        float* sink) {
+  const bool timer = blockIdx.x == 0 && threadIdx.x == 0;
+  unsigned long long t0 = 0, r0 = 0;
+  if (timer) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
+  float x[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) x[c] = -0.001f * (float)((threadIdx.x + c) & 15);
+  const float a = 0.999f, b = -0.0001f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if constexpr (OP == 0)
+        x[c] = __builtin_fmaf(x[c], a, b);
+      else
+        x[c] = __builtin_amdgcn_exp2f(x[c]) - 1.0f;  // stays in (-1, 0]: no overflow
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sum += x[c];
+  // never true for these values; keeps the chains alive
+  if (sum == 12345.0f) sink[blockIdx.x * 256 + threadIdx.x] = sum;
+  if (timer) {
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    clk[0] = t1 - t0;
+    clk[1] = r1 - r0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// op 0: fp32 FMA, 1: exp2 (plus one subtraction per exp); blocks of 256
+// threads, iters x 8 operations per lane.  clk_out (device, 2 x u64) as in
+// gqa_mb_mfma_bf16; sink: blocks x 256 floats (device).
+int gqa_mb_valu(int op, int blocks, int iters, unsigned long long* clk_out, float* sink,
+                void* stream) {
+  if (op < 0 || op > 1 || blocks < 1 || iters < 1 || !clk_out || !sink) return 1;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (op == 0)
+    hipLaunchKernelGGL(valu_rate_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, st, iters, clk_out, sink);
+  else
+    hipLaunchKernelGGL(valu_rate_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, iters, clk_out, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // LDS pattern pat (0 .. 10: see lds_addr), blocks of 256 threads, reps x 16
 // accesses per wave; sink: 256 uint32 (device).

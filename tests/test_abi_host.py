@@ -387,11 +387,11 @@ def test_mixed_binding_checks_parts_before_the_library():
 
 def test_microbench_library_exports_and_rejects_bad_arguments():
     """The measurement library (bench.py's machine peaks and --lds-probe) loads,
-    exports its three entry points, and refuses invalid arguments before any
+    exports its entry points, and refuses invalid arguments before any
     HIP call (return 1)."""
     path = os.path.join(os.path.dirname(binding.LIBRARY), "libgqa_microbench.so")
     lib = ctypes.CDLL(path)
-    for name in ("gqa_mb_mfma_bf16", "gqa_mb_read", "gqa_mb_lds"):
+    for name in ("gqa_mb_mfma_bf16", "gqa_mb_read", "gqa_mb_lds", "gqa_mb_valu"):
         assert hasattr(lib, name), name
     lib.gqa_mb_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                ctypes.c_void_p]
@@ -401,3 +401,7 @@ def test_microbench_library_exports_and_rejects_bad_arguments():
     assert lib.gqa_mb_lds(0, 0, 1, sink, None) == 1
     assert lib.gqa_mb_lds(0, 1, 0, sink, None) == 1
     assert lib.gqa_mb_lds(0, 1, 1, None, None) == 1
+    lib.gqa_mb_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.gqa_mb_valu(2, 1, 1, sink, sink, None) == 1
+    assert lib.gqa_mb_valu(0, 1, 1, None, sink, None) == 1
