@@ -472,6 +472,9 @@ def _random_shapes():
     shapes.append((FwdShape(2, 32, 8, 2100, 2100, 128, True, 0), None))
     shapes.append((FwdShape(6, 24, 4, 1500, 1700, 64, False, 0), None))
     shapes.append((FwdShape(4, 40, 8, 1100, 1300, 128, True, 200, torch.float32), None))
+    # non-causal d = 128 with more than two units per resident workgroup: persistent
+    # schedule with K loaded straight into LDS, last key tile ragged (2300 = 71 * 32 + 28)
+    shapes.append((FwdShape(2, 32, 8, 2200, 2300, 128, False, 0), None))
     # causal, one pair per CU or more: pair schedule
     shapes.append((FwdShape(1, 48, 12, 2000, 2000, 128, True, 0), None))
     shapes.append((FwdShape(2, 40, 8, 1100, 1300, 128, True, 200, torch.float32), None))

@@ -55,11 +55,18 @@ def test_bthd_chunked_prefill_bitwise():
 
 
 @pytest.mark.parametrize("s", [FwdShape(1, 48, 12, 2000, 2000, 128, True, 0),
-                               FwdShape(2, 32, 8, 256, 1000, 128, True, 744)],
-                         ids=["pair", "quad"])
+                               FwdShape(2, 32, 8, 256, 1000, 128, True, 744),
+                               FwdShape(2, 32, 8, 2200, 2300, 128, False, 0),
+                               FwdShape(4, 16, 4, 4000, 4000, 64, False, 0)],
+                         ids=["pair", "quad", "persistent_d128", "persistent_d64"])
 def test_bthd_ragged_keys_bitwise(s):
-    """Key counts that end in a partial 32-key tile, on the pair and quad
-    schedules (K rows loaded straight into LDS through the token stride)."""
+    """Key counts that end in a partial key tile, on the schedules that load K
+    rows straight into LDS (pair, quad, non-causal persistent at d = 128 and
+    64), through the token stride.  The shapes have enough units for the
+    persistent schedule whatever the kernels' occupancy: the balanced
+    schedule's chunk plan follows the resident workgroups, which may differ
+    between the strided and contiguous kernels, and with it the summation
+    order (both then stay within the oracle's bar, not bit for bit)."""
     _bitwise_case(s, 5)
 
 
