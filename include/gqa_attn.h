@@ -118,7 +118,12 @@ int gqa_attn_fwd(const void* q, const void* k, const void* v, void* o,
  *   output rows (GQA_ERR_BAD_SHAPE); the K/V token stride below 2^25 bytes
  *   (GQA_ERR_BAD_SHAPE).  K and V may overlap or repeat (a zero stride
  *   broadcasts); O must not overlap Q, K or V.  Everything else as
- *   gqa_attn_fwd, whose result this equals bit for bit for the same values.
+ *   gqa_attn_fwd, whose result this equals bit for bit for the same values
+ *   on the pair, quad and persistent schedules.  Where the balanced schedule
+ *   runs (few units), its key-tile chunks follow the resident workgroups of
+ *   the kernel launched, which for a run-time K/V stride may be fewer, so
+ *   the units can be cut differently and the result then equals
+ *   gqa_attn_fwd's to within rounding order.
  */
 int gqa_attn_fwd_strided(const void* q, const void* k, const void* v, void* o,
                          int B, int Hq, int Hkv, int Nq, int Nk, int d,
