@@ -957,7 +957,7 @@ def other_workloads(K):
         "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
         "algorithmic_gflop": round(bwd_flops(ps) / 1e9, 4),
         "note": "gqa_attn_bwd: dQ kernel (one pass, online softmax, row statistics), "
-                "dK/dV kernel (query range of each key block in up to 8 parts) and their "
+                "dK/dV kernel (query range of each key block in up to 16 parts) and their "
                 "merge; 5 contractions counted (the kernels execute 6: S twice)"}
     for name in ("llama3_8b_mixed", "llama3_8b_mixed_c128"):
         wm = WORKLOADS[name]

@@ -362,8 +362,8 @@ int gqa_attn_mixed(const void* q, const void* k, const void* v, void* o,
 /*
  * Bytes of device workspace gqa_attn_bwd needs for these sizes: two fp32
  * row statistics per query row (B * Hq * Nq rows, rounded up to 16 bytes),
- * then, when the K/V side is small (fewer than 256 * 16 waves of 32 keys),
- * P = min(8, ceil(4096 / (ceil(Nk / 64) * Hkv * B * 2))) fp32 partial copies
+ * then, when the K/V side is small (fewer than 1024 key blocks of 64 keys),
+ * P = min(16, ceil(1024 / (ceil(Nk / 64) * Hkv * B))) fp32 partial copies
  * of dk and dv (P * 2 * B * Hkv * Nk * d floats).  Returns 0 for invalid
  * sizes.
  */
@@ -391,7 +391,7 @@ size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int 
  * workspace: device memory of at least gqa_attn_bwd_workspace_bytes(B, Hq,
  * Hkv, Nq, Nk, d) bytes, owned by the caller, contents on entry irrelevant;
  * it receives each row's log-sum-exp and D, and the fp32 dk, dv of the
- * parts (up to eight) each key block's query range is cut into, added in a
+ * parts (up to sixteen) each key block's query range is cut into, added in a
  * fixed order at the end.  scale must be finite and > 0
  * (GQA_ERR_UNSUPPORTED otherwise).  Outputs must not alias inputs.  Other
  * status codes and error behaviour as gqa_attn_fwd (plus GQA_ERR_WORKSPACE).

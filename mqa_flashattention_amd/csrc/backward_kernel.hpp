@@ -55,7 +55,7 @@ struct BwdArgs {
 // every query sees) do not serialise the kernel and small launches still
 // fill the CUs; bwd_merge_kernel adds the parts' dK, dV in part order.
 // With one part the kernel writes dK, dV itself.
-constexpr int kBwdQuerySplitMax = 8;
+constexpr int kBwdQuerySplitMax = 16;
 
 // LDS buffers of staged tiles in the backward kernels: two (tile t + 1
 // written while tile t is used) when they fit in half of a CU's LDS, so
@@ -342,9 +342,13 @@ __global__ void __launch_bounds__(C::NT) bwd_dkdv_kernel(BwdArgs ba) {
   const int j = lane & 31;
   const int h2 = lane >> 5;
 
-  const int part = blockIdx.x % ba.qsplit;
-  const int k0 = (blockIdx.x / ba.qsplit) * 32 * C::NW;
-  const int hkv = blockIdx.y;
+  // a batch's blocks in (key block, part, K/V head) order, heads fastest:
+  // the heaviest key blocks of a causal launch, of every head, come first,
+  // and consecutive blocks (on different XCDs) take different heads
+  const int lin = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+  const int hkv = lin % a.Hkv;
+  const int part = (lin / a.Hkv) % ba.qsplit;
+  const int k0 = (lin / a.Hkv / ba.qsplit) * 32 * C::NW;
   const int b = blockIdx.z;
   const int key = k0 + 32 * w + j;
   const bool kvalid = key < a.Nk;
@@ -538,9 +542,13 @@ bwd_dkdv16_kernel(BwdArgs ba) {
   const int n = lane & 15;  // the lane's key within the wave's 16
   const int G = lane >> 4;  // the lane's group: queries 8 G .. 8 G + 7 of a tile
 
-  const int part = blockIdx.x % ba.qsplit;
-  const int k0 = (blockIdx.x / ba.qsplit) * 64;
-  const int hkv = blockIdx.y;
+  // a batch's blocks in (key block, part, K/V head) order, heads fastest:
+  // the heaviest key blocks of a causal launch, of every head, come first,
+  // and consecutive blocks (on different XCDs) take different heads
+  const int lin = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+  const int hkv = lin % a.Hkv;
+  const int part = (lin / a.Hkv) % ba.qsplit;
+  const int k0 = (lin / a.Hkv / ba.qsplit) * 64;
   const int b = blockIdx.z;
   const int key = k0 + 16 * w + n;
   const bool kvalid = key < a.Nk;

@@ -1023,14 +1023,16 @@ int mixed_entry(const void* q, const void* k, const void* v, void* o, int B, int
 
 // ------------------------------------------------------------------ backward
 
-// Query parts per dK/dV key block (64 keys, two waves): about 16 dK/dV waves
-// per CU of a 256-CU gfx950 part (four rounds at one resident wave per
-// SIMD, so causal launches balance), at most kBwdQuerySplitMax.  A function
-// of the shape alone, so that the workspace query and the launch agree.
-constexpr long long kBwdSplitWaves = 16LL * 256;
+// Query parts per dK/dV key block (64 keys): about four dK/dV workgroups
+// per CU of a 256-CU gfx950 part, at most kBwdQuerySplitMax.  The kernels
+// take their blocks heaviest key block first, so a causal launch balances
+// with a few rounds of workgroups; more parts only add records for the
+// merge to read.  A function of the shape alone, so that the workspace
+// query and the launch agree.
+constexpr long long kBwdSplitBlocks = 4LL * 256;
 int bwd_query_parts(int B, int Hkv, int Nk) {
-  const long long waves = (long long)((Nk + 63) / 64) * Hkv * B * 2;
-  const long long qs = (kBwdSplitWaves + waves - 1) / waves;
+  const long long blocks = (long long)((Nk + 63) / 64) * Hkv * B;
+  const long long qs = (kBwdSplitBlocks + blocks - 1) / blocks;
   return (int)std::max(1LL, std::min<long long>(qs, gqa::kBwdQuerySplitMax));
 }
 

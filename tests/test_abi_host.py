@@ -310,12 +310,14 @@ def test_bwd_rejects_invalid_arguments(kw, code):
 def test_bwd_workspace_bytes():
     ws = binding.bwd_workspace_bytes
     # two fp32 row statistics (log-sum-exp and D) per query row, rounded up to
-    # 16 bytes, then P query parts' fp32 dK and dV, P = min(8, ceil(4096 /
-    # dK/dV waves)), none when P = 1
-    assert ws(1, 32, 8, 2048, 2048, 128) == 2 * 32 * 2048 * 4 + 8 * 2 * 8 * 2048 * 128 * 4
-    assert ws(1, 16, 16, 2048, 2048, 64) == 2 * 16 * 2048 * 4 + 4 * 2 * 16 * 2048 * 64 * 4
-    assert ws(3, 5, 5, 7, 9, 32) == 848 + 8 * 2 * 3 * 5 * 9 * 32 * 4  # 840 bytes -> 848
-    assert ws(8, 8, 8, 2048, 2048, 128) == 2 * 8 * 8 * 2048 * 4  # 4096 waves: one part
+    # 16 bytes, then P query parts' fp32 dK and dV, P = min(16, ceil(1024 /
+    # key blocks)) with ceil(Nk / 64) key blocks per (batch, K/V head), none
+    # when P = 1
+    assert ws(1, 32, 8, 2048, 2048, 128) == 2 * 32 * 2048 * 4 + 4 * 2 * 8 * 2048 * 128 * 4
+    assert ws(1, 16, 16, 2048, 2048, 64) == 2 * 16 * 2048 * 4 + 2 * 2 * 16 * 2048 * 64 * 4
+    assert ws(1, 32, 1, 4096, 4096, 128) == 2 * 32 * 4096 * 4 + 16 * 2 * 4096 * 128 * 4
+    assert ws(3, 5, 5, 7, 9, 32) == 848 + 16 * 2 * 3 * 5 * 9 * 32 * 4  # 840 bytes -> 848
+    assert ws(8, 8, 8, 2048, 2048, 128) == 2 * 8 * 8 * 2048 * 4  # 2048 key blocks: one part
     for bad in [(0, 1, 1, 1, 1, 32), (1, 3, 2, 1, 1, 32), (1, 1, 1, 0, 1, 32),
                 (1, 1, 1, 1, 0, 32), (1, 1, 1, 1, 1, 48)]:
         assert ws(*bad) == 0
