@@ -81,17 +81,22 @@ def test_bwd_llama3_8b_shape_full():
     _check(WORKLOADS["llama3_8b_prefill"].fwd[0], seed=0)
 
 
+# query parts per key block: min(16, ceil(1024 / key blocks)), with
+# ceil(Nk / 64) key blocks per (batch, K/V head)
 @pytest.mark.parametrize("s", [
-    FwdShape(1, 16, 16, 2048, 2048, 64, True, 0),  # four query parts per key block
-    FwdShape(2, 16, 16, 2048, 2048, 64, True, 0),  # two
-    FwdShape(4, 16, 16, 2048, 2048, 64, True, 0),  # one: dK, dV written directly
-    FwdShape(1, 16, 16, 2048, 2048, 128, True, 0),  # d = 128: the 16-key dK/dV kernel
-    FwdShape(4, 16, 16, 2048, 2048, 128, True, 0),  # d = 128, one part
-], ids=["four_parts", "two_parts", "one_part", "d128_four_parts", "d128_one_part"])
+    FwdShape(1, 16, 4, 2048, 2048, 64, True, 0),   # 128 key blocks: eight query parts
+    FwdShape(1, 16, 8, 2048, 2048, 64, True, 0),   # 256: four
+    FwdShape(1, 16, 16, 2048, 2048, 64, True, 0),  # 512: two
+    FwdShape(4, 16, 16, 2048, 2048, 64, True, 0),  # 2048: one, dK and dV written directly
+    FwdShape(1, 16, 8, 2048, 2048, 128, True, 0),  # d = 128 (the 16-key dK/dV kernel), four
+    FwdShape(4, 16, 16, 2048, 2048, 128, True, 0),  # d = 128, one
+], ids=["eight_parts", "four_parts", "two_parts", "one_part", "d128_four_parts",
+        "d128_one_part"])
 def test_bwd_query_split_counts(s):
     """Launches large enough that each key block's query range is cut into
-    four or two parts, or not cut at all (the small shapes above use eight);
-    bf16 at d = 128 runs the 16-key dK/dV kernel, the others the 32-key one."""
+    eight, four or two parts, or not cut at all (the small shapes above use
+    sixteen); bf16 at d = 128 runs the 16-key dK/dV kernel, the others the
+    32-key one."""
     _check(s, seed=5)
 
 
